@@ -244,20 +244,23 @@ static void rows_bwd_body(int64_t r, void *vc) {
     double *dab = c->dab + r * 2 * h, *dx = c->dx + r * d;
     /* dH'_j = sum_q dy_q W2[q, j]  (not stored);  SwiGLU backward from the
        stored a, b:  s = sigmoid(a), dA = dH' b s (1 + a (1 - s)), dB = dH' silu(a) */
+    /* loops run q (resp. j) outermost so the weights are read row by row;
+       every output element still sums its terms in ascending order */
+    double *g = (double *)calloc((size_t)(h > d ? h : d), sizeof(double));
+    for (int q = 0; q < d; q++)
+        for (int j = 0; j < h; j++) g[j] += dy[q] * w2[(int64_t)q * h + j];
     for (int j = 0; j < h; j++) {
-        double g = 0.0;
-        for (int q = 0; q < d; q++) g += dy[q] * w2[(int64_t)q * h + j];
         double a = ab[j], b = ab[h + j], s = sigmoid(a);
-        dab[j] = round_to(c->dt, g * b * s * (1.0 + a * (1.0 - s)));
-        dab[h + j] = round_to(c->dt, g * a * s);
+        dab[j] = round_to(c->dt, g[j] * b * s * (1.0 + a * (1.0 - s)));
+        dab[h + j] = round_to(c->dt, g[j] * a * s);
     }
     const double *g1 = c->dab_in ? c->dab_in + r * 2 * h : dab;
     /* dx_q = sum_j dAB_j W1[j, q] */
-    for (int q = 0; q < d; q++) {
-        double s = 0.0;
-        for (int j = 0; j < 2 * h; j++) s += g1[j] * w1[(int64_t)j * d + q];
-        dx[q] = round_to(c->dt, s);
-    }
+    for (int q = 0; q < d; q++) g[q] = 0.0;
+    for (int j = 0; j < 2 * h; j++)
+        for (int q = 0; q < d; q++) g[q] += g1[j] * w1[(int64_t)j * d + q];
+    for (int q = 0; q < d; q++) dx[q] = round_to(c->dt, g[q]);
+    free(g);
 }
 
 /* Backward of the expert FFN for n rows, given the stored dy_perm rows and

@@ -22,8 +22,8 @@ MUTATIONS = {
                             "if (best < 0 || l[e] >= l[best]) best = e;"),
     "router_bwd_sign": ("(float)(g * (dgate[t * k + j] - dot))", "(float)(g * (dot - dgate[t * k + j]))"),
     "slot_index": ("sorted_slot[p] = j;", "sorted_slot[p] = k - 1 - j;"),
-    "dB_uses_b": ("dab[h + j] = round_to(c->dt, g * a * s);", "dab[h + j] = round_to(c->dt, g * b * s);"),
-    "dA_dropped_term": ("g * b * s * (1.0 + a * (1.0 - s))", "g * b * s"),
+    "dB_uses_b": ("dab[h + j] = round_to(c->dt, g[j] * a * s);", "dab[h + j] = round_to(c->dt, g[j] * b * s);"),
+    "dA_dropped_term": ("g[j] * b * s * (1.0 + a * (1.0 - s))", "g[j] * b * s"),
     "combine_bwd_no_gate": ("dy_perm[p * d + q] = round_to(dt, g * dout[t * d + q]);",
                             "dy_perm[p * d + q] = round_to(dt, dout[t * d + q]);"),
     "gemm2_reads_unrounded": ("const double *g2 = c->hp_in ? c->hp_in + r * h : hp;",
