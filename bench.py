@@ -1,0 +1,222 @@
+"""Throughput of the MoE expert layer (forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload e128_bf16]
+
+A step is one pass of the whole path on one batch of synthetic inputs already
+resident in HBM: route -> permute -> grouped GEMM1 + SwiGLU -> grouped GEMM2
+-> combine, then the full backward (combine/router backward, GEMM2 dgrad +
+SwiGLU backward, GEMM2 wgrad, GEMM1 dgrad, GEMM1 wgrad, unpermute backward).
+Prints one JSON line. Default workload: T=16384 tokens, d=2048, E=128
+experts, top-4, SwiGLU hidden 1024, bf16 with fp32 accumulation, random
+routing (the pages' measurement condition: kongchang.com, "caveats behind the
+numbers").
+
+Besides the layer throughput the line carries:
+  roofline     -- the grouped GEMM1 + SwiGLU kernel (the largest forward
+                  GEMM): useful flops 2*R*d*2h per launch over its average
+                  duration, timed with HIP events on the launch stream inside
+                  the timed region, against the dense bf16 MFMA peak;
+  cpu_baseline -- the CPU oracle (plain loops, fp64) on the host cores, on a
+                  bounded sample: the same layer on the first few hundred
+                  tokens of the workload (all experts), in tokens/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd+bwd tokens/s, E=128 top-4; grouped-GEMM % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="e128_bf16")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=256,
+                    help="tokens in the oracle's bounded sample")
+    ap.add_argument("--breakdown", action="store_true",
+                    help="also time every ABI call separately (stderr)")
+    ap.add_argument("--copy-calib", type=int, default=0,
+                    help="run a plain device copy of this many MiB (PMC byte calibration)")
+    return ap.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the MoE layer here is "
+              "a single-GPU build with no collectives", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import routing_grouped_gemm_router_amd as moe
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = synth.WORKLOADS[a.workload]
+    if w.dtype != "bf16":
+        print(f"workload {w.name} is not a bf16 workload", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    inp = synth.device_inputs(w, seed=a.seed, with_dout=w.backward)
+    T, d, E, k, h = w.T, w.d, w.E, w.k, w.h
+    R = T * k
+    layer = moe.MoELayer(inp["w1"], inp["w2"], k)
+    x, logits, dout = inp["x"], inp["logits"], inp["dout"]
+    stream = torch.cuda.current_stream()
+
+    ev = []
+
+    def step(timed):
+        layer._alloc(T, x.device, x.dtype)
+        r = moe.moe_route(logits, k, out=layer.route, ws=layer.route_ws)
+        moe.moe_permute(x, r["token_pos"], layer.x_perm)
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        moe.moe_grouped_gemm(moe.MOE_GG_FWD, layer.x_perm, layer.w1, layer.ab, r["offsets"],
+                             moe.MOE_EPI_SWIGLU_FWD, N=2 * h, K=d, aux_out=layer.hp)
+        if timed:
+            e1.record(stream)
+            ev.append((e0, e1))
+        moe.moe_grouped_gemm(moe.MOE_GG_FWD, layer.hp, layer.w2, layer.y_perm, r["offsets"],
+                             N=d, K=h)
+        moe.moe_combine(layer.y_perm, r["topk_gate"], r["token_pos"], layer.out)
+        if w.backward:
+            layer.backward(dout)
+
+    for _ in range(a.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms = elapsed * 1e3 / a.steps
+    g1_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
+    g1_flops = 2.0 * R * d * 2 * h
+    g1_tflops = g1_flops / (g1_ms * 1e-3) / 1e12
+    flops = w.fwd_bwd_flops() if w.backward else w.fwd_flops()
+
+    if a.breakdown:
+        breakdown(moe, torch, layer, x, logits, dout, w)
+    if a.copy_calib:
+        n = a.copy_calib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": METRIC,
+        "value": T * a.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: MoE expert layer {'fwd+bwd' if w.backward else 'fwd'}, "
+                        f"T={T} tokens, d_model={d}, E={E} experts, top-{k}, SwiGLU hidden={h}, "
+                        f"bf16 storage / fp32 accumulate, {'Zipf(1.2)-skewed' if w.zipf_s else 'uniform random'} routing",
+            "tokens": T, "d_model": d, "experts": E, "top_k": k, "hidden": h,
+            "layer_tflops": flops / (ms * 1e-3) / 1e12,
+            "layer_frac_of_bf16_mfma_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        },
+        "roofline": {
+            "kernel": "grouped GEMM1 + SwiGLU forward (gg_bf16<FWD, SWIGLU_FWD>)",
+            "bound": "mfma",
+            "achieved": g1_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": g1_tflops / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "avg_launch_ms": g1_ms,
+            "flops_per_launch": g1_flops,
+        },
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, w, a.cpu_tokens)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(inp, w, n_tok):
+    """The oracle, untuned, on the host cores: the same layer (all E experts,
+    same weights) forward + backward on the workload's first n_tok tokens."""
+    import numpy as np
+    import oracle
+
+    sub = dict(logits=inp["logits"][:n_tok].float().cpu().numpy(),
+               x=inp["x"][:n_tok].float().cpu().numpy(),
+               w1=inp["w1"].float().cpu().numpy(), w2=inp["w2"].float().cpu().numpy(),
+               dout=inp["dout"][:n_tok].float().cpu().numpy() if w.backward else None)
+    t0 = time.perf_counter()
+    f = oracle.layer_forward(sub, w.k, "bf16")
+    if w.backward:
+        oracle.layer_backward(sub, f, w.k, "bf16")
+    dt = time.perf_counter() - t0
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"first {n_tok} of {w.T} tokens of {w.name} (all {w.E} experts), "
+                      f"{'fwd+bwd' if w.backward else 'fwd'}, fp64 oracle, {dt:.1f} s"}
+
+
+def breakdown(moe, torch, layer, x, logits, dout, w, reps=5):
+    """Per-call event timing of one step (a separate, untimed pass)."""
+    T, d, E, k, h = w.T, w.d, w.E, w.k, w.h
+    R = T * k
+    r = layer.route
+    calls = [
+        ("route", lambda: moe.moe_route(logits, k, out=r, ws=layer.route_ws), 0, 4 * T * E),
+        ("permute", lambda: moe.moe_permute(x, r["token_pos"], layer.x_perm), 0, 2 * T * d * (1 + k)),
+        ("gemm1_swiglu", lambda: moe.moe_grouped_gemm(moe.MOE_GG_FWD, layer.x_perm, layer.w1, layer.ab,
+                                                      r["offsets"], moe.MOE_EPI_SWIGLU_FWD, N=2 * h,
+                                                      K=d, aux_out=layer.hp), 4 * R * d * h, 0),
+        ("gemm2", lambda: moe.moe_grouped_gemm(moe.MOE_GG_FWD, layer.hp, layer.w2, layer.y_perm,
+                                               r["offsets"], N=d, K=h), 2 * R * d * h, 0),
+        ("combine", lambda: moe.moe_combine(layer.y_perm, r["topk_gate"], r["token_pos"], layer.out),
+         0, 2 * T * d * (1 + k)),
+        ("backward(all)", lambda: layer.backward(dout), 12 * R * d * h, 0),
+    ]
+    for name, fn, flops, nbytes in calls:
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        extra = ""
+        if flops:
+            extra += f" {flops / ms / 1e9:.1f} TFLOP/s ({flops / ms / 1e9 / PEAK_BF16_TFLOPS:.1%})"
+        if nbytes:
+            extra += f" {nbytes / ms / 1e6:.0f} GB/s ({nbytes / ms / 1e6 / PEAK_HBM_GBS:.1%})"
+        print(f"[breakdown] {name:14s} {ms * 1e3:9.1f} us{extra}", file=sys.stderr, flush=True)
+
+
+if __name__ == "__main__":
+    main()

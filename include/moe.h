@@ -1,0 +1,269 @@
+/*
+ * moe.h -- C ABI of libmoe: the MoE expert layer on one MI355X (gfx950).
+ *
+ * The layer (as the pages describe it in prose):
+ *   - each token activates a few of E experts (e.g. 4 of 128)
+ *     [Ai2 Olmo-core 3, kongchang.com, section "capacity tax"];
+ *   - routing is computed on the GPU and its metadata (the split sizes and the
+ *     per-expert group sizes) stays there, so the host enqueues work without
+ *     waiting for a device-to-host copy [kongchang.com, "routing is a systems
+ *     problem"; aizyradar.cn, "What changed"; bytechap.com, "How it works"];
+ *   - only the selected token rows are written straight into the experts'
+ *     input buffers [kongchang.com, "capacity tax"; bytechap.com, "How it
+ *     works"];
+ *   - a device-scheduled grouped GEMM runs the uneven per-expert shapes
+ *     without padding every expert to one capacity [kongchang.com, "routing is
+ *     a systems problem"];
+ *   - MXFP8 (OCP, one shared scale per 32 elements) is used for the GEMMs and
+ *     the dispatch payload [kongchang.com, "caveats behind the numbers";
+ *     aikraft.ru, "Technical optimisations"].
+ * The pages give no router function, FFN shape or API; this header fixes them
+ * (softmax top-k router, SwiGLU experts, the calls below).
+ *
+ * Conventions for every call
+ *   - Tensor arguments are DEVICE pointers to dense row-major buffers that the
+ *     caller allocates and owns. The library never allocates, frees, copies
+ *     device->host or synchronises; it only enqueues kernels on `stream`
+ *     (a hipStream_t; NULL = the default stream). Every call can therefore be
+ *     captured in a HIP graph.
+ *   - Scratch memory, where a call needs it, comes in through (ws, ws_bytes);
+ *     the matching *_workspace_size() gives the minimum.
+ *   - Validation looks only at host-visible scalars and pointers (null,
+ *     16-byte alignment, shape limits); device data is never inspected. On a
+ *     validation error nothing is enqueued. After enqueueing, a launch error
+ *     is reported as MOE_ERR_LAUNCH.
+ *   - Limits: 1 <= E <= 256; 1 <= k <= min(E, 8); 0 <= T; T*k < 2^31;
+ *     d and h multiples of 32; d, h <= 16384.
+ *   - Non-finite logits are outside the contract: outputs are then
+ *     unspecified, but no kernel indexes out of bounds.
+ *   - Stateless and re-entrant: concurrent calls on different streams are
+ *     safe given distinct output and workspace buffers.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,       /* a required pointer is null */
+    MOE_ERR_SHAPE = 2,      /* a size is out of range or inconsistent */
+    MOE_ERR_DTYPE = 3,      /* unsupported dtype / mode / epilogue combination */
+    MOE_ERR_ALIGN = 4,      /* a tensor pointer is not 16-byte aligned */
+    MOE_ERR_WORKSPACE = 5,  /* workspace smaller than *_workspace_size() */
+    MOE_ERR_LAUNCH = 6      /* the HIP runtime reported an error at launch */
+};
+
+typedef int32_t moe_dtype;
+enum {
+    MOE_F32 = 0,    /* fp32 storage */
+    MOE_BF16 = 1,   /* bfloat16 storage, fp32 accumulation */
+    MOE_MXFP8 = 2   /* OCP MXFP8: E4M3 bytes + one E8M0 byte per 32 elements */
+};
+
+/* Human-readable name of a status code (static string). */
+const char *moe_status_str(moe_status s);
+
+/* ABI version of this header (major * 100 + minor). */
+int32_t moe_version(void);
+
+/* ------------------------------------------------------------------ */
+/* Routing                                                              */
+
+/* Bytes of scratch moe_route needs: 4 * E * ceil(T / 64), rounded up to 256. */
+size_t moe_route_workspace_size(int64_t T, int32_t E, int32_t k);
+
+/* Top-k softmax routing and the layer's routing metadata, all on device.
+ *   logits       [T, E] fp32 (router scores; an input: the router's linear
+ *                layer is outside this call)
+ *   topk_idx     [T, k] int32 out: the k experts of each token, best first;
+ *                experts are compared by fp32 logit, equal logits (IEEE, so
+ *                -0 == +0) go to the lower expert index
+ *   topk_gate    [T, k] fp32 out: softmax over the k selected logits (the full
+ *                softmax renormalised over the top k); sums to 1 per token
+ *   counts       [E] int32 out: rows routed to each expert (the group sizes)
+ *   offsets      [E+1] int32 out: exclusive prefix sum of counts; expert e owns
+ *                rows [offsets[e], offsets[e+1]) of every permuted buffer
+ *   token_pos    [T, k] int32 out: row of (token t, slot j) in the permuted
+ *                buffers = offsets[e] + #{t' < t that selected e}; rows inside
+ *                a group are therefore in ascending token order
+ *   sorted_token [T*k] int32 out: token of each permuted row (inverse map)
+ *   sorted_slot  [T*k] int32 out: slot j of each permuted row
+ *   tile_offsets [E+1] int32 out: exclusive prefix sum of ceil(counts/tile_m),
+ *                for callers running their own tiled GEMM (moe_grouped_gemm
+ *                derives its own schedule from offsets); tile_m >= 1
+ * Indices, counts, offsets and positions are bit-exact and deterministic
+ * (no order-dependent atomics). T = 0 writes zero counts and offsets. */
+moe_status moe_route(const float *logits, int64_t T, int32_t E, int32_t k, int32_t tile_m,
+                     int32_t *topk_idx, float *topk_gate, int32_t *counts, int32_t *offsets,
+                     int32_t *token_pos, int32_t *sorted_token, int32_t *sorted_slot,
+                     int32_t *tile_offsets, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* Dispatch and combine                                                 */
+
+/* Row-wise dispatch: every token row is read once and written to its k rows
+ * of the per-expert buffer: x_perm[token_pos[t, j]] = x[t], bit for bit.
+ *   x        [T, d] in dtype dt (MXFP8: E4M3 bytes)
+ *   x_scale  [T, d/32] E8M0 bytes (MXFP8 only, else ignored)
+ *   token_pos[T, k] int32; entries < 0 are dropped rows (padded baseline)
+ *   x_perm   [T*k, d] out (rows of dropped entries are not written)
+ *   x_perm_scale [T*k, d/32] out (MXFP8 only) */
+moe_status moe_permute(const void *x, const uint8_t *x_scale, moe_dtype dt, int64_t T, int32_t d,
+                       int32_t k, const int32_t *token_pos, void *x_perm, uint8_t *x_perm_scale,
+                       void *stream);
+
+/* Gate-weighted combine back to token order:
+ *   out[t] = sum_{j<k} topk_gate[t, j] * y_perm[token_pos[t, j]]
+ * summed in fp32 in ascending j, then rounded (to nearest even) to dt.
+ * Entries with token_pos < 0 contribute nothing. dt is MOE_F32 or MOE_BF16
+ * (y_perm and out share it). */
+moe_status moe_combine(const void *y_perm, moe_dtype dt, const float *topk_gate,
+                       const int32_t *token_pos, int64_t T, int32_t d, int32_t k, void *out,
+                       void *stream);
+
+/* ------------------------------------------------------------------ */
+/* Device-scheduled grouped GEMM                                         */
+
+enum { MOE_GG_FWD = 0, MOE_GG_DGRAD = 1, MOE_GG_WGRAD = 2 };
+enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU_FWD = 1, MOE_EPI_SWIGLU_BWD = 2 };
+
+/* One grouped GEMM over E groups of rows. Group g owns rows
+ * [offsets[g], offsets[g+1]) of the row-indexed operands; offsets is read on
+ * the device, so the host never learns the group sizes. A persistent grid
+ * walks every tile of every group; groups of 0 rows cost nothing in FWD and
+ * DGRAD and produce zeros in WGRAD.
+ *
+ * mode MOE_GG_FWD:   C[r, n]    = sum_k A[r, k] * B[g][n, k]
+ *                    A [rows, K], B [E, N, K], C [rows, N]
+ * mode MOE_GG_DGRAD: C[r, n]    = sum_k A[r, k] * B[g][k, n]
+ *                    A [rows, K], B [E, K, N], C [rows, N]
+ * mode MOE_GG_WGRAD: C[g][m, n] = sum_{r in g} A[r, m] * B[r, n]
+ *                    A [rows, M], B [rows, N], C [E, M, N] fp32, overwritten
+ *
+ * epilogue MOE_EPI_SWIGLU_FWD (mode FWD, N = 2h, B = W1 [E, 2h, d]):
+ *   C = AB [rows, 2h] (gate pre-activation a in columns 0..h-1, up b in
+ *   h..2h-1) and aux_out = H' [rows, h] = silu(a) * b computed from the fp32
+ *   accumulators.
+ * epilogue MOE_EPI_SWIGLU_BWD (mode DGRAD, N = h, A = dy [rows, d],
+ *   B = W2 [E, d, h]): the product dH' [rows, h] is not stored; with
+ *   aux = AB [rows, 2h] and s = sigmoid(a): C = dAB [rows, 2h] with
+ *   dA = dH' * b * s * (1 + a (1 - s)) in columns 0..h-1 and
+ *   dB = dH' * silu(a) in h..2h-1.
+ *
+ * dtype MOE_F32 or MOE_BF16: A, B and C (except WGRAD's fp32 C) have that
+ * dtype; accumulation is fp32; stores round to nearest even.
+ * dtype MOE_MXFP8 (MOE_GG_FWD and MOE_GG_DGRAD): A and B are E4M3 bytes with
+ * E8M0 scales in a_scale / b_scale, one per 32 elements along K
+ * (A: [rows, K/32]; B: [E, N, K/32], i.e. B given K-contiguous as [E, N, K]
+ * in both modes); C is bf16; aux_out_scale (SWIGLU_FWD) receives H' as MXFP8
+ * along its rows: aux_out = E4M3 [rows, h], aux_out_scale = [rows, h/32].
+ */
+typedef struct moe_gemm_desc {
+    int32_t mode;          /* MOE_GG_* */
+    int32_t dtype;         /* MOE_F32 | MOE_BF16 | MOE_MXFP8 */
+    int32_t epilogue;      /* MOE_EPI_* */
+    int32_t n_groups;      /* E */
+    int64_t rows;          /* total rows of the row-indexed operands (T*k) */
+    int32_t M, N, K;       /* FWD/DGRAD: N, K used (M is per group); WGRAD: M, N */
+    const int32_t *offsets;  /* device [n_groups + 1] */
+    const void *A;
+    const void *B;
+    void *C;
+    const uint8_t *a_scale;  /* MXFP8 */
+    const uint8_t *b_scale;  /* MXFP8 */
+    const void *aux;         /* SWIGLU_BWD: AB [rows, 2h] */
+    void *aux_out;           /* SWIGLU_FWD: H' [rows, h] */
+    uint8_t *aux_out_scale;  /* SWIGLU_FWD with MXFP8: H' scales */
+    void *ws;                /* scratch (split-K partials); may be null if ws_bytes = 0 */
+    size_t ws_bytes;
+} moe_gemm_desc;
+
+/* Scratch bytes moe_grouped_gemm needs for this descriptor (0 when none). */
+size_t moe_grouped_gemm_workspace_size(const moe_gemm_desc *g);
+
+moe_status moe_grouped_gemm(const moe_gemm_desc *g, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* Backward of the whole layer                                          */
+
+/* Backward of route -> permute -> GEMM1 + SwiGLU -> GEMM2 -> combine.
+ * Enqueues, in order: combine-bwd with the router backward fused in
+ * (dy_perm, dgate, dlogits), GEMM2-dgrad with the SwiGLU backward (dAB),
+ * GEMM2-wgrad (dW2), GEMM1-dgrad (dx_perm), GEMM1-wgrad (dW1),
+ * unpermute-bwd (dX). Saved forward tensors and the three intermediates are
+ * caller-owned buffers.
+ *   dlogits[t, e] = g_i (dg_i - sum_j g_j dg_j) for e = topk_idx[t, i], and
+ *   exactly 0 for unselected experts, with dg_j = <dOut[t], y_perm[row]>.
+ * dtype MOE_F32 or MOE_BF16 (activations, weights, dOut, dX, intermediates);
+ * dW1, dW2, dlogits and dgate are fp32. */
+typedef struct moe_bwd_desc {
+    int32_t dtype;
+    int32_t d, h, E, k;
+    int64_t T;
+    /* saved from the forward */
+    const void *x_perm;        /* [T*k, d] */
+    const void *ab;            /* [T*k, 2h] */
+    const void *hp;            /* [T*k, h] */
+    const void *y_perm;        /* [T*k, d] */
+    const float *topk_gate;    /* [T, k] */
+    const int32_t *topk_idx;   /* [T, k] */
+    const int32_t *token_pos;  /* [T, k] */
+    const int32_t *offsets;    /* [E+1] */
+    const void *w1;            /* [E, 2h, d] */
+    const void *w2;            /* [E, d, h] */
+    const void *dout;          /* [T, d] */
+    /* outputs */
+    void *dx;                  /* [T, d] */
+    float *dlogits;            /* [T, E] */
+    float *dw1;                /* [E, 2h, d] */
+    float *dw2;                /* [E, d, h] */
+    float *dgate;              /* [T, k], may be null */
+    /* caller-owned intermediates */
+    void *dy_perm;             /* [T*k, d] */
+    void *dab;                 /* [T*k, 2h] */
+    void *dx_perm;             /* [T*k, d] */
+    void *ws;
+    size_t ws_bytes;
+} moe_bwd_desc;
+
+size_t moe_backward_workspace_size(const moe_bwd_desc *b);
+
+moe_status moe_backward(const moe_bwd_desc *b, void *stream);
+
+/* ------------------------------------------------------------------ */
+/* MXFP8 quantisation (OCP Microscaling v1.0)                            */
+
+/* Quantise a [rows, cols] fp32 or bf16 matrix to MXFP8: per block of 32
+ * elements, the E8M0 shared exponent is floor(log2(amax)) - 8 (8 = the E4M3
+ * maximum exponent), clamped to [-127, 127], -127 for an all-zero block; the
+ * elements are x * 2^-shared rounded to nearest even E4M3 and saturated to
+ * +-448 (OCP E4M3: bias 7, no infinities, NaN = S.1111.111).
+ *   axis = 1: blocks along each row (cols % 32 == 0). q [rows, cols] E4M3,
+ *             scale [rows, cols/32].
+ *   axis = 0: blocks along each column, for a GEMM that reduces over rows.
+ *             Rows are split into n_groups groups by group_offsets (device,
+ *             n_groups+1 entries; null = one group of all rows, n_groups
+ *             ignored); blocks restart at each group and a group's last block
+ *             may be short. Output is transposed per group and padded to whole
+ *             blocks: with nb_g = ceil(len_g/32), bb_g = sum_{g'<g} nb_g',
+ *               q[bb_g*32*cols + c*nb_g*32 + i] = element (o_g + i, c) for
+ *               i < len_g, and 0 for len_g <= i < nb_g*32;
+ *               scale[bb_g*cols + c*nb_g + b] = block b of column c.
+ *             Size q and scale for the worst case (rows/32 + n_groups) blocks.
+ *             n_groups <= 1024.
+ * in_dt: MOE_F32 or MOE_BF16. */
+moe_status mxfp8_quantize(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
+                          int32_t axis, const int32_t *group_offsets, int32_t n_groups,
+                          uint8_t *q, uint8_t *scale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,330 @@
+"""Python binding of libmoe, the MI355X MoE expert layer (argument marshalling only).
+
+Every function here has the name of a C entry point in include/moe.h and does
+nothing but check tensor shapes/dtypes on the host, pass `data_ptr()`s, sizes
+and the current HIP stream to the library, and raise on a non-OK status. All
+arithmetic runs in the library's HIP kernels. The library is loaded from this
+package's directory; if it is missing, importing the binding raises (there is
+no fallback path).
+
+`MoELayer` strings the calls together in the layer's order (route -> permute
+-> grouped GEMM + SwiGLU -> grouped GEMM -> combine; `moe_backward`) and owns
+the saved tensors and intermediates as torch allocations.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, \
+    MOE_ERR_LAUNCH = range(7)
+MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
+MOE_GG_FWD, MOE_GG_DGRAD, MOE_GG_WGRAD = 0, 1, 2
+MOE_EPI_NONE, MOE_EPI_SWIGLU_FWD, MOE_EPI_SWIGLU_BWD = 0, 1, 2
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn}: {_lib.moe_status_str(status).decode()} (status {status})")
+        self.status = status
+
+
+class GemmDesc(ctypes.Structure):
+    _fields_ = [("mode", _I32), ("dtype", _I32), ("epilogue", _I32), ("n_groups", _I32),
+                ("rows", _I64), ("M", _I32), ("N", _I32), ("K", _I32),
+                ("offsets", _P), ("A", _P), ("B", _P), ("C", _P), ("a_scale", _P),
+                ("b_scale", _P), ("aux", _P), ("aux_out", _P), ("aux_out_scale", _P),
+                ("ws", _P), ("ws_bytes", _SZ)]
+
+
+class BwdDesc(ctypes.Structure):
+    _fields_ = [("dtype", _I32), ("d", _I32), ("h", _I32), ("E", _I32), ("k", _I32), ("T", _I64),
+                ("x_perm", _P), ("ab", _P), ("hp", _P), ("y_perm", _P), ("topk_gate", _P),
+                ("topk_idx", _P), ("token_pos", _P), ("offsets", _P), ("w1", _P), ("w2", _P),
+                ("dout", _P), ("dx", _P), ("dlogits", _P), ("dw1", _P), ("dw2", _P),
+                ("dgate", _P), ("dy_perm", _P), ("dab", _P), ("dx_perm", _P), ("ws", _P),
+                ("ws_bytes", _SZ)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m routing_grouped_gemm_router_amd.build` "
+            "(the MoE layer has no non-HIP path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.moe_status_str.argtypes = [_I32]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_version.restype = _I32
+    lib.moe_route_workspace_size.argtypes = [_I64, _I32, _I32]
+    lib.moe_route_workspace_size.restype = _SZ
+    lib.moe_route.argtypes = [_P, _I64, _I32, _I32, _I32] + [_P] * 9 + [_SZ, _P]
+    lib.moe_route.restype = _I32
+    lib.moe_permute.argtypes = [_P, _P, _I32, _I64, _I32, _I32, _P, _P, _P, _P]
+    lib.moe_permute.restype = _I32
+    lib.moe_combine.argtypes = [_P, _I32, _P, _P, _I64, _I32, _I32, _P, _P]
+    lib.moe_combine.restype = _I32
+    lib.moe_grouped_gemm.argtypes = [ctypes.POINTER(GemmDesc), _P]
+    lib.moe_grouped_gemm.restype = _I32
+    lib.moe_grouped_gemm_workspace_size.argtypes = [ctypes.POINTER(GemmDesc)]
+    lib.moe_grouped_gemm_workspace_size.restype = _SZ
+    lib.moe_backward.argtypes = [ctypes.POINTER(BwdDesc), _P]
+    lib.moe_backward.restype = _I32
+    lib.moe_backward_workspace_size.argtypes = [ctypes.POINTER(BwdDesc)]
+    lib.moe_backward_workspace_size.restype = _SZ
+    lib.mxfp8_quantize.argtypes = [_P, _I32, _I64, _I64, _I32, _P, _I32, _P, _P, _P]
+    lib.mxfp8_quantize.restype = _I32
+    return lib
+
+
+# torch must be imported first so that libmoe binds to the HIP runtime torch
+# already loaded (both carry the soname libamdhip64.so.7)
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _check(fn, st):
+    if st != MOE_OK:
+        raise MoeError(fn, st)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.uint8:
+        return MOE_MXFP8
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t, shape, dtype, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on GPU, got "
+                         f"{t.dtype} {tuple(t.shape)} (contiguous={t.is_contiguous()}, "
+                         f"device={t.device})")
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+
+
+def moe_route_workspace_size(T: int, E: int, k: int) -> int:
+    return int(_lib.moe_route_workspace_size(T, E, k))
+
+
+def moe_route(logits: torch.Tensor, k: int, tile_m: int = 128, out: dict | None = None,
+              ws: torch.Tensor | None = None) -> dict:
+    """Top-k routing + metadata (see moe.h). Returns a dict of device tensors."""
+    T, E = logits.shape
+    dev = logits.device
+    R = T * k
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = dict(topk_idx=torch.empty((T, k), **i32),
+                   topk_gate=torch.empty((T, k), dtype=torch.float32, device=dev),
+                   counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+                   token_pos=torch.empty((T, k), **i32), sorted_token=torch.empty(R, **i32),
+                   sorted_slot=torch.empty(R, **i32), tile_offsets=torch.empty(E + 1, **i32))
+    _need(logits, (T, E), torch.float32, "logits")
+    wsb = moe_route_workspace_size(T, E, k)
+    if ws is None:
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _check("moe_route", _lib.moe_route(
+        _p(logits), T, E, k, tile_m, _p(out["topk_idx"]), _p(out["topk_gate"]), _p(out["counts"]),
+        _p(out["offsets"]), _p(out["token_pos"]), _p(out["sorted_token"]), _p(out["sorted_slot"]),
+        _p(out["tile_offsets"]), _p(ws), ws.numel(), _stream()))
+    return out
+
+
+def moe_permute(x: torch.Tensor, token_pos: torch.Tensor, x_perm: torch.Tensor | None = None,
+                x_scale: torch.Tensor | None = None, x_perm_scale: torch.Tensor | None = None):
+    """x_perm[token_pos[t, j]] = x[t]. For MXFP8 pass uint8 x plus x_scale."""
+    T, d = x.shape
+    k = token_pos.shape[1]
+    if x_perm is None:
+        x_perm = torch.empty((T * k, d), dtype=x.dtype, device=x.device)
+    dt = _dt(x)
+    if dt == MOE_MXFP8 and x_perm_scale is None:
+        x_perm_scale = torch.empty((T * k, d // 32), dtype=torch.uint8, device=x.device)
+    _check("moe_permute", _lib.moe_permute(_p(x), _p(x_scale), dt, T, d, k, _p(token_pos),
+                                           _p(x_perm), _p(x_perm_scale), _stream()))
+    return (x_perm, x_perm_scale) if dt == MOE_MXFP8 else x_perm
+
+
+def moe_combine(y_perm: torch.Tensor, topk_gate: torch.Tensor, token_pos: torch.Tensor,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    T, k = token_pos.shape
+    d = y_perm.shape[1]
+    if out is None:
+        out = torch.empty((T, d), dtype=y_perm.dtype, device=y_perm.device)
+    _check("moe_combine", _lib.moe_combine(_p(y_perm), _dt(y_perm), _p(topk_gate), _p(token_pos),
+                                           T, d, k, _p(out), _stream()))
+    return out
+
+
+def moe_grouped_gemm(mode: int, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                     offsets: torch.Tensor, epilogue: int = MOE_EPI_NONE, M: int = 0, N: int = 0,
+                     K: int = 0, aux: torch.Tensor | None = None,
+                     aux_out: torch.Tensor | None = None, a_scale=None, b_scale=None,
+                     aux_out_scale=None, dtype: int | None = None):
+    """One grouped GEMM (see moe.h for the modes and epilogues)."""
+    desc = GemmDesc()
+    desc.mode = mode
+    desc.dtype = _dt(A) if dtype is None else dtype
+    desc.epilogue = epilogue
+    desc.n_groups = offsets.numel() - 1
+    desc.rows = A.shape[0]
+    desc.M, desc.N, desc.K = M, N, K
+    desc.offsets = offsets.data_ptr()
+    desc.A, desc.B, desc.C = A.data_ptr(), B.data_ptr(), C.data_ptr()
+    desc.a_scale = a_scale.data_ptr() if a_scale is not None else None
+    desc.b_scale = b_scale.data_ptr() if b_scale is not None else None
+    desc.aux = aux.data_ptr() if aux is not None else None
+    desc.aux_out = aux_out.data_ptr() if aux_out is not None else None
+    desc.aux_out_scale = aux_out_scale.data_ptr() if aux_out_scale is not None else None
+    wsb = int(_lib.moe_grouped_gemm_workspace_size(ctypes.byref(desc)))
+    ws = torch.empty(wsb, dtype=torch.uint8, device=A.device) if wsb else None
+    desc.ws = ws.data_ptr() if ws is not None else None
+    desc.ws_bytes = wsb
+    _check("moe_grouped_gemm", _lib.moe_grouped_gemm(ctypes.byref(desc), _stream()))
+    return C
+
+
+def moe_backward(saved: dict, dout: torch.Tensor, E: int, k: int, d: int, h: int,
+                 out: dict | None = None, want_dgate: bool = True) -> dict:
+    """Backward of the whole layer. `saved` holds the forward tensors
+    (x_perm, ab, hp, y_perm, topk_gate, topk_idx, token_pos, offsets, w1, w2)."""
+    T = dout.shape[0]
+    R = T * k
+    dev, dt = dout.device, dout.dtype
+    if out is None:
+        out = dict(dx=torch.empty((T, d), dtype=dt, device=dev),
+                   dlogits=torch.empty((T, E), dtype=torch.float32, device=dev),
+                   dw1=torch.empty((E, 2 * h, d), dtype=torch.float32, device=dev),
+                   dw2=torch.empty((E, d, h), dtype=torch.float32, device=dev),
+                   dgate=torch.empty((T, k), dtype=torch.float32, device=dev) if want_dgate else None,
+                   dy_perm=torch.empty((R, d), dtype=dt, device=dev),
+                   dab=torch.empty((R, 2 * h), dtype=dt, device=dev),
+                   dx_perm=torch.empty((R, d), dtype=dt, device=dev))
+    b = BwdDesc()
+    b.dtype = _dt(dout)
+    b.d, b.h, b.E, b.k, b.T = d, h, E, k, T
+    for name in ("x_perm", "ab", "hp", "y_perm", "topk_gate", "topk_idx", "token_pos", "offsets",
+                 "w1", "w2"):
+        setattr(b, name, saved[name].data_ptr())
+    b.dout = dout.data_ptr()
+    for name in ("dx", "dlogits", "dw1", "dw2", "dy_perm", "dab", "dx_perm"):
+        setattr(b, name, out[name].data_ptr())
+    b.dgate = out["dgate"].data_ptr() if out.get("dgate") is not None else None
+    wsb = int(_lib.moe_backward_workspace_size(ctypes.byref(b)))
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    b.ws = ws.data_ptr() if ws is not None else None
+    b.ws_bytes = wsb
+    _check("moe_backward", _lib.moe_backward(ctypes.byref(b), _stream()))
+    return out
+
+
+def mxfp8_quantize(x: torch.Tensor, axis: int = 1, group_offsets: torch.Tensor | None = None,
+                   q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                   max_blocks: int | None = None):
+    """OCP MXFP8 quantisation (see moe.h). axis=1 returns q [rows, cols] and
+    scale [rows, cols/32]; axis=0 returns the flat grouped, transposed,
+    block-padded q and scale sized for the worst case."""
+    rows, cols = x.shape
+    dev = x.device
+    ng = 0 if group_offsets is None else group_offsets.numel() - 1
+    if axis == 1:
+        q = q if q is not None else torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        scale = scale if scale is not None else torch.empty((rows, cols // 32), dtype=torch.uint8,
+                                                            device=dev)
+    else:
+        nb = max_blocks if max_blocks is not None else (rows // 32 + max(ng, 1))
+        q = q if q is not None else torch.empty(nb * 32 * cols, dtype=torch.uint8, device=dev)
+        scale = scale if scale is not None else torch.empty(nb * cols, dtype=torch.uint8, device=dev)
+    _check("mxfp8_quantize", _lib.mxfp8_quantize(_p(x), _dt(x), rows, cols, axis,
+                                                 _p(group_offsets), ng, _p(q), _p(scale),
+                                                 _stream()))
+    return q, scale
+
+
+# ---------------------------------------------------------------------------
+# the layer
+
+
+class MoELayer:
+    """Forward and backward of the MoE expert layer through the C ABI.
+
+    Buffers are allocated once per (T) and reused across calls, so a step
+    issues only kernel launches (no allocation, no device->host traffic)."""
+
+    def __init__(self, w1: torch.Tensor, w2: torch.Tensor, k: int):
+        self.w1, self.w2, self.k = w1, w2, k
+        self.E, h2, self.d = w1.shape
+        self.h = h2 // 2
+        self._T = None
+
+    def _alloc(self, T, dev, dt):
+        if self._T == T:
+            return
+        E, k, d, h = self.E, self.k, self.d, self.h
+        R = T * k
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.route = dict(topk_idx=torch.empty((T, k), **i32),
+                          topk_gate=torch.empty((T, k), dtype=torch.float32, device=dev),
+                          counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+                          token_pos=torch.empty((T, k), **i32), sorted_token=torch.empty(R, **i32),
+                          sorted_slot=torch.empty(R, **i32), tile_offsets=torch.empty(E + 1, **i32))
+        self.route_ws = torch.empty(max(moe_route_workspace_size(T, E, k), 1), dtype=torch.uint8,
+                                    device=dev)
+        self.x_perm = torch.empty((R, d), dtype=dt, device=dev)
+        self.ab = torch.empty((R, 2 * h), dtype=dt, device=dev)
+        self.hp = torch.empty((R, h), dtype=dt, device=dev)
+        self.y_perm = torch.empty((R, d), dtype=dt, device=dev)
+        self.out = torch.empty((T, d), dtype=dt, device=dev)
+        self.grads = None
+        self._T = T
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor) -> torch.Tensor:
+        T, d = x.shape
+        self._alloc(T, x.device, x.dtype)
+        r = moe_route(logits, self.k, out=self.route, ws=self.route_ws)
+        moe_permute(x, r["token_pos"], self.x_perm)
+        moe_grouped_gemm(MOE_GG_FWD, self.x_perm, self.w1, self.ab, r["offsets"],
+                         MOE_EPI_SWIGLU_FWD, N=2 * self.h, K=d, aux_out=self.hp)
+        moe_grouped_gemm(MOE_GG_FWD, self.hp, self.w2, self.y_perm, r["offsets"], N=d, K=self.h)
+        moe_combine(self.y_perm, r["topk_gate"], r["token_pos"], self.out)
+        return self.out
+
+    def saved(self) -> dict:
+        r = self.route
+        return dict(x_perm=self.x_perm, ab=self.ab, hp=self.hp, y_perm=self.y_perm,
+                    topk_gate=r["topk_gate"], topk_idx=r["topk_idx"], token_pos=r["token_pos"],
+                    offsets=r["offsets"], w1=self.w1, w2=self.w2)
+
+    def backward(self, dout: torch.Tensor) -> dict:
+        self.grads = moe_backward(self.saved(), dout, self.E, self.k, self.d, self.h,
+                                  out=self.grads)
+        return self.grads

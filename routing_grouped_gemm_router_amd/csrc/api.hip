@@ -1,0 +1,238 @@
+// api.hip -- the C ABI of libmoe: argument checks, then kernel launches.
+//
+// Every entry point validates host-visible scalars and pointers first and
+// returns before enqueueing anything on a validation error; it never reads
+// device memory, allocates, copies device->host or synchronises.
+#include <string.h>
+
+#include "common.h"
+
+namespace moe {
+
+moe_status route_launch(const float *logits, int64_t T, int E, int k, int tile_m,
+                        int32_t *topk_idx, float *topk_gate, int32_t *counts, int32_t *offsets,
+                        int32_t *token_pos, int32_t *sorted_token, int32_t *sorted_slot,
+                        int32_t *tile_offsets, void *ws, hipStream_t s);
+moe_status permute_launch(const void *x, const uint8_t *x_scale, moe_dtype dt, int64_t T, int d,
+                          int k, const int32_t *token_pos, void *x_perm, uint8_t *x_perm_scale,
+                          hipStream_t s);
+moe_status combine_launch(const void *y, moe_dtype dt, const float *gate,
+                          const int32_t *token_pos, int64_t T, int d, int k, void *out,
+                          bool unit_gate, hipStream_t s);
+moe_status combine_bwd_launch(const void *dout, const void *y, moe_dtype dt, const float *gate,
+                              const int32_t *topk_idx, const int32_t *token_pos, int64_t T,
+                              int d, int k, int E, void *dy, float *dlogits, float *dgate,
+                              hipStream_t s);
+moe_status gemm_launch(const moe_gemm_desc *d, hipStream_t s);
+moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
+                                 int axis, const int32_t *group_offsets, int n_groups,
+                                 uint8_t *q, uint8_t *scale, hipStream_t s);
+
+int num_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+static bool routing_shape_ok(int64_t T, int32_t E, int32_t k) {
+    return T >= 0 && E >= 1 && E <= 256 && k >= 1 && k <= 8 && k <= E &&
+           T * (int64_t)k < ((int64_t)1 << 31);
+}
+
+static bool width_ok(int32_t w) { return w >= 32 && w <= 16384 && w % 32 == 0; }
+
+static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char *moe_status_str(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is null";
+        case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: a size is out of range or inconsistent";
+        case MOE_ERR_DTYPE: return "MOE_ERR_DTYPE: unsupported dtype/mode/epilogue";
+        case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+        case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH: the HIP runtime reported a launch error";
+        default: return "unknown moe_status";
+    }
+}
+
+int32_t moe_version(void) { return 100; }
+
+size_t moe_route_workspace_size(int64_t T, int32_t E, int32_t k) {
+    (void)k;
+    if (T < 0 || E < 1) return 0;
+    return round256(sizeof(int32_t) * (size_t)E * (size_t)((T + 63) / 64));
+}
+
+moe_status moe_route(const float *logits, int64_t T, int32_t E, int32_t k, int32_t tile_m,
+                     int32_t *topk_idx, float *topk_gate, int32_t *counts, int32_t *offsets,
+                     int32_t *token_pos, int32_t *sorted_token, int32_t *sorted_slot,
+                     int32_t *tile_offsets, void *ws, size_t ws_bytes, void *stream) {
+    if (!routing_shape_ok(T, E, k) || tile_m < 1) return MOE_ERR_SHAPE;
+    if (!counts || !offsets || !tile_offsets) return MOE_ERR_NULL;
+    if (T > 0 && (!logits || !topk_idx || !topk_gate || !token_pos || !sorted_token ||
+                  !sorted_slot || !ws))
+        return MOE_ERR_NULL;
+    if (T > 0 && !aligned16(logits)) return MOE_ERR_ALIGN;
+    if (ws_bytes < moe_route_workspace_size(T, E, k)) return MOE_ERR_WORKSPACE;
+    return route_launch(logits, T, E, k, tile_m, topk_idx, topk_gate, counts, offsets, token_pos,
+                        sorted_token, sorted_slot, tile_offsets, ws, (hipStream_t)stream);
+}
+
+moe_status moe_permute(const void *x, const uint8_t *x_scale, moe_dtype dt, int64_t T, int32_t d,
+                       int32_t k, const int32_t *token_pos, void *x_perm, uint8_t *x_perm_scale,
+                       void *stream) {
+    if (dt != MOE_F32 && dt != MOE_BF16 && dt != MOE_MXFP8) return MOE_ERR_DTYPE;
+    if (T < 0 || k < 1 || k > 8 || T * (int64_t)k >= ((int64_t)1 << 31) || !width_ok(d))
+        return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!x || !token_pos || !x_perm) return MOE_ERR_NULL;
+    if (dt == MOE_MXFP8 && (!x_scale || !x_perm_scale)) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_ALIGN;
+    return permute_launch(x, x_scale, dt, T, d, k, token_pos, x_perm, x_perm_scale,
+                          (hipStream_t)stream);
+}
+
+moe_status moe_combine(const void *y_perm, moe_dtype dt, const float *topk_gate,
+                       const int32_t *token_pos, int64_t T, int32_t d, int32_t k, void *out,
+                       void *stream) {
+    if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
+    if (T < 0 || k < 1 || k > 8 || T * (int64_t)k >= ((int64_t)1 << 31) || !width_ok(d))
+        return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!y_perm || !topk_gate || !token_pos || !out) return MOE_ERR_NULL;
+    if (!aligned16(y_perm) || !aligned16(out)) return MOE_ERR_ALIGN;
+    return combine_launch(y_perm, dt, topk_gate, token_pos, T, d, k, out, false,
+                          (hipStream_t)stream);
+}
+
+static moe_status check_gemm(const moe_gemm_desc *g) {
+    if (!g) return MOE_ERR_NULL;
+    if (g->mode < MOE_GG_FWD || g->mode > MOE_GG_WGRAD) return MOE_ERR_DTYPE;
+    if (g->dtype != MOE_F32 && g->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (g->epilogue == MOE_EPI_SWIGLU_FWD && g->mode != MOE_GG_FWD) return MOE_ERR_DTYPE;
+    if (g->epilogue == MOE_EPI_SWIGLU_BWD && g->mode != MOE_GG_DGRAD) return MOE_ERR_DTYPE;
+    if (g->epilogue < MOE_EPI_NONE || g->epilogue > MOE_EPI_SWIGLU_BWD) return MOE_ERR_DTYPE;
+    if (g->n_groups < 1 || g->n_groups > 256) return MOE_ERR_SHAPE;
+    if (g->rows < 0 || g->rows >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+    if (g->mode == MOE_GG_WGRAD) {
+        if (!width_ok(g->M) || !width_ok(g->N)) return MOE_ERR_SHAPE;
+    } else {
+        if (!width_ok(g->N) || !width_ok(g->K)) return MOE_ERR_SHAPE;
+        if (g->epilogue == MOE_EPI_SWIGLU_FWD && (g->N / 2) % 32) return MOE_ERR_SHAPE;
+    }
+    // with no rows, the row-indexed operands may be empty (null) buffers; WGRAD
+    // still writes its (zero) weight gradients
+    const bool rows_needed = g->rows > 0;
+    if (!g->offsets) return MOE_ERR_NULL;
+    if (!g->B && (rows_needed || g->mode != MOE_GG_WGRAD)) return MOE_ERR_NULL;
+    if (rows_needed && !g->A) return MOE_ERR_NULL;
+    if ((rows_needed || g->mode == MOE_GG_WGRAD) && !g->C) return MOE_ERR_NULL;
+    if (rows_needed && g->epilogue == MOE_EPI_SWIGLU_FWD && !g->aux_out) return MOE_ERR_NULL;
+    if (rows_needed && g->epilogue == MOE_EPI_SWIGLU_BWD && !g->aux) return MOE_ERR_NULL;
+    if ((g->A && !aligned16(g->A)) || !aligned16(g->B) || (g->C && !aligned16(g->C)))
+        return MOE_ERR_ALIGN;
+    if (g->aux && !aligned16(g->aux)) return MOE_ERR_ALIGN;
+    if (g->aux_out && !aligned16(g->aux_out)) return MOE_ERR_ALIGN;
+    if (g->ws_bytes < moe_grouped_gemm_workspace_size(g)) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+size_t moe_grouped_gemm_workspace_size(const moe_gemm_desc *g) {
+    (void)g;
+    return 0;
+}
+
+moe_status moe_grouped_gemm(const moe_gemm_desc *g, void *stream) {
+    moe_status st = check_gemm(g);
+    if (st != MOE_OK) return st;
+    if (g->rows == 0 && g->mode != MOE_GG_WGRAD) return MOE_OK;   // every group is empty
+    return gemm_launch(g, (hipStream_t)stream);
+}
+
+size_t moe_backward_workspace_size(const moe_bwd_desc *b) {
+    (void)b;
+    return 0;
+}
+
+moe_status moe_backward(const moe_bwd_desc *b, void *stream) {
+    if (!b) return MOE_ERR_NULL;
+    if (b->dtype != MOE_F32 && b->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (!routing_shape_ok(b->T, b->E, b->k) || !width_ok(b->d) || !width_ok(b->h))
+        return MOE_ERR_SHAPE;
+    if (!b->dw1 || !b->dw2 || !b->offsets || !b->w1 || !b->w2) return MOE_ERR_NULL;
+    const bool any = b->T > 0;
+    if (any && (!b->x_perm || !b->ab || !b->hp || !b->y_perm || !b->topk_gate || !b->topk_idx ||
+                !b->token_pos || !b->dout || !b->dx || !b->dlogits || !b->dy_perm || !b->dab ||
+                !b->dx_perm))
+        return MOE_ERR_NULL;
+    const void *al[] = {b->x_perm, b->ab, b->hp, b->y_perm, b->w1, b->w2, b->dout, b->dx,
+                        b->dw1, b->dw2, b->dy_perm, b->dab, b->dx_perm};
+    for (const void *p : al)
+        if (p && !aligned16(p)) return MOE_ERR_ALIGN;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t R = b->T * b->k;
+    moe_status st = combine_bwd_launch(b->dout, b->y_perm, b->dtype, b->topk_gate, b->topk_idx,
+                                       b->token_pos, b->T, b->d, b->k, b->E, b->dy_perm,
+                                       b->dlogits, b->dgate, s);
+    if (st != MOE_OK) return st;
+    moe_gemm_desc g;
+    memset(&g, 0, sizeof(g));
+    g.dtype = b->dtype;
+    g.n_groups = b->E;
+    g.rows = R;
+    g.offsets = b->offsets;
+    // GEMM2 dgrad with the SwiGLU backward: dAB from dy_perm . W2[e]
+    g.mode = MOE_GG_DGRAD; g.epilogue = MOE_EPI_SWIGLU_BWD;
+    g.N = b->h; g.K = b->d;
+    g.A = b->dy_perm; g.B = b->w2; g.C = b->dab; g.aux = b->ab;
+    if (R > 0 && (st = gemm_launch(&g, s)) != MOE_OK) return st;
+    // GEMM2 wgrad: dW2[e] = dy^T H'
+    g.mode = MOE_GG_WGRAD; g.epilogue = MOE_EPI_NONE; g.aux = nullptr;
+    g.M = b->d; g.N = b->h; g.K = 0;
+    g.A = b->dy_perm; g.B = b->hp; g.C = b->dw2;
+    if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
+    // GEMM1 dgrad: dx_perm = dAB . W1[e]
+    g.mode = MOE_GG_DGRAD; g.M = 0; g.N = b->d; g.K = 2 * b->h;
+    g.A = b->dab; g.B = b->w1; g.C = b->dx_perm;
+    if (R > 0 && (st = gemm_launch(&g, s)) != MOE_OK) return st;
+    // GEMM1 wgrad: dW1[e] = dAB^T x
+    g.mode = MOE_GG_WGRAD; g.M = 2 * b->h; g.N = b->d; g.K = 0;
+    g.A = b->dab; g.B = b->x_perm; g.C = b->dw1;
+    if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
+    // unpermute backward: dX[t] = sum_j dx_perm[token_pos[t, j]]
+    return combine_launch(b->dx_perm, b->dtype, nullptr, b->token_pos, b->T, b->d, b->k, b->dx,
+                          true, s);
+}
+
+moe_status mxfp8_quantize(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
+                          int32_t axis, const int32_t *group_offsets, int32_t n_groups,
+                          uint8_t *q, uint8_t *scale, void *stream) {
+    if (in_dt != MOE_F32 && in_dt != MOE_BF16) return MOE_ERR_DTYPE;
+    if (rows < 0 || cols < 32 || cols % 32 || rows >= ((int64_t)1 << 31) ||
+        cols >= ((int64_t)1 << 20))
+        return MOE_ERR_SHAPE;
+    if (axis != 0 && axis != 1) return MOE_ERR_SHAPE;
+    if (axis == 0 && group_offsets && (n_groups < 1 || n_groups > 1024)) return MOE_ERR_SHAPE;
+    if (rows == 0) return MOE_OK;
+    if (!in || !q || !scale) return MOE_ERR_NULL;
+    if (!aligned16(in) || !aligned16(q)) return MOE_ERR_ALIGN;
+    return mxfp8_quantize_launch(in, in_dt, rows, cols, axis, group_offsets,
+                                 group_offsets ? n_groups : 1, q, scale, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+"""The C ABI (no GPU needed): the library loads, exports every function that
+include/moe.h declares, and rejects bad arguments with the documented status
+before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "routing_grouped_gemm_router_amd", "libmoe.so")
+
+
+def declared():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted({n for n in names if n.startswith(("moe_", "mxfp8_"))})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from routing_grouped_gemm_router_amd.build import build
+        build()
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for n in ("moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_backward",
+              "mxfp8_quantize"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    lib.moe_status_str.restype = ctypes.c_char_p
+    for s in range(7):
+        assert lib.moe_status_str(s).startswith(b"MOE_")
+    lib.moe_version.restype = ctypes.c_int32
+    assert lib.moe_version() == 100
+
+
+def test_validation_without_gpu(lib):
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    lib.moe_route.argtypes = [P, I64, I32, I32, I32] + [P] * 9 + [SZ, P]
+    fake = ctypes.c_void_p(0x100000)      # never dereferenced: validation fails first
+    nul = ctypes.c_void_p(0)
+    args = lambda T, E, k, ws=1 << 20, logits=fake, counts=fake: (
+        logits, T, E, k, 128, fake, fake, counts, fake, fake, fake, fake, fake, fake, ws, nul)
+    assert lib.moe_route(*args(16, 8, 9)) == 2          # k > E
+    assert lib.moe_route(*args(16, 300, 2)) == 2        # E > 256
+    assert lib.moe_route(*args(1 << 30, 8, 4)) == 2     # T*k >= 2^31
+    assert lib.moe_route(*args(16, 8, 2, logits=nul)) == 1
+    assert lib.moe_route(*args(16, 8, 2, counts=nul)) == 1
+    assert lib.moe_route(*args(16, 8, 2, ws=3)) == 5    # workspace too small
+    unaligned = ctypes.c_void_p(0x100004)
+    assert lib.moe_route(*args(16, 8, 2, logits=unaligned)) == 4
+    lib.moe_route_workspace_size.argtypes = [I64, I32, I32]
+    lib.moe_route_workspace_size.restype = SZ
+    assert lib.moe_route_workspace_size(16384, 128, 4) == 4 * 128 * 256
+    lib.moe_permute.argtypes = [P, P, I32, I64, I32, I32, P, P, P, P]
+    assert lib.moe_permute(fake, nul, 1, 16, 48, 2, fake, fake, nul, nul) == 2   # d % 32
+    assert lib.moe_permute(fake, nul, 7, 16, 64, 2, fake, fake, nul, nul) == 3   # dtype
+    assert lib.moe_permute(fake, nul, 2, 16, 64, 2, fake, fake, nul, nul) == 1   # MXFP8 scales
+    assert lib.moe_permute(nul, nul, 1, 0, 64, 2, nul, nul, nul, nul) == 0       # T = 0: no-op
+    lib.moe_combine.argtypes = [P, I32, P, P, I64, I32, I32, P, P]
+    assert lib.moe_combine(fake, 2, fake, fake, 16, 64, 2, fake, nul) == 3       # no MXFP8 combine
+    lib.mxfp8_quantize.argtypes = [P, I32, I64, I64, I32, P, I32, P, P, P]
+    assert lib.mxfp8_quantize(fake, 1, 64, 40, 1, nul, 0, fake, fake, nul) == 2
+    assert lib.mxfp8_quantize(fake, 1, 64, 64, 2, nul, 0, fake, fake, nul) == 2
+
+
+def test_gemm_descriptor_validation(lib):
+    import sys
+    sys.path.insert(0, ROOT)
+    # the binding needs torch only for device buffers; the descriptor layout is plain ctypes
+    from routing_grouped_gemm_router_amd import GemmDesc, BwdDesc
+    lib.moe_grouped_gemm.argtypes = [ctypes.POINTER(GemmDesc), ctypes.c_void_p]
+    g = GemmDesc()
+    g.mode, g.dtype, g.epilogue, g.n_groups, g.rows = 0, 1, 0, 8, 64
+    g.N, g.K = 64, 64
+    g.offsets = g.A = g.B = g.C = 0x100000
+    bad = GemmDesc.from_buffer_copy(g)
+    bad.mode = 7
+    assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 3
+    bad = GemmDesc.from_buffer_copy(g)
+    bad.epilogue = 2                          # SwiGLU backward needs DGRAD
+    assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 3
+    bad = GemmDesc.from_buffer_copy(g)
+    bad.n_groups = 0
+    assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 2
+    bad = GemmDesc.from_buffer_copy(g)
+    bad.K = 48
+    assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 2
+    bad = GemmDesc.from_buffer_copy(g)
+    bad.A = 0
+    assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 1
+    bad = GemmDesc.from_buffer_copy(g)
+    bad.epilogue = 1                          # SwiGLU forward needs aux_out
+    assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 1
+    lib.moe_backward.argtypes = [ctypes.POINTER(BwdDesc), ctypes.c_void_p]
+    b = BwdDesc()
+    b.dtype, b.d, b.h, b.E, b.k, b.T = 1, 64, 64, 8, 2, 16
+    assert lib.moe_backward(ctypes.byref(b), None) == 1
+    b.dtype = 2
+    assert lib.moe_backward(ctypes.byref(b), None) == 3
