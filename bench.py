@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--workload", default="e128_bf16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=256,
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens in the oracle's bounded sample")
     ap.add_argument("--breakdown", action="store_true",
                     help="also time every ABI call separately (stderr)")

@@ -29,6 +29,7 @@
 //    same registers, so H' = silu(a) * b is formed from the fp32
 //    accumulators); SwiGLU backward (reads the stored a, b).
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 
@@ -83,188 +84,345 @@ MOE_DEV int find_group(const int32_t *s_tile, int E, int mt) {
 MOE_DEV float silu_f(float a) { return a / (1.f + __expf(-a)); }
 
 // ---------------------------------------------------------------------------
+// XCD-aware tile schedule
+//
+// MI355X has 8 XCDs with a private L2 each, and consecutive workgroup ids go
+// to consecutive XCDs. The persistent grid (a multiple of 8 workgroups) is
+// therefore split per XCD: workgroup b serves XCD x = b % 8 as its (b / 8)-th
+// worker. Each expert's m-tiles are cut into chunks of at most CHM m-tiles;
+// chunk c belongs to XCD c % 8, and an XCD walks its chunks' tiles in order
+// with the n-tile fastest. The ~32 CUs of an XCD thus work on a few m-tiles
+// of one expert at a time: every activation tile and every weight panel is
+// fetched into that XCD's L2 once and served from there to all tiles that
+// need it, instead of being fetched by every XCD.
+// Correctness does not depend on the XCD mapping: every tile id is owned by
+// exactly one workgroup.
+
+constexpr int kMaxChunks = 2048;
+
+struct RowSchedule {
+    int n_tiles;      // n-tiles per m-tile
+    int chm;          // m-tiles per chunk
+    int total;        // tiles owned by this workgroup's XCD
+};
+
+// s_tile: exclusive prefix of m-tiles per group (from build_tile_table).
+// Builds s_chunk (chunk prefix per group, E+1) and s_xpre (tile prefix over
+// this XCD's chunks, up to kMaxChunks/8 + 1 entries). blockDim.x >= 256.
+MOE_DEV RowSchedule build_row_schedule(const int32_t *s_tile, int E, int n_tiles, int xcd,
+                                       int32_t *s_chunk, int32_t *s_xpre) {
+    const int tid = threadIdx.x;
+    const int mt_total = s_tile[E];
+    // chunk size: at least 8 m-tiles, more when needed to stay within kMaxChunks
+    const int chm = max(8, (mt_total + (kMaxChunks - 256) - 1) / (kMaxChunks - 256));
+    int32_t nc = 0;
+    if (tid < E) nc = (s_tile[tid + 1] - s_tile[tid] + chm - 1) / chm;
+    if (tid < 256) s_chunk[tid + 1] = nc;
+    if (tid == 0) s_chunk[0] = 0;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        int32_t v = (tid < 256 && tid >= o) ? s_chunk[tid + 1 - o] : 0;
+        __syncthreads();
+        if (tid < 256) s_chunk[tid + 1] += v;
+        __syncthreads();
+    }
+    const int C = s_chunk[E];
+    const int cx = C > xcd ? (C - xcd + 7) / 8 : 0;     // chunks of this XCD (<= 256)
+    int32_t t = 0;
+    if (tid < cx) {
+        const int c = xcd + 8 * tid;
+        const int e = find_group(s_chunk, E, c);
+        const int ci = c - s_chunk[e];
+        const int mt_e = s_tile[e + 1] - s_tile[e];
+        t = min(chm, mt_e - ci * chm) * n_tiles;
+    }
+    if (tid < 256) s_xpre[tid + 1] = t;
+    if (tid == 0) s_xpre[0] = 0;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        int32_t v = (tid < 256 && tid >= o) ? s_xpre[tid + 1 - o] : 0;
+        __syncthreads();
+        if (tid < 256) s_xpre[tid + 1] += v;
+        __syncthreads();
+    }
+    RowSchedule r;
+    r.n_tiles = n_tiles;
+    r.chm = chm;
+    r.total = s_xpre[cx];
+    (void)cx;
+    return r;
+}
+
+// position p of this XCD's list -> (group e, m-tile index within e, n-tile)
+MOE_DEV void decode_row_tile(const RowSchedule &rs, const int32_t *s_chunk,
+                             const int32_t *s_xpre, int E, int xcd, int p, int &e, int &mt_e,
+                             int &nt) {
+    int lo = 0, hi = kMaxChunks / 8;      // largest lc with s_xpre[lc] <= p
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (s_xpre[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    // entries past this XCD's chunk count repeat the total, which is > p
+    const int c = xcd + 8 * lo;
+    const int o = p - s_xpre[lo];
+    e = find_group(s_chunk, E, c);
+    mt_e = (c - s_chunk[e]) * rs.chm + o / rs.n_tiles;
+    nt = o % rs.n_tiles;
+}
+
+// ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 
 constexpr int kBK = 64;
 
-MOE_DEV int swz(int row, int kc) { return row * 8 + (kc ^ (row & 7)); }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define MOE_LDS __attribute__((address_space(3)))
 
-// K-contiguous operand tile [R rows][64 k] -> registers. row_ptr(r) gives the
-// address of the row's element k=0 (or null when the row is out of range).
-template <int R, int NT>
-struct KcStage {
-    static constexpr int CH = R * 8 / NT;
-    static_assert(CH >= 1 && R * 8 % NT == 0, "tile/thread mismatch");
-    uint4 v[CH];
+// Source of the LDS copies of masked chunks (rows past a group's end, the K
+// tail, columns past N): zero-initialised device memory.
+__device__ uint4 g_zero_chunk[64] = {};
+
+// K-layout LDS tile: [R rows][64 k] bf16 (128-byte rows). LDS has 64 4-byte
+// banks, i.e. two 128-byte rows per bank cycle; XOR-swizzling the 16-byte
+// chunks with (row/2) % 8 puts the 16 rows that a ds_read_b128 serves per
+// cycle on 16 different 16-byte bank groups (measured: 2x the read rate of a
+// row % 8 swizzle, 7x that of no swizzle).
+MOE_DEV int kl_swz(int row) { return (row >> 1) & 7; }
+MOE_DEV int kl_chunk(int row, int kc) { return row * 8 + (kc ^ kl_swz(row)); }
+
+// MN-layout LDS tile: [64 k][R] bf16, i.e. the global tile copied as is.
+// Chunk c of row k sits at c ^ ((k & 3) << 2): the four k rows that one
+// transpose read touches fall in four different 64-byte bank windows.
+template <int R>
+MOE_DEV int mn_chunk(int k, int c) { return k * (R / 8) + (c ^ ((k & 3) << 2)); }
+
+// Wait until at most N vector-memory instructions of this wave are in flight
+// (loads complete in issue order).
+template <int N>
+MOE_DEV void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier for the LDS pipeline: this wave's LDS reads have
+// completed (lgkmcnt(0)), then s_barrier, then an acquire fence on LDS only so
+// later LDS reads stay below the barrier. No global-memory fence: that would
+// drain the LDS copies that are still in flight for later stages.
+MOE_DEV void lds_sync() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Copy 16 bytes per lane from global memory straight into LDS: lane l's
+// bytes land at lds_wave_base + 16 * l (lds_wave_base is wave-uniform, passed
+// in M0). Issued through inline asm so that the only waits on these copies
+// are the explicit ones of the pipeline below (wait_vmem + lds_sync); the
+// instruction has no result registers, and the "memory" clobber keeps LDS
+// reads from moving across it.
+MOE_DEV void dma16(const void *src, const uint4 *lds_wave_base) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)(const MOE_LDS void *)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(m0v)
+                 : "memory", "m0");
+}
+
+// One operand tile per stage, copied HBM -> LDS by global_load_lds_dwordx4:
+// every instruction writes 64 lanes x 16 bytes to a contiguous 1 KiB of LDS,
+// so each lane picks the global chunk that belongs at its LDS position.
+// NW waves share the copy; IPW instructions per wave.
+//
+// KL = true : K-layout tile [R rows][64 k]; src rows are K-contiguous.
+// KL = false: MN-layout tile [64 k][R cols]; src is [k][ld], cols contiguous.
+template <int R, bool KL, int NW>
+struct DmaTile {
+    static constexpr int CHUNKS = R * 8;
+    static constexpr int IPW = CHUNKS / 64 / NW;
+    static_assert(IPW >= 1 && CHUNKS % (64 * NW) == 0, "tile/wave mismatch");
+    static_assert(KL || R >= 128, "MN-layout swizzle needs >= 16 chunks per row");
+    // per lane and instruction: source of k-step 0 (nullptr = always zero) and
+    // the k offset (KL: chunk's k; MN: chunk's row) for the K-range check
+    const uint16_t *src[IPW];
+    int kofs[IPW];
+    int64_t kstride;        // elements to advance per k-step of 64
+
+    // KL: row_ptr(r) -> address of element k = 0 of tile row r, or nullptr
     template <typename RowFn>
-    MOE_DEV void load(RowFn row_ptr, int k0, int K) {
-        const int tid = threadIdx.x;
+    MOE_DEV void setup_kl(RowFn row_ptr, int wave, int lane) {
 #pragma unroll
-        for (int i = 0; i < CH; i++) {
-            const int id = tid + i * NT, row = id >> 3, kc = id & 7;
-            const uint16_t *p = row_ptr(row);
-            const int kk = k0 + kc * 8;
-            if (p != nullptr && kk < K)
-                v[i] = *reinterpret_cast<const uint4 *>(p + kk);
-            else
-                v[i] = make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < IPW; i++) {
+            const int p = (wave * IPW + i) * 64 + lane;
+            const int row = p >> 3, kc = (p & 7) ^ kl_swz(row);
+            const uint16_t *rp = row_ptr(row);
+            src[i] = rp ? rp + kc * 8 : nullptr;
+            kofs[i] = kc * 8;
+        }
+        kstride = kBK;
+    }
+    // MN: base = element (k = 0, col 0) of the tile, ld = row pitch,
+    // cvalid = valid columns
+    MOE_DEV void setup_mn(const uint16_t *base, int64_t ld, int cvalid, int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < IPW; i++) {
+            const int p = (wave * IPW + i) * 64 + lane;
+            const int k = p / (R / 8), c = (p % (R / 8)) ^ ((k & 3) << 2);
+            src[i] = c * 8 < cvalid ? base + (int64_t)k * ld + c * 8 : nullptr;
+            kofs[i] = k;
+        }
+        kstride = kBK * ld;
+    }
+    // enqueue the copy of k-step kt (k range limit klen) into stage buffer lds
+    MOE_DEV void issue(uint4 *lds, int kt, int klen, int wave) const {
+        const int k0 = kt * kBK;
+#pragma unroll
+        for (int i = 0; i < IPW; i++) {
+            const bool ok = src[i] != nullptr && k0 + kofs[i] < klen;
+            const void *s = ok ? (const void *)(src[i] + kt * kstride)
+                               : (const void *)&g_zero_chunk[threadIdx.x & 63];
+            dma16(s, lds + (wave * IPW + i) * 64);
         }
     }
-    MOE_DEV void store(uint4 *lds) const {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < CH; i++) {
-            const int id = tid + i * NT, row = id >> 3, kc = id & 7;
-            lds[swz(row, kc)] = v[i];
-        }
-    }
-};
-
-// M/N-contiguous operand: global [k][ld] with the tile's R columns contiguous.
-// Each working thread loads an 8(k) x 8(col) block and transposes it.
-template <int R, int NT>
-struct McStage {
-    static constexpr int NBLK = R;                       // (64/8) * (R/8)
-    static constexpr int PER = (NBLK + NT - 1) / NT;
-    uint4 v[PER][8];
-    // base: pointer to element (k=0 of the tile, col=0 of the tile);
-    // ld: row pitch in elements; kvalid: rows [0, kvalid) are valid;
-    // cvalid: columns [0, cvalid) are valid (multiple of 8).
-    MOE_DEV void load(const uint16_t *base, int64_t ld, int k0, int kvalid, int cvalid) {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < PER; i++) {
-            const int b = tid + i * NT;
-            const int mb = b % (R / 8), kb = b / (R / 8);
-            const bool okc = (b < NBLK) && (mb * 8 < cvalid);
-#pragma unroll
-            for (int ii = 0; ii < 8; ii++) {
-                const int kr = k0 + kb * 8 + ii;
-                if (okc && kr < kvalid)
-                    v[i][ii] = *reinterpret_cast<const uint4 *>(base + (int64_t)kr * ld + mb * 8);
-                else
-                    v[i][ii] = make_uint4(0, 0, 0, 0);
-            }
-        }
-    }
-    MOE_DEV void store(uint4 *lds) const {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < PER; i++) {
-            const int b = tid + i * NT;
-            if (b >= NBLK) continue;
-            const int mb = b % (R / 8), kb = b / (R / 8);
-            const uint32_t *w = reinterpret_cast<const uint32_t *>(v[i]);   // w[ii*4 + c]
-#pragma unroll
-            for (int c = 0; c < 4; c++) {
-                uint4 lo, hi;   // columns 2c and 2c+1, eight k values each
-                uint32_t *l = reinterpret_cast<uint32_t *>(&lo);
-                uint32_t *hh = reinterpret_cast<uint32_t *>(&hi);
-#pragma unroll
-                for (int p = 0; p < 4; p++) {
-                    const uint32_t a = w[(2 * p) * 4 + c], bq = w[(2 * p + 1) * 4 + c];
-                    l[p] = (a & 0xffffu) | (bq << 16);
-                    hh[p] = (a >> 16) | (bq & 0xffff0000u);
-                }
-                const int r0 = mb * 8 + 2 * c;
-                lds[swz(r0, kb)] = lo;
-                lds[swz(r0 + 1, kb)] = hi;
-            }
+    // MFMA operand for rows/cols r0..r0+31, k slice kk (16 wide):
+    // lanes 0-31 get k 16*kk..+7, lanes 32-63 k 16*kk+8..+15
+    MOE_DEV static bf16x8 frag(const uint4 *lds, int r0, int kk, int lane) {
+        if constexpr (KL) {
+            return __builtin_bit_cast(bf16x8, lds[kl_chunk(r0 + (lane & 31), kk * 2 + (lane >> 5))]);
+        } else {
+            // ds_read_b64_tr_b16: within a 16-lane group, lane i receives element
+            // (i % 4) of the 8-byte segments read by lanes 4j + i/4, j = 0..3. Lane
+            // s reads columns m0 + 4*(s%4)..+3 of row k0 + s/4, so lane i ends up
+            // with column m0 + i at rows k0..k0+3.
+            const int grp = lane >> 4, s = lane & 15;
+            const int m = r0 + (grp & 1) * 16 + 4 * (s & 3);
+            const int k = kk * 16 + (grp >> 1) * 8 + (s >> 2);
+            const char *base = reinterpret_cast<const char *>(lds);
+            const int o0 = mn_chunk<R>(k, m >> 3) * 16 + (m & 7) * 2;
+            const int o1 = mn_chunk<R>(k + 4, m >> 3) * 16 + (m & 7) * 2;
+            v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS v4i16 *)(base + o0));
+            v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS v4i16 *)(base + o1));
+            typedef short v8i16 __attribute__((ext_vector_type(8)));
+            v8i16 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+            return __builtin_bit_cast(bf16x8, r);
         }
     }
 };
 
-template <int MODE, int EPI, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM *WN * 64) void gg_bf16(GemmArgs g) {
-    constexpr int NT = WM * WN * 64;
+// STAGES LDS buffers; the copy of k-step kt+STAGES-1 is enqueued while k-step
+// kt is multiplied, so STAGES-1 copies are in flight behind the MFMAs.
+template <int MODE, int EPI, int BM, int BN, int WM, int WN, int STAGES, int WPE>
+__global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void gg_bf16(GemmArgs g) {
+    constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(TM >= 1 && TN >= 1, "wave tile");
+    static_assert(STAGES >= 2, "pipeline depth");
     static_assert(EPI != MOE_EPI_SWIGLU_FWD || TN % 2 == 0, "SwiGLU pairs gate/up sub-tiles");
-    constexpr bool A_KC = MODE != MOE_GG_WGRAD;
-    constexpr bool B_KC = MODE == MOE_GG_FWD;
+    constexpr bool A_KL = MODE != MOE_GG_WGRAD;
+    constexpr bool B_KL = MODE == MOE_GG_FWD;
+    using AT = DmaTile<BM, A_KL, NW>;
+    using BT = DmaTile<BN, B_KL, NW>;
+    constexpr int IPS = AT::IPW + BT::IPW;     // copy instructions per wave per stage
 
-    __shared__ __attribute__((aligned(16))) uint4 lds_a[2][BM * 8];
-    __shared__ __attribute__((aligned(16))) uint4 lds_b[2][BN * 8];
+    // LDS pool: STAGES x (A tile | B tile) during the K loop; reused after it
+    // to stage the output tile for coalesced stores (the copies into LDS are
+    // issued through inline asm, so the compiler tracks no LDS writes of its
+    // own here and a single array serves every stage)
+    constexpr int STAGE_U4 = (BM + BN) * 8;
+    constexpr bool F32_STAGE = MODE == MOE_GG_WGRAD || EPI == MOE_EPI_SWIGLU_BWD;
+    constexpr int PF = BN * 4 + 32;      // fp32 staging pitch (bytes)
+    constexpr int PB = BN * 2 + 16;      // bf16 staging pitch (bytes)
+    constexpr int PH = BN + 16;          // H' staging pitch (bytes)
+    constexpr int EPI_BYTES = F32_STAGE ? BM * PF
+                            : (EPI == MOE_EPI_SWIGLU_FWD ? BM * PB + BM * PH : BM * PB);
+    constexpr int POOL_U4 = STAGES * STAGE_U4 > (EPI_BYTES + 15) / 16 ? STAGES * STAGE_U4
+                                                                       : (EPI_BYTES + 15) / 16;
+    __shared__ __attribute__((aligned(1024))) uint4 lds_pool[POOL_U4];
+    static_assert(STAGES <= 3, "at most three stages");
     __shared__ int32_t s_off[257];
     __shared__ int32_t s_tile[257];
+    __shared__ int32_t s_chunk[257];
+    __shared__ int32_t s_xpre[kMaxChunks / 8 + 1];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int E = g.E;
 
+    const int xcd = blockIdx.x & 7, worker = blockIdx.x >> 3, workers = gridDim.x >> 3;
     int n_tiles, total;
+    RowSchedule rs;
     if constexpr (MODE == MOE_GG_WGRAD) {
+        // whole experts per XCD: expert e on XCD e % 8, its tiles n-fastest
         if (tid <= E) s_off[tid] = g.offsets[tid];
         __syncthreads();
         n_tiles = (g.N + BN - 1) / BN;
-        total = E * ((g.M + BM - 1) / BM) * n_tiles;
+        const int per_e = ((g.M + BM - 1) / BM) * n_tiles;
+        total = (E > xcd ? (E - xcd + 7) / 8 : 0) * per_e;
     } else {
-        const int mt = build_tile_table(g.offsets, E, BM, s_off, s_tile);
+        build_tile_table(g.offsets, E, BM, s_off, s_tile);
         n_tiles = (EPI == MOE_EPI_SWIGLU_FWD) ? (g.h + BN / 2 - 1) / (BN / 2)
                                               : (g.N + BN - 1) / BN;
-        total = mt * n_tiles;
+        rs = build_row_schedule(s_tile, E, n_tiles, xcd, s_chunk, s_xpre);
+        total = rs.total;
     }
 
     const uint16_t *A = reinterpret_cast<const uint16_t *>(g.A);
     const uint16_t *B = reinterpret_cast<const uint16_t *>(g.B);
 
-    using AStageT = typename std::conditional<A_KC, KcStage<BM, NT>, McStage<BM, NT>>::type;
-    using BStageT = typename std::conditional<B_KC, KcStage<BN, NT>, McStage<BN, NT>>::type;
-
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    for (int pos = worker; pos < total; pos += workers) {
         // ---- decode the tile
         int e, row0 = 0, row_end = 0, m0 = 0, n0, nt, klen;
         if constexpr (MODE == MOE_GG_WGRAD) {
             const int mtiles = (g.M + BM - 1) / BM;
-            nt = tile % n_tiles;
-            const int rest = tile / n_tiles;
-            const int mtl = rest % mtiles;
-            e = rest / mtiles;
-            m0 = mtl * BM;
+            const int per_e = mtiles * n_tiles;
+            e = xcd + 8 * (pos / per_e);
+            const int t = pos % per_e;
+            nt = t % n_tiles;
+            m0 = (t / n_tiles) * BM;
             row0 = s_off[e];
             klen = s_off[e + 1] - row0;     // reduction over the group's rows
         } else {
-            nt = tile % n_tiles;
-            const int mt = tile / n_tiles;
-            e = find_group(s_tile, E, mt);
-            row0 = s_off[e] + (mt - s_tile[e]) * BM;
+            int mt_e;
+            decode_row_tile(rs, s_chunk, s_xpre, E, xcd, pos, e, mt_e, nt);
+            row0 = s_off[e] + mt_e * BM;
             row_end = s_off[e + 1];
             klen = g.K;
         }
         n0 = nt * BN;
 
-        // ---- operand row pointers
-        auto a_row = [&](int r) -> const uint16_t * {
-            const int gr = row0 + r;
-            return gr < row_end ? A + (int64_t)gr * g.K : nullptr;
-        };
-        auto b_row = [&](int n) -> const uint16_t * {
-            // FWD: B[e] is [N, K]; SwiGLU lays the panel out per wave as
-            // [gate rows | up rows] of the same hidden units
-            int wrow;
-            if constexpr (EPI == MOE_EPI_SWIGLU_FWD) {
-                const int wc = n / WTN, off = n % WTN, half = WTN / 2;
-                const int j = nt * (BN / 2) + wc * half + (off % half);
-                if (j >= g.h) return nullptr;
-                wrow = off < half ? j : g.h + j;
-            } else {
-                wrow = n0 + n;
-                if (wrow >= g.N) return nullptr;
-            }
-            return B + ((int64_t)e * g.N + wrow) * g.K;
-        };
-
-        AStageT sa;
-        BStageT sb;
-        auto load_stage = [&](int k0) {
-            if constexpr (A_KC) sa.load(a_row, k0, klen);
-            else sa.load(A + (int64_t)row0 * g.M + m0, g.M, k0, klen, g.M - m0);
-            if constexpr (MODE == MOE_GG_FWD) sb.load(b_row, k0, klen);
-            else if constexpr (MODE == MOE_GG_DGRAD)
-                sb.load(B + (int64_t)e * g.K * g.N + n0, g.N, k0, klen, g.N - n0);
-            else sb.load(B + (int64_t)row0 * g.N + n0, g.N, k0, klen, g.N - n0);
-        };
+        AT ta;
+        BT tb;
+        if constexpr (A_KL) {
+            ta.setup_kl([&](int r) -> const uint16_t * {
+                const int gr = row0 + r;
+                return gr < row_end ? A + (int64_t)gr * g.K : nullptr;
+            }, wave, lane);
+        } else {
+            ta.setup_mn(A + (int64_t)row0 * g.M + m0, g.M, g.M - m0, wave, lane);
+        }
+        if constexpr (MODE == MOE_GG_FWD) {
+            tb.setup_kl([&](int n) -> const uint16_t * {
+                // B[e] is [N, K]; with SwiGLU each wave's panel is laid out as
+                // [gate rows | up rows] of the same hidden units
+                int wrow;
+                if constexpr (EPI == MOE_EPI_SWIGLU_FWD) {
+                    const int wc = n / WTN, off = n % WTN, half = WTN / 2;
+                    const int j = nt * (BN / 2) + wc * half + (off % half);
+                    if (j >= g.h) return nullptr;
+                    wrow = off < half ? j : g.h + j;
+                } else {
+                    wrow = n0 + n;
+                    if (wrow >= g.N) return nullptr;
+                }
+                return B + ((int64_t)e * g.N + wrow) * g.K;
+            }, wave, lane);
+        } else if constexpr (MODE == MOE_GG_DGRAD) {
+            tb.setup_mn(B + (int64_t)e * g.K * g.N + n0, g.N, g.N - n0, wave, lane);
+        } else {
+            tb.setup_mn(B + (int64_t)row0 * g.N + n0, g.N, g.N - n0, wave, lane);
+        }
 
         f32x16 acc[TM][TN];
 #pragma unroll
@@ -275,119 +433,161 @@ __global__ __launch_bounds__(WM *WN * 64) void gg_bf16(GemmArgs g) {
                 for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
         const int nk = (klen + kBK - 1) / kBK;
-        if (nk > 0) {
-            load_stage(0);
-            sa.store(lds_a[0]);
-            sb.store(lds_b[0]);
-            __syncthreads();
-        }
-        for (int kt = 0; kt < nk; kt++) {
-            const int cur = kt & 1;
-            if (kt + 1 < nk) load_stage((kt + 1) * kBK);
-            const uint4 *la = lds_a[cur];
-            const uint4 *lb = lds_b[cur];
+        auto bufs = [&](auto I) {
+            constexpr int i = decltype(I)::value;
+            return std::make_pair(lds_pool + i * STAGE_U4, lds_pool + i * STAGE_U4 + BM * 8);
+        };
+        auto issue = [&](auto I, int kt) {
+            auto bb = bufs(I);
+            ta.issue(bb.first, kt, klen, wave);
+            tb.issue(bb.second, kt, klen, wave);
+        };
+        // one K step with stage buffer CUR (compile time)
+        auto step = [&](auto CUR, int kt) {
+            constexpr int cur = decltype(CUR)::value;
+            constexpr int nb = (cur + STAGES - 1) % STAGES;
+            // copies of later stages may stay in flight; k-step kt's must be done
+            if (kt + STAGES - 2 < nk) wait_vmem<(STAGES - 2) * IPS>();
+            else wait_vmem<0>();
+            lds_sync();
+            if (kt + STAGES - 1 < nk) issue(std::integral_constant<int, nb>(), kt + STAGES - 1);
+            auto bb = bufs(CUR);
+            const uint4 *sa = bb.first;
+            const uint4 *sb = bb.second;
 #pragma unroll
             for (int kk = 0; kk < kBK / 16; kk++) {
-                const int kc = kk * 2 + (lane >> 5);
                 bf16x8 fa[TM], fb[TN];
 #pragma unroll
-                for (int i = 0; i < TM; i++) {
-                    const int r = wm * WTM + i * 32 + (lane & 31);
-                    uint4 u = la[swz(r, kc)];
-                    fa[i] = __builtin_bit_cast(bf16x8, u);
-                }
+                for (int i = 0; i < TM; i++) fa[i] = AT::frag(sa, wm * WTM + i * 32, kk, lane);
 #pragma unroll
-                for (int j = 0; j < TN; j++) {
-                    const int r = wn * WTN + j * 32 + (lane & 31);
-                    uint4 u = lb[swz(r, kc)];
-                    fb[j] = __builtin_bit_cast(bf16x8, u);
-                }
+                for (int j = 0; j < TN; j++) fb[j] = BT::frag(sb, wn * WTN + j * 32, kk, lane);
 #pragma unroll
                 for (int i = 0; i < TM; i++)
 #pragma unroll
                     for (int j = 0; j < TN; j++)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
             }
-            if (kt + 1 < nk) {
-                sa.store(lds_a[cur ^ 1]);
-                sb.store(lds_b[cur ^ 1]);
-            }
-            __syncthreads();
+        };
+        // the previous tile's LDS reads must be over before its buffers refill
+        lds_sync();
+        if (0 < nk) issue(std::integral_constant<int, 0>(), 0);
+        if constexpr (STAGES > 2)
+            if (1 < nk) issue(std::integral_constant<int, 1>(), 1);
+        for (int kt = 0; kt < nk; kt += STAGES) {
+            step(std::integral_constant<int, 0>(), kt);
+            if (kt + 1 < nk) step(std::integral_constant<int, 1>(), kt + 1);
+            if constexpr (STAGES > 2)
+                if (kt + 2 < nk) step(std::integral_constant<int, 2>(), kt + 2);
         }
 
         // ---- epilogue. acc[i][j][v] holds row (v/4)*8 + (lane/32)*4 + v%4 and
-        // column lane%32 of the wave's (i, j) 32x32 tile.
+        // column lane%32 of the wave's (i, j) 32x32 tile. The tile is first
+        // written to LDS, then copied out by rows with 16-byte accesses.
+        lds_sync();                                   // stage buffers no longer read
+        char *stg = reinterpret_cast<char *>(lds_pool);
         const int col_l = lane & 31;
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int j = 0; j < (EPI == MOE_EPI_SWIGLU_FWD ? TN / 2 : TN); j++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    const int r = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                    if constexpr (F32_STAGE) {
+                        const int c = wn * WTN + j * 32 + col_l;
+                        *reinterpret_cast<float *>(stg + r * PF + c * 4) = acc[i][j][v];
+                    } else if constexpr (EPI == MOE_EPI_SWIGLU_FWD) {
+                        const int jt = wn * (WTN / 2) + j * 32 + col_l;
+                        const float a = acc[i][j][v], b = acc[i][j + TN / 2][v];
+                        uint16_t *abr = reinterpret_cast<uint16_t *>(stg + r * PB);
+                        abr[jt] = f32_to_bf16(a);
+                        abr[BN / 2 + jt] = f32_to_bf16(b);
+                        reinterpret_cast<uint16_t *>(stg + BM * PB + r * PH)[jt] =
+                            f32_to_bf16(silu_f(a) * b);
+                    } else {
+                        const int c = wn * WTN + j * 32 + col_l;
+                        reinterpret_cast<uint16_t *>(stg + r * PB)[c] = f32_to_bf16(acc[i][j][v]);
+                    }
+                }
+        lds_sync();
+        constexpr int NT = NW * 64;
         if constexpr (MODE == MOE_GG_WGRAD) {
             float *C = reinterpret_cast<float *>(g.C) + (int64_t)e * g.M * g.N;
-#pragma unroll
-            for (int i = 0; i < TM; i++)
-#pragma unroll
-                for (int j = 0; j < TN; j++) {
-                    const int n = n0 + wn * WTN + j * 32 + col_l;
-                    if (n >= g.N) continue;
-#pragma unroll
-                    for (int v = 0; v < 16; v++) {
-                        const int m = m0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-                        if (m < g.M) C[(int64_t)m * g.N + n] = acc[i][j][v];
-                    }
-                }
-        } else if constexpr (EPI == MOE_EPI_SWIGLU_FWD) {
-            uint16_t *AB = reinterpret_cast<uint16_t *>(g.C);
-            uint16_t *HP = reinterpret_cast<uint16_t *>(g.aux_out);
-            const int h = g.h;
-#pragma unroll
-            for (int i = 0; i < TM; i++)
-#pragma unroll
-                for (int j = 0; j < TN / 2; j++) {
-                    const int jj = nt * (BN / 2) + wn * (WTN / 2) + j * 32 + col_l;
-                    if (jj >= h) continue;
-#pragma unroll
-                    for (int v = 0; v < 16; v++) {
-                        const int r = row0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-                        if (r >= row_end) continue;
-                        const float a = acc[i][j][v], b = acc[i][j + TN / 2][v];
-                        AB[(int64_t)r * 2 * h + jj] = f32_to_bf16(a);
-                        AB[(int64_t)r * 2 * h + h + jj] = f32_to_bf16(b);
-                        HP[(int64_t)r * h + jj] = f32_to_bf16(silu_f(a) * b);
-                    }
-                }
+            constexpr int CPR = BN / 4;
+            for (int it = tid; it < BM * CPR; it += NT) {
+                const int r = it / CPR, c = it % CPR;
+                const int m = m0 + r, n = n0 + c * 4;
+                if (m < g.M && n < g.N)
+                    *reinterpret_cast<uint4 *>(C + (int64_t)m * g.N + n) =
+                        *reinterpret_cast<const uint4 *>(stg + r * PF + c * 16);
+            }
         } else if constexpr (EPI == MOE_EPI_SWIGLU_BWD) {
             const uint16_t *AB = reinterpret_cast<const uint16_t *>(g.aux);
             uint16_t *dAB = reinterpret_cast<uint16_t *>(g.C);
             const int h = g.h;
+            constexpr int CPR = BN / 8;
+            for (int it = tid; it < BM * CPR; it += NT) {
+                const int r = it / CPR, c = it % CPR;
+                const int grow = row0 + r, jj = n0 + c * 8;
+                if (grow >= row_end || jj >= h) continue;
+                const uint16_t *abr = AB + (int64_t)grow * 2 * h;
+                const uint4 ua = *reinterpret_cast<const uint4 *>(abr + jj);
+                const uint4 ub = *reinterpret_cast<const uint4 *>(abr + h + jj);
+                const float4 d0 = *reinterpret_cast<const float4 *>(stg + r * PF + c * 32);
+                const float4 d1 = *reinterpret_cast<const float4 *>(stg + r * PF + c * 32 + 16);
+                const float dh[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                const uint32_t wa[4] = {ua.x, ua.y, ua.z, ua.w}, wb[4] = {ub.x, ub.y, ub.z, ub.w};
+                uint32_t oa[4], ob[4];
 #pragma unroll
-            for (int i = 0; i < TM; i++)
+                for (int q = 0; q < 4; q++) {
+                    float da2[2], db2[2];
 #pragma unroll
-                for (int j = 0; j < TN; j++) {
-                    const int jj = n0 + wn * WTN + j * 32 + col_l;
-                    if (jj >= h) continue;
-#pragma unroll
-                    for (int v = 0; v < 16; v++) {
-                        const int r = row0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-                        if (r >= row_end) continue;
-                        const float a = bf16_to_f32(AB[(int64_t)r * 2 * h + jj]);
-                        const float b = bf16_to_f32(AB[(int64_t)r * 2 * h + h + jj]);
-                        const float dh = acc[i][j][v];
-                        const float s = 1.f / (1.f + __expf(-a));
-                        dAB[(int64_t)r * 2 * h + jj] = f32_to_bf16(dh * b * s * (1.f + a * (1.f - s)));
-                        dAB[(int64_t)r * 2 * h + h + jj] = f32_to_bf16(dh * a * s);
+                    for (int hh = 0; hh < 2; hh++) {
+                        const float a = hh ? hi_bf16(wa[q]) : lo_bf16(wa[q]);
+                        const float b = hh ? hi_bf16(wb[q]) : lo_bf16(wb[q]);
+                        const float sg = 1.f / (1.f + __expf(-a));
+                        const float d = dh[2 * q + hh];
+                        da2[hh] = d * b * sg * (1.f + a * (1.f - sg));
+                        db2[hh] = d * a * sg;
                     }
+                    oa[q] = pack_bf16x2(da2[0], da2[1]);
+                    ob[q] = pack_bf16x2(db2[0], db2[1]);
                 }
+                uint16_t *dr = dAB + (int64_t)grow * 2 * h;
+                *reinterpret_cast<uint4 *>(dr + jj) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
+                *reinterpret_cast<uint4 *>(dr + h + jj) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+            }
+        } else if constexpr (EPI == MOE_EPI_SWIGLU_FWD) {
+            uint16_t *AB = reinterpret_cast<uint16_t *>(g.C);
+            uint16_t *HP = reinterpret_cast<uint16_t *>(g.aux_out);
+            const int h = g.h, j0 = nt * (BN / 2);
+            constexpr int CPR = BN / 8;               // gate half then up half
+            for (int it = tid; it < BM * CPR; it += NT) {
+                const int r = it / CPR, c = it % CPR;
+                const int grow = row0 + r;
+                const int half = c >= CPR / 2, jj = j0 + (c - half * (CPR / 2)) * 8;
+                if (grow >= row_end || jj >= h) continue;
+                *reinterpret_cast<uint4 *>(AB + (int64_t)grow * 2 * h + half * h + jj) =
+                    *reinterpret_cast<const uint4 *>(stg + r * PB + c * 16);
+            }
+            constexpr int CPH = BN / 16;
+            for (int it = tid; it < BM * CPH; it += NT) {
+                const int r = it / CPH, c = it % CPH;
+                const int grow = row0 + r, jj = j0 + c * 8;
+                if (grow >= row_end || jj >= h) continue;
+                *reinterpret_cast<uint4 *>(HP + (int64_t)grow * h + jj) =
+                    *reinterpret_cast<const uint4 *>(stg + BM * PB + r * PH + c * 16);
+            }
         } else {
             uint16_t *C = reinterpret_cast<uint16_t *>(g.C);
-#pragma unroll
-            for (int i = 0; i < TM; i++)
-#pragma unroll
-                for (int j = 0; j < TN; j++) {
-                    const int n = n0 + wn * WTN + j * 32 + col_l;
-                    if (n >= g.N) continue;
-#pragma unroll
-                    for (int v = 0; v < 16; v++) {
-                        const int r = row0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-                        if (r < row_end) C[(int64_t)r * g.N + n] = f32_to_bf16(acc[i][j][v]);
-                    }
-                }
+            constexpr int CPR = BN / 8;
+            for (int it = tid; it < BM * CPR; it += NT) {
+                const int r = it / CPR, c = it % CPR;
+                const int grow = row0 + r, n = n0 + c * 8;
+                if (grow < row_end && n < g.N)
+                    *reinterpret_cast<uint4 *>(C + (int64_t)grow * g.N + n) =
+                        *reinterpret_cast<const uint4 *>(stg + r * PB + c * 16);
+            }
         }
     }
 }
@@ -545,11 +745,63 @@ __global__ __launch_bounds__(256) void gg_f32(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // launch
 
+// Tile configurations: rows x columns of the output tile, the wave grid, LDS
+// stages and workgroups per CU of the persistent grid.
+#ifndef MOE_ROW_BM
+#define MOE_ROW_BM 128      // FWD / DGRAD: routed rows per tile
+#endif
+#ifndef MOE_ROW_BN
+#define MOE_ROW_BN 256
+#endif
+#ifndef MOE_ROW_STAGES
+#define MOE_ROW_STAGES 3
+#endif
+#ifndef MOE_ROW_OCC
+#define MOE_ROW_OCC 1
+#endif
+#ifndef MOE_ROW_WPE
+#define MOE_ROW_WPE 2
+#endif
+#ifndef MOE_WG_BM
+#define MOE_WG_BM 128       // WGRAD: weight-gradient rows per tile
+#endif
+#ifndef MOE_WG_BN
+#define MOE_WG_BN 256
+#endif
+#ifndef MOE_WG_STAGES
+#define MOE_WG_STAGES 3
+#endif
+#ifndef MOE_WG_OCC
+#define MOE_WG_OCC 1
+#endif
+#ifndef MOE_WG_WPE
+#define MOE_WG_WPE 2
+#endif
+
+#ifndef MOE_ROW_WM
+#define MOE_ROW_WM 2
+#endif
+#ifndef MOE_ROW_WN
+#define MOE_ROW_WN 4
+#endif
+#ifndef MOE_WG_WM
+#define MOE_WG_WM 2
+#endif
+#ifndef MOE_WG_WN
+#define MOE_WG_WN 4
+#endif
+
 template <int MODE, int EPI>
 static void launch_bf16(const GemmArgs &a, hipStream_t s) {
-    constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
-    const int grid = num_cus() * 2;
-    gg_bf16<MODE, EPI, BM, BN, WM, WN><<<grid, WM * WN * 64, 0, s>>>(a);
+    if constexpr (MODE == MOE_GG_WGRAD) {
+        const int grid = (num_cus() * MOE_WG_OCC + 7) / 8 * 8;
+        gg_bf16<MODE, EPI, MOE_WG_BM, MOE_WG_BN, MOE_WG_WM, MOE_WG_WN, MOE_WG_STAGES, MOE_WG_WPE>
+            <<<grid, MOE_WG_WM * MOE_WG_WN * 64, 0, s>>>(a);
+    } else {
+        const int grid = (num_cus() * MOE_ROW_OCC + 7) / 8 * 8;
+        gg_bf16<MODE, EPI, MOE_ROW_BM, MOE_ROW_BN, MOE_ROW_WM, MOE_ROW_WN, MOE_ROW_STAGES,
+                MOE_ROW_WPE><<<grid, MOE_ROW_WM * MOE_ROW_WN * 64, 0, s>>>(a);
+    }
 }
 
 template <int MODE, int EPI>
