@@ -234,9 +234,9 @@ def unpermute_bwd(token_pos, dx_perm, dtype: str, lib=None):
 
 def mxfp8_quantize(a, axis: int, group_offsets=None, lib=None):
     """OCP MXFP8 quantisation (E4M3 elements, one E8M0 scale per 32 along
-    `axis`). axis=1 keeps the layout; axis=0 returns the per-group transposed,
-    block-padded layout described in moe_oracle.c. Returns (q, scale) as
-    flat uint8 arrays for axis=0 and shaped arrays for axis=1."""
+    `axis`). axis=1 keeps the layout; axis=0 returns the per-group transposed
+    layout, each group padded to 128 rows, described in moe_oracle.c. Returns
+    (q, scale) as flat uint8 arrays for axis=0 and shaped arrays for axis=1."""
     lib = lib or load()
     a = _c(a, np.float32)
     rows, cols = a.shape
@@ -246,7 +246,7 @@ def mxfp8_quantize(a, axis: int, group_offsets=None, lib=None):
     else:
         go = np.array([0, rows], np.int32) if group_offsets is None else _c(group_offsets, np.int32)
         ng = len(go) - 1
-        nb = int(sum((go[g + 1] - go[g] + 31) // 32 for g in range(ng)))
+        nb = int(sum(4 * ((go[g + 1] - go[g] + 127) // 128) for g in range(ng)))
         q = np.empty(nb * 32 * cols, np.uint8); s = np.empty(nb * cols, np.uint8)
     rc = lib.oracle_mxfp8_quantize(_ptr(a), rows, cols, axis, _ptr(go), ng, _ptr(q), _ptr(s))
     if rc != 0:

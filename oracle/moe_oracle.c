@@ -413,11 +413,13 @@ uint8_t oracle_mx_scale(double amax) {
  *             whose reduction runs over rows. Rows are split into groups by
  *             group_offsets (n_groups+1 entries; null = one group of all rows);
  *             blocks restart at every group start and a group's last block may
- *             be short. The output is transposed per group and padded to whole
- *             blocks: with nb_g = ceil(len_g/32) and bb_g = sum_{g'<g} nb_g',
+ *             be short. The output is transposed per group and each group is
+ *             padded to a multiple of 4 blocks (128 rows): with
+ *             nb_g = 4*ceil(len_g/128) and bb_g = sum_{g'<g} nb_g',
  *               q[bb_g*32*cols + c*(nb_g*32) + i] = element (o_g + i, c),
  *                 i < len_g; positions len_g <= i < nb_g*32 hold 0;
- *               scale[bb_g*cols + c*nb_g + b] = block b of column c of group g.
+ *               scale[bb_g*cols + c*nb_g + b] = block b of column c of group g
+ *               (blocks wholly past len_g hold scale byte 0).
  * Returns 0, or -1 on bad arguments. */
 int oracle_mxfp8_quantize(const float *in, int64_t rows, int64_t cols, int32_t axis,
                           const int32_t *group_offsets, int32_t n_groups,
@@ -442,7 +444,7 @@ int oracle_mxfp8_quantize(const float *in, int64_t rows, int64_t cols, int32_t a
     int32_t ng = group_offsets ? n_groups : 1;
     int64_t bb = 0;
     for (int g = 0; g < ng; g++) {
-        int64_t len = go[g + 1] - go[g], nb = (len + 31) / 32;
+        int64_t len = go[g + 1] - go[g], nb = 4 * ((len + 127) / 128);
         uint8_t *qg = q + bb * 32 * cols;
         uint8_t *sg = scale + bb * cols;
         for (int64_t c = 0; c < cols; c++)

@@ -95,7 +95,7 @@ def test_special_blocks():
 @pytest.mark.parametrize("groups", [[0, 64], [0, 40, 40, 77, 141], [0, 1, 33, 33, 100]])
 def test_axis0_grouped_layout(groups):
     """Column blocks restart at each group; a group of exactly whole blocks equals
-    the row-wise quantisation of its transpose; partial tails are zero-padded."""
+    the row-wise quantisation of its transpose; tails are zero-padded to 128 rows."""
     rng = np.random.default_rng(2)
     rows = groups[-1]
     cols = 64
@@ -106,7 +106,7 @@ def test_axis0_grouped_layout(groups):
     for g in range(len(go) - 1):
         lo, hi = go[g], go[g + 1]
         n = hi - lo
-        nb = -(-n // 32)
+        nb = 4 * (-(-n // 128))
         if nb == 0:
             continue
         seg = np.zeros((cols, nb * 32), np.float32)
