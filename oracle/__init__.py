@@ -385,3 +385,130 @@ def layer_sampled(inp: dict, k: int, dtype: str, tokens, experts, tile_m: int = 
         dW1[e] = wgrad(dab[sel], x_rows[sel], lib) if len(sel) else np.zeros((2 * h, d))
     res.update(dgate=dg, dlogits=dlogits, dx=dx, dW1=dW1, dW2=dW2, dy=dy, dab=dab, dx_perm=dxp)
     return res
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 layer: every GEMM input is quantised to MXFP8 along that GEMM's
+# reduction axis (OCP MX: one E8M0 scale per 32 elements) and used at its
+# exact dequantised value; accumulation is fp64; stored tensors are bf16.
+# MXFP8 is named for the GEMMs, saved activations and dispatch payload
+# (kongchang.com, "caveats behind the numbers").
+
+
+def mx_rows(a, lib=None):
+    """Dequantised values of `a` quantised along rows (blocks of 32 columns)."""
+    q, s = mxfp8_quantize(np.asarray(a, np.float32), 1, lib=lib)
+    return mxfp8_dequantize_rowwise(q, s)
+
+
+def mx_cols(a, lib=None):
+    """Dequantised values of `a` quantised along columns (blocks of 32 rows,
+    one group), returned in a's own [rows, cols] layout."""
+    a = np.asarray(a, np.float32)
+    rows, cols = a.shape
+    q, s = mxfp8_quantize(a, 0, np.array([0, rows], np.int32), lib=lib)
+    return mx_cols_dequantize(q, s, np.array([0, rows], np.int32), cols)
+
+
+def mx_cols_dequantize(q, s, group_offsets, cols):
+    """Exact values of the column-block layout, back in [rows, cols] order."""
+    tab = e4m3_decode_table()
+    go = np.asarray(group_offsets, np.int64)
+    out = np.zeros((go[-1], cols))
+    bb = 0
+    for g in range(len(go) - 1):
+        n = go[g + 1] - go[g]
+        nb = 4 * (-(-n // 128))
+        if nb:
+            qg = q[bb * 32 * cols:(bb + nb) * 32 * cols].reshape(cols, nb * 32)[:, :n]
+            sg = s[bb * cols:(bb + nb) * cols].reshape(cols, nb).astype(np.int64)
+            sc = np.ldexp(1.0, np.repeat(sg, 32, axis=1)[:, :n] - 127)
+            out[go[g]:go[g + 1]] = (tab[qg] * sc).T
+        bb += nb
+    return out
+
+
+def _mx_weights(W1, W2, experts, lib=None):
+    """Per expert: W1 along d, W2 along h (forward), W1 along 2h and W2 along d
+    (backward), all dequantised from the fp32 masters."""
+    E = W1.shape[0]
+    w1f = [mx_rows(W1[e], lib) if e in experts else None for e in range(E)]
+    w2f = [mx_rows(W2[e], lib) if e in experts else None for e in range(E)]
+    w1b = [mx_cols(W1[e], lib) if e in experts else None for e in range(E)]
+    w2b = [mx_cols(W2[e], lib) if e in experts else None for e in range(E)]
+    return w1f, w2f, w1b, w2b
+
+
+def _mx_layer_rows(inp, k, rows, r, lib, backward):
+    """MXFP8 layer values for the routed rows `rows` (sorted positions)."""
+    W1, W2 = inp["w1"], inp["w2"]
+    h = W1.shape[1] // 2
+    expert_all = expert_of_rows(r["counts"])
+    expert = expert_all[rows]
+    needed = set(np.unique(expert).tolist())
+    w1f, w2f, w1b, w2b = _mx_weights(W1, W2, needed, lib)
+    src = r["sorted_token"][rows]
+    x = np.asarray(inp["x"], np.float32)
+    xq = mx_rows(x[np.unique(src)], lib)                     # x quantised along d before dispatch
+    xq_full = {int(t): i for i, t in enumerate(np.unique(src))}
+    x_rows = xq[[xq_full[int(t)] for t in src]]
+    ab, hp, _ = rows_fwd(x_rows, expert, w1f, w2f, h, "bf16", lib=lib)
+    hq = mx_rows(hp, lib)                                    # H' along h for GEMM2
+    _, _, y = rows_fwd(x_rows, expert, w1f, w2f, h, "bf16", hp_in=hq, lib=lib)
+    res = dict(rows=rows, expert=expert, src=src, ab=ab, hp=hp, y=y,
+               w=(w1f, w2f, w1b, w2b))
+    return res
+
+
+def layer_mx(inp: dict, k: int, tokens=None, experts=None, backward: bool = True, lib=None):
+    """The MXFP8 layer, forward (+ backward) for the rows of `tokens` (all if
+    None) and the weight gradients of `experts` (all if None)."""
+    lib = lib or load()
+    logits, x, W1, W2 = inp["logits"], inp["x"], inp["w1"], inp["w2"]
+    E = W1.shape[0]
+    h = W1.shape[1] // 2
+    d = x.shape[1]
+    T = logits.shape[0]
+    r = route(logits, k, 128, lib)
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    experts = np.arange(E) if experts is None else np.asarray(experts, np.int64)
+    tok_rows = r["token_pos"][tokens].reshape(-1)
+    exp_rows = np.concatenate([np.arange(r["offsets"][e], r["offsets"][e + 1]) for e in experts]) \
+        if len(experts) else np.zeros(0, np.int64)
+    rows = np.unique(np.concatenate([tok_rows, exp_rows]).astype(np.int64))
+    f = _mx_layer_rows(inp, k, rows, r, lib, backward)
+    row_index = {int(p): i for i, p in enumerate(rows)}
+    pos_c = np.array([[row_index[int(p)] for p in r["token_pos"][t]] for t in tokens], np.int32)
+    gate_s = r["topk_gate"][tokens]
+    out = combine(gate_s, pos_c, f["y"], "bf16", lib)
+    res = dict(route=r, rows=rows, out=out, ab=f["ab"], hp=f["hp"], y=f["y"])
+    if not backward:
+        return res
+    w1f, w2f, w1b, w2b = f["w"]
+    dout = np.asarray(inp["dout"], np.float64)
+    src, slot, expert = f["src"], r["sorted_slot"][rows], f["expert"]
+    g_row = r["topk_gate"][src, slot]
+    dy, _ = combine_bwd(g_row.astype(np.float32)[:, None],
+                        np.arange(len(rows), dtype=np.int32)[:, None], dout[src], f["y"], "bf16",
+                        lib)
+    _, dg = combine_bwd(gate_s, pos_c, dout[tokens], f["y"], "bf16", lib)
+    dlogits = router_bwd(r["topk_idx"][tokens], gate_s, dg, E, lib)
+    dyq = mx_rows(dy, lib)                                   # dy along d for GEMM2 dgrad
+    dab, _ = rows_bwd(dyq, f["ab"], expert, w1b, w2b, h, "bf16", lib=lib)
+    dabq = mx_rows(dab, lib)                                 # dAB along 2h for GEMM1 dgrad
+    _, dxp = rows_bwd(dyq, f["ab"], expert, w1b, w2b, h, "bf16", dab_in=dabq, lib=lib)
+    dx = unpermute_bwd(pos_c, dxp, "bf16", lib)
+    xb = np.asarray(x, np.float32)                           # bf16 values of the layer input
+    dW1, dW2 = {}, {}
+    for e in experts:
+        e = int(e)
+        sel = np.array([row_index[int(p)] for p in range(r["offsets"][e], r["offsets"][e + 1])],
+                       np.int64)
+        if len(sel) == 0:
+            dW2[e] = np.zeros((d, h)); dW1[e] = np.zeros((2 * h, d))
+            continue
+        # wgrad operands along rows, blocks restarting at the expert's first row
+        dW2[e] = wgrad(mx_cols(dy[sel], lib), mx_cols(f["hp"][sel], lib), lib)
+        dW1[e] = wgrad(mx_cols(dab[sel], lib), mx_cols(xb[src[sel]], lib), lib)
+    res.update(dy=dy, dgate=dg, dlogits=dlogits, dab=dab, dx_perm=dxp, dx=dx, dW1=dW1, dW2=dW2)
+    return res

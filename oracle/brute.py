@@ -116,3 +116,77 @@ def autograd_layer(logits, x, w1, w2, dout, k: int):
     (out * D).sum().backward()
     return dict(out=out.detach().numpy(), dx=X.grad.numpy(), dW1=W1.grad.numpy(),
                 dW2=W2.grad.numpy(), dlogits=L.grad.numpy())
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 layer, dense per expert, quantising with torch's float8_e4m3fn cast
+
+
+def mx_rows_torch(a):
+    """OCP MXFP8 round trip along rows (blocks of 32 columns): scale exponent
+    floor(log2 amax) - 8 via frexp, clamp [-127, 127]; elements cast by torch
+    after clipping to +-448 (torch's cast does not saturate)."""
+    import torch
+    a = np.asarray(a, np.float64)
+    n, c = a.shape
+    blk = a.reshape(n, c // 32, 32)
+    amax = np.abs(blk).max(axis=2, keepdims=True)
+    _, e = np.frexp(amax)
+    s = np.clip(e - 1 - 8, -127, 127)
+    s = np.where(amax > 0, s, -127)
+    v = np.clip(blk * np.ldexp(1.0, -s), -448.0, 448.0)
+    qv = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).double().numpy()
+    return (qv * np.ldexp(1.0, s)).reshape(n, c)
+
+
+def mx_cols_torch(a):
+    """Round trip along columns (blocks of 32 rows; a short last block)."""
+    a = np.asarray(a, np.float64)
+    n, c = a.shape
+    pad = -n % 32
+    t = np.concatenate([a.T, np.zeros((c, pad))], axis=1)
+    return mx_rows_torch(t)[:, :n].T
+
+
+def mx_layer(logits, x, w1, w2, dout, k: int):
+    """Forward and backward of the MXFP8 layer, one expert at a time over the
+    tokens that chose it (ascending)."""
+    r = route(np.asarray(logits, np.float32), k)
+    x = np.asarray(x, np.float64)
+    T, d = x.shape
+    E, h2, _ = w1.shape
+    h = h2 // 2
+    idx, gate = r["topk_idx"], r["topk_gate"].astype(np.float64)
+    xq = mx_rows_torch(x)
+    out = np.zeros((T, d)); dx = np.zeros((T, d)); dg = np.zeros((T, k))
+    dW1 = np.zeros((E, h2, d)); dW2 = np.zeros((E, d, h))
+    ys, dxs = {}, {}
+    for e in range(E):
+        toks, slots = np.nonzero(idx == e)
+        if len(toks) == 0:
+            continue
+        pre = xq[toks] @ mx_rows_torch(w1[e]).T
+        a, b = pre[:, :h], pre[:, h:]
+        ab = round_bf16(pre)
+        hp = round_bf16(a / (1 + np.exp(-a)) * b)
+        y = round_bf16(mx_rows_torch(hp) @ mx_rows_torch(w2[e]).T)
+        g = gate[toks, slots][:, None]
+        dy = round_bf16(g * dout[toks])
+        dg[toks, slots] = (dout[toks] * y).sum(1)
+        dh = mx_rows_torch(dy) @ mx_cols_torch(w2[e])
+        aa, bb = ab[:, :h], ab[:, h:]
+        sg = 1 / (1 + np.exp(-aa))
+        dab = round_bf16(np.concatenate([dh * bb * sg * (1 + aa * (1 - sg)), dh * aa * sg], 1))
+        dxe = round_bf16(mx_rows_torch(dab) @ mx_cols_torch(w1[e]))
+        dW2[e] = (mx_cols_torch(dy).T @ mx_cols_torch(hp)).astype(np.float32)
+        dW1[e] = (mx_cols_torch(dab).T @ mx_cols_torch(x[toks])).astype(np.float32)
+        for i, (t, j) in enumerate(zip(toks, slots)):
+            ys[(t, j)] = y[i]
+            dxs[(t, j)] = dxe[i]
+    for t in range(T):
+        out[t] = round_bf16(sum(gate[t, j] * ys[(t, j)] for j in range(k)))
+        dx[t] = round_bf16(sum(dxs[(t, j)] for j in range(k)))
+    s = (gate * dg).sum(1, keepdims=True)
+    dlogits = np.zeros((T, E))
+    np.put_along_axis(dlogits, idx.astype(np.int64), (gate * (dg - s)).astype(np.float32), 1)
+    return dict(out=out, dx=dx, dW1=dW1, dW2=dW2, dlogits=dlogits, dgate=dg)
