@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer fwd+bwd tokens/s, E=128 top-4; grouped-GEMM % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 
 
@@ -67,34 +68,59 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     w = synth.WORKLOADS[a.workload]
-    if w.dtype != "bf16":
-        print(f"workload {w.name} is not a bf16 workload", file=sys.stderr)
+    if w.dtype not in ("bf16", "mxfp8"):
+        print(f"workload {w.name} is not a bf16 or MXFP8 workload", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
     inp = synth.device_inputs(w, seed=a.seed, with_dout=w.backward)
     T, d, E, k, h = w.T, w.d, w.E, w.k, w.h
     R = T * k
-    layer = moe.MoELayer(inp["w1"], inp["w2"], k)
+    mx = w.dtype == "mxfp8"
+    # MXFP8: the fp32 masters are quantised (both orientations) once per weight
+    # update, outside the step, as a training step would between optimizer steps
+    layer = moe.MoELayerMX(inp["w1"], inp["w2"], k) if mx else moe.MoELayer(inp["w1"], inp["w2"], k)
     x, logits, dout = inp["x"], inp["logits"], inp["dout"]
     stream = torch.cuda.current_stream()
 
     ev = []
 
+    def gemm1(r):
+        if mx:
+            moe.moe_grouped_gemm(moe.MOE_GG_FWD, layer.xpq, layer.w1q, layer.ab, r["offsets"],
+                                 moe.MOE_EPI_SWIGLU_FWD, N=2 * h, K=d, aux_out=layer.hp,
+                                 a_scale=layer.xps, b_scale=layer.w1s, dtype=moe.MOE_MXFP8)
+        else:
+            moe.moe_grouped_gemm(moe.MOE_GG_FWD, layer.x_perm, layer.w1, layer.ab, r["offsets"],
+                                 moe.MOE_EPI_SWIGLU_FWD, N=2 * h, K=d, aux_out=layer.hp)
+
     def step(timed):
-        layer._alloc(T, x.device, x.dtype)
-        r = moe.moe_route(logits, k, out=layer.route, ws=layer.route_ws)
-        moe.moe_permute(x, r["token_pos"], layer.x_perm)
+        if mx:
+            layer._alloc(T, x.device)
+            layer.x = x
+            moe.mxfp8_quantize(x, 1, q=layer.xq, scale=layer.xs)
+            r = moe.moe_route(logits, k, out=layer.route, ws=layer.route_ws)
+            moe.moe_permute(layer.xq, r["token_pos"], layer.xpq, x_scale=layer.xs,
+                            x_perm_scale=layer.xps)
+        else:
+            layer._alloc(T, x.device, x.dtype)
+            r = moe.moe_route(logits, k, out=layer.route, ws=layer.route_ws)
+            moe.moe_permute(x, r["token_pos"], layer.x_perm)
         if timed:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        moe.moe_grouped_gemm(moe.MOE_GG_FWD, layer.x_perm, layer.w1, layer.ab, r["offsets"],
-                             moe.MOE_EPI_SWIGLU_FWD, N=2 * h, K=d, aux_out=layer.hp)
+        gemm1(r)
         if timed:
             e1.record(stream)
             ev.append((e0, e1))
-        moe.moe_grouped_gemm(moe.MOE_GG_FWD, layer.hp, layer.w2, layer.y_perm, r["offsets"],
-                             N=d, K=h)
+        if mx:
+            moe.mxfp8_quantize(layer.hp, 1, q=layer.hpq, scale=layer.hps)
+            moe.moe_grouped_gemm(moe.MOE_GG_FWD, layer.hpq, layer.w2q, layer.y_perm, r["offsets"],
+                                 N=d, K=h, a_scale=layer.hps, b_scale=layer.w2s,
+                                 dtype=moe.MOE_MXFP8)
+        else:
+            moe.moe_grouped_gemm(moe.MOE_GG_FWD, layer.hp, layer.w2, layer.y_perm, r["offsets"],
+                                 N=d, K=h)
         moe.moe_combine(layer.y_perm, r["topk_gate"], r["token_pos"], layer.out)
         if w.backward:
             layer.backward(dout)
@@ -113,8 +139,9 @@ def main():
     g1_flops = 2.0 * R * d * 2 * h
     g1_tflops = g1_flops / (g1_ms * 1e-3) / 1e12
     flops = w.fwd_bwd_flops() if w.backward else w.fwd_flops()
+    peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
 
-    if a.breakdown:
+    if a.breakdown and not mx:
         breakdown(moe, torch, layer, x, logits, dout, w)
     if a.copy_calib:
         n = a.copy_calib * (1 << 20)
@@ -135,23 +162,25 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8" if mx else "bf16",
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: MoE expert layer {'fwd+bwd' if w.backward else 'fwd'}, "
                         f"T={T} tokens, d_model={d}, E={E} experts, top-{k}, SwiGLU hidden={h}, "
-                        f"bf16 storage / fp32 accumulate, {'Zipf(1.2)-skewed' if w.zipf_s else 'uniform random'} routing",
+                        + ("MXFP8 GEMMs and dispatch (E4M3 + E8M0/32), bf16 activations, "
+                           "fp32 accumulate" if mx else "bf16 storage / fp32 accumulate")
+                        + f", {'Zipf(1.2)-skewed' if w.zipf_s else 'uniform random'} routing",
             "tokens": T, "d_model": d, "experts": E, "top_k": k, "hidden": h,
             "layer_tflops": flops / (ms * 1e-3) / 1e12,
-            "layer_frac_of_bf16_mfma_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "layer_frac_of_mfma_peak": flops / (ms * 1e-3) / 1e12 / peak,
         },
         "roofline": {
-            "kernel": "grouped GEMM1 + SwiGLU forward (gg_bf16<FWD, SWIGLU_FWD>)",
+            "kernel": f"grouped GEMM1 + SwiGLU forward (gg_mfma<FWD, SWIGLU_FWD, {'MXFP8' if mx else 'bf16'}>)",
             "bound": "mfma",
             "achieved": g1_tflops,
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": g1_tflops / PEAK_BF16_TFLOPS,
+            "frac": g1_tflops / peak,
             "traffic": None,
             "avg_launch_ms": g1_ms,
             "flops_per_launch": g1_flops,
@@ -173,9 +202,12 @@ def cpu_baseline(inp, w, n_tok):
                w1=inp["w1"].float().cpu().numpy(), w2=inp["w2"].float().cpu().numpy(),
                dout=inp["dout"][:n_tok].float().cpu().numpy() if w.backward else None)
     t0 = time.perf_counter()
-    f = oracle.layer_forward(sub, w.k, "bf16")
-    if w.backward:
-        oracle.layer_backward(sub, f, w.k, "bf16")
+    if w.dtype == "mxfp8":
+        oracle.layer_mx(sub, w.k, backward=w.backward)
+    else:
+        f = oracle.layer_forward(sub, w.k, "bf16")
+        if w.backward:
+            oracle.layer_backward(sub, f, w.k, "bf16")
     dt = time.perf_counter() - t0
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"first {n_tok} of {w.T} tokens of {w.name} (all {w.E} experts), "

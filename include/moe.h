@@ -159,11 +159,17 @@ enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU_FWD = 1, MOE_EPI_SWIGLU_BWD = 2 };
  *
  * dtype MOE_F32 or MOE_BF16: A, B and C (except WGRAD's fp32 C) have that
  * dtype; accumulation is fp32; stores round to nearest even.
- * dtype MOE_MXFP8 (MOE_GG_FWD and MOE_GG_DGRAD): A and B are E4M3 bytes with
- * E8M0 scales in a_scale / b_scale, one per 32 elements along K
- * (A: [rows, K/32]; B: [E, N, K/32], i.e. B given K-contiguous as [E, N, K]
- * in both modes); C is bf16; aux_out_scale (SWIGLU_FWD) receives H' as MXFP8
- * along its rows: aux_out = E4M3 [rows, h], aux_out_scale = [rows, h/32].
+ * dtype MOE_MXFP8: operands are E4M3 bytes with E8M0 scales (a_scale,
+ * b_scale; 4-byte aligned), one per 32 elements along the reduction, and
+ * both operands are given K-contiguous in every mode:
+ *   FWD / DGRAD: A [rows, K] with scales [rows, K/32]; B [E, N, K] with
+ *     scales [E, N, K/32] (for DGRAD that is the weight in its second
+ *     orientation, e.g. mxfp8_quantize axis 0 of W[e] per expert); K % 128 == 0;
+ *     C (and AB / H' / dAB of the epilogues) is bf16;
+ *   WGRAD: A and B in the column-block layout of mxfp8_quantize (axis 0,
+ *     groups = offsets): A holds the [rows, M] operand, B the [rows, N]
+ *     operand; C [E, M, N] fp32.
+ * (aux_out_scale is reserved and must be null.)
  */
 typedef struct moe_gemm_desc {
     int32_t mode;          /* MOE_GG_* */
@@ -201,8 +207,16 @@ moe_status moe_grouped_gemm(const moe_gemm_desc *g, void *stream);
  * caller-owned buffers.
  *   dlogits[t, e] = g_i (dg_i - sum_j g_j dg_j) for e = topk_idx[t, i], and
  *   exactly 0 for unselected experts, with dg_j = <dOut[t], y_perm[row]>.
- * dtype MOE_F32 or MOE_BF16 (activations, weights, dOut, dX, intermediates);
- * dW1, dW2, dlogits and dgate are fp32. */
+ * dtype MOE_F32 or MOE_BF16: activations, weights, dOut, dX and the
+ * intermediates in that dtype. dW1, dW2, dlogits and dgate are fp32.
+ * dtype MOE_MXFP8: activations, dOut, dX and the intermediates are bf16
+ * (x_perm is not needed; x and sorted_token are); the four backward GEMMs
+ * run in MXFP8 on operands the call quantises itself into ws: dy_perm along
+ * d and along rows, H' along rows, dAB along 2h and along rows, and the rows
+ * x[sorted_token] along rows. The weights come pre-quantised in their second
+ * orientation (w1t/w1t_scale = W1[e] along 2h as [E, d, 2h];
+ * w2t/w2t_scale = W2[e] along d as [E, h, d]; see mxfp8_quantize axis 0),
+ * i.e. once per weight update. Needs d % 128 == 0 and h % 128 == 0. */
 typedef struct moe_bwd_desc {
     int32_t dtype;
     int32_t d, h, E, k;
@@ -229,7 +243,14 @@ typedef struct moe_bwd_desc {
     void *dy_perm;             /* [T*k, d] */
     void *dab;                 /* [T*k, 2h] */
     void *dx_perm;             /* [T*k, d] */
-    void *ws;
+    /* MXFP8 only */
+    const void *x;                 /* [T, d] bf16 layer input */
+    const int32_t *sorted_token;   /* [T*k] from moe_route */
+    const uint8_t *w1t;            /* [E, d, 2h] E4M3 */
+    const uint8_t *w1t_scale;      /* [E, d, 2h/32] */
+    const uint8_t *w2t;            /* [E, h, d] E4M3 */
+    const uint8_t *w2t_scale;      /* [E, h, d/32] */
+    void *ws;                      /* scratch, moe_backward_workspace_size bytes */
     size_t ws_bytes;
 } moe_bwd_desc;
 
@@ -251,17 +272,25 @@ moe_status moe_backward(const moe_bwd_desc *b, void *stream);
  *             Rows are split into n_groups groups by group_offsets (device,
  *             n_groups+1 entries; null = one group of all rows, n_groups
  *             ignored); blocks restart at each group and a group's last block
- *             may be short. Output is transposed per group and padded to whole
- *             blocks: with nb_g = ceil(len_g/32), bb_g = sum_{g'<g} nb_g',
+ *             may be short. Output is transposed per group and each group is
+ *             padded to a multiple of 4 blocks (128 rows): with
+ *             nb_g = 4*ceil(len_g/128) and bb_g = sum_{g'<g} nb_g',
  *               q[bb_g*32*cols + c*nb_g*32 + i] = element (o_g + i, c) for
  *               i < len_g, and 0 for len_g <= i < nb_g*32;
- *               scale[bb_g*cols + c*nb_g + b] = block b of column c.
- *             Size q and scale for the worst case (rows/32 + n_groups) blocks.
+ *               scale[bb_g*cols + c*nb_g + b] = block b of column c
+ *               (blocks wholly past len_g: scale byte 0).
+ *             Size q for mxfp8_col_blocks(rows, n_groups) * 32 * cols bytes
+ *             and scale for mxfp8_col_blocks(rows, n_groups) * cols bytes.
  *             n_groups <= 1024.
+ * row_map (device, nullable): input row r is in[row_map[r]] (a fused
+ * gather, e.g. x[sorted_token] for the permuted rows).
  * in_dt: MOE_F32 or MOE_BF16. */
 moe_status mxfp8_quantize(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
                           int32_t axis, const int32_t *group_offsets, int32_t n_groups,
-                          uint8_t *q, uint8_t *scale, void *stream);
+                          const int32_t *row_map, uint8_t *q, uint8_t *scale, void *stream);
+
+/* Worst-case block count of the column-block layout: rows/32 + 4*n_groups + 4. */
+size_t mxfp8_col_blocks(int64_t rows, int32_t n_groups);
 
 #ifdef __cplusplus
 }

@@ -52,8 +52,9 @@ class BwdDesc(ctypes.Structure):
                 ("x_perm", _P), ("ab", _P), ("hp", _P), ("y_perm", _P), ("topk_gate", _P),
                 ("topk_idx", _P), ("token_pos", _P), ("offsets", _P), ("w1", _P), ("w2", _P),
                 ("dout", _P), ("dx", _P), ("dlogits", _P), ("dw1", _P), ("dw2", _P),
-                ("dgate", _P), ("dy_perm", _P), ("dab", _P), ("dx_perm", _P), ("ws", _P),
-                ("ws_bytes", _SZ)]
+                ("dgate", _P), ("dy_perm", _P), ("dab", _P), ("dx_perm", _P), ("x", _P),
+                ("sorted_token", _P), ("w1t", _P), ("w1t_scale", _P), ("w2t", _P),
+                ("w2t_scale", _P), ("ws", _P), ("ws_bytes", _SZ)]
 
 
 def _load():
@@ -81,8 +82,10 @@ def _load():
     lib.moe_backward.restype = _I32
     lib.moe_backward_workspace_size.argtypes = [ctypes.POINTER(BwdDesc)]
     lib.moe_backward_workspace_size.restype = _SZ
-    lib.mxfp8_quantize.argtypes = [_P, _I32, _I64, _I64, _I32, _P, _I32, _P, _P, _P]
+    lib.mxfp8_quantize.argtypes = [_P, _I32, _I64, _I64, _I32, _P, _I32, _P, _P, _P, _P]
     lib.mxfp8_quantize.restype = _I32
+    lib.mxfp8_col_blocks.argtypes = [_I64, _I32]
+    lib.mxfp8_col_blocks.restype = _SZ
     return lib
 
 
@@ -214,9 +217,11 @@ def moe_grouped_gemm(mode: int, A: torch.Tensor, B: torch.Tensor, C: torch.Tenso
 
 
 def moe_backward(saved: dict, dout: torch.Tensor, E: int, k: int, d: int, h: int,
-                 out: dict | None = None, want_dgate: bool = True) -> dict:
+                 out: dict | None = None, want_dgate: bool = True, mxfp8: bool = False) -> dict:
     """Backward of the whole layer. `saved` holds the forward tensors
-    (x_perm, ab, hp, y_perm, topk_gate, topk_idx, token_pos, offsets, w1, w2)."""
+    (x_perm, ab, hp, y_perm, topk_gate, topk_idx, token_pos, offsets, w1, w2;
+    with mxfp8: x, sorted_token, w1t, w1t_scale, w2t, w2t_scale instead of
+    x_perm, w1, w2)."""
     T = dout.shape[0]
     R = T * k
     dev, dt = dout.device, dout.dtype
@@ -230,30 +235,41 @@ def moe_backward(saved: dict, dout: torch.Tensor, E: int, k: int, d: int, h: int
                    dab=torch.empty((R, 2 * h), dtype=dt, device=dev),
                    dx_perm=torch.empty((R, d), dtype=dt, device=dev))
     b = BwdDesc()
-    b.dtype = _dt(dout)
+    b.dtype = MOE_MXFP8 if mxfp8 else _dt(dout)
     b.d, b.h, b.E, b.k, b.T = d, h, E, k, T
-    for name in ("x_perm", "ab", "hp", "y_perm", "topk_gate", "topk_idx", "token_pos", "offsets",
-                 "w1", "w2"):
+    names = ("ab", "hp", "y_perm", "topk_gate", "topk_idx", "token_pos", "offsets")
+    names += (("x", "sorted_token", "w1t", "w1t_scale", "w2t", "w2t_scale") if mxfp8
+              else ("x_perm", "w1", "w2"))
+    for name in names:
         setattr(b, name, saved[name].data_ptr())
     b.dout = dout.data_ptr()
     for name in ("dx", "dlogits", "dw1", "dw2", "dy_perm", "dab", "dx_perm"):
         setattr(b, name, out[name].data_ptr())
     b.dgate = out["dgate"].data_ptr() if out.get("dgate") is not None else None
     wsb = int(_lib.moe_backward_workspace_size(ctypes.byref(b)))
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
-    b.ws = ws.data_ptr() if ws is not None else None
+    ws = out.get("_ws")
+    if wsb and (ws is None or ws.numel() < wsb):
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        out["_ws"] = ws
+    b.ws = ws.data_ptr() if wsb else None
     b.ws_bytes = wsb
     _check("moe_backward", _lib.moe_backward(ctypes.byref(b), _stream()))
     return out
 
 
+def mxfp8_col_blocks(rows: int, n_groups: int) -> int:
+    return int(_lib.mxfp8_col_blocks(rows, n_groups))
+
+
 def mxfp8_quantize(x: torch.Tensor, axis: int = 1, group_offsets: torch.Tensor | None = None,
                    q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
-                   max_blocks: int | None = None):
+                   row_map: torch.Tensor | None = None):
     """OCP MXFP8 quantisation (see moe.h). axis=1 returns q [rows, cols] and
-    scale [rows, cols/32]; axis=0 returns the flat grouped, transposed,
-    block-padded q and scale sized for the worst case."""
-    rows, cols = x.shape
+    scale [rows, cols/32]; axis=0 returns the flat column-block layout (groups
+    padded to 128 rows) sized for the worst case. With row_map, output row r
+    quantises x[row_map[r]] (rows = row_map.numel())."""
+    rows = x.shape[0] if row_map is None else row_map.numel()
+    cols = x.shape[1]
     dev = x.device
     ng = 0 if group_offsets is None else group_offsets.numel() - 1
     if axis == 1:
@@ -261,12 +277,12 @@ def mxfp8_quantize(x: torch.Tensor, axis: int = 1, group_offsets: torch.Tensor |
         scale = scale if scale is not None else torch.empty((rows, cols // 32), dtype=torch.uint8,
                                                             device=dev)
     else:
-        nb = max_blocks if max_blocks is not None else (rows // 32 + max(ng, 1))
+        nb = mxfp8_col_blocks(rows, max(ng, 1))
         q = q if q is not None else torch.empty(nb * 32 * cols, dtype=torch.uint8, device=dev)
         scale = scale if scale is not None else torch.empty(nb * cols, dtype=torch.uint8, device=dev)
     _check("mxfp8_quantize", _lib.mxfp8_quantize(_p(x), _dt(x), rows, cols, axis,
-                                                 _p(group_offsets), ng, _p(q), _p(scale),
-                                                 _stream()))
+                                                 _p(group_offsets), ng, _p(row_map), _p(q),
+                                                 _p(scale), _stream()))
     return q, scale
 
 
@@ -327,4 +343,90 @@ class MoELayer:
     def backward(self, dout: torch.Tensor) -> dict:
         self.grads = moe_backward(self.saved(), dout, self.E, self.k, self.d, self.h,
                                   out=self.grads)
+        return self.grads
+
+
+class MoELayerMX:
+    """The layer with MXFP8 GEMMs and an MXFP8 dispatch payload.
+
+    fp32 master weights are quantised once per weight update
+    (`prepare_weights`), in both orientations: along d / h for the forward
+    GEMMs and, per expert, along 2h / d for the backward dgrads. The forward
+    quantises x along d before dispatch, so the row-wise dispatch moves E4M3
+    bytes plus their scales; GEMM1 writes AB and H' in bf16, H' is quantised
+    along h for GEMM2, and y, out stay bf16. The backward (moe_backward with
+    MXFP8) quantises its own GEMM operands."""
+
+    def __init__(self, w1_master: torch.Tensor, w2_master: torch.Tensor, k: int):
+        self.E, h2, self.d = w1_master.shape
+        self.h = h2 // 2
+        self.k = k
+        self.prepare_weights(w1_master, w2_master)
+        self._T = None
+
+    def prepare_weights(self, w1: torch.Tensor, w2: torch.Tensor):
+        E, d, h = self.E, self.d, self.h
+        dev = w1.device
+        self.w1q, self.w1s = mxfp8_quantize(w1.reshape(E * 2 * h, d), 1)
+        self.w2q, self.w2s = mxfp8_quantize(w2.reshape(E * d, h), 1)
+        g1 = torch.arange(0, E + 1, dtype=torch.int32, device=dev) * (2 * h)
+        g2 = torch.arange(0, E + 1, dtype=torch.int32, device=dev) * d
+        self.w1t, self.w1ts = mxfp8_quantize(w1.reshape(E * 2 * h, d), 0, g1)
+        self.w2t, self.w2ts = mxfp8_quantize(w2.reshape(E * d, h), 0, g2)
+
+    def _alloc(self, T, dev):
+        if self._T == T:
+            return
+        E, k, d, h = self.E, self.k, self.d, self.h
+        R = T * k
+        i32 = dict(dtype=torch.int32, device=dev)
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        u8 = dict(dtype=torch.uint8, device=dev)
+        self.route = dict(topk_idx=torch.empty((T, k), **i32),
+                          topk_gate=torch.empty((T, k), dtype=torch.float32, device=dev),
+                          counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+                          token_pos=torch.empty((T, k), **i32), sorted_token=torch.empty(R, **i32),
+                          sorted_slot=torch.empty(R, **i32), tile_offsets=torch.empty(E + 1, **i32))
+        self.route_ws = torch.empty(max(moe_route_workspace_size(T, E, k), 1), **u8)
+        self.xq = torch.empty((T, d), **u8)
+        self.xs = torch.empty((T, d // 32), **u8)
+        self.xpq = torch.empty((R, d), **u8)
+        self.xps = torch.empty((R, d // 32), **u8)
+        self.ab = torch.empty((R, 2 * h), **bf)
+        self.hp = torch.empty((R, h), **bf)
+        self.hpq = torch.empty((R, h), **u8)
+        self.hps = torch.empty((R, h // 32), **u8)
+        self.y_perm = torch.empty((R, d), **bf)
+        self.out = torch.empty((T, d), **bf)
+        self.grads = None
+        self.bwd_ws = None
+        self._T = T
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor) -> torch.Tensor:
+        T, d = x.shape
+        h = self.h
+        self._alloc(T, x.device)
+        self.x = x
+        mxfp8_quantize(x, 1, q=self.xq, scale=self.xs)
+        r = moe_route(logits, self.k, out=self.route, ws=self.route_ws)
+        moe_permute(self.xq, r["token_pos"], self.xpq, x_scale=self.xs, x_perm_scale=self.xps)
+        moe_grouped_gemm(MOE_GG_FWD, self.xpq, self.w1q, self.ab, r["offsets"], MOE_EPI_SWIGLU_FWD,
+                         N=2 * h, K=d, aux_out=self.hp, a_scale=self.xps, b_scale=self.w1s,
+                         dtype=MOE_MXFP8)
+        mxfp8_quantize(self.hp, 1, q=self.hpq, scale=self.hps)
+        moe_grouped_gemm(MOE_GG_FWD, self.hpq, self.w2q, self.y_perm, r["offsets"], N=d, K=h,
+                         a_scale=self.hps, b_scale=self.w2s, dtype=MOE_MXFP8)
+        moe_combine(self.y_perm, r["topk_gate"], r["token_pos"], self.out)
+        return self.out
+
+    def saved(self) -> dict:
+        r = self.route
+        return dict(x=self.x, sorted_token=r["sorted_token"], ab=self.ab, hp=self.hp,
+                    y_perm=self.y_perm, topk_gate=r["topk_gate"], topk_idx=r["topk_idx"],
+                    token_pos=r["token_pos"], offsets=r["offsets"], w1t=self.w1t,
+                    w1t_scale=self.w1ts, w2t=self.w2t, w2t_scale=self.w2ts)
+
+    def backward(self, dout: torch.Tensor) -> dict:
+        self.grads = moe_backward(self.saved(), dout, self.E, self.k, self.d, self.h,
+                                  out=self.grads, mxfp8=True)
         return self.grads

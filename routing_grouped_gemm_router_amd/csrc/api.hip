@@ -26,7 +26,9 @@ moe_status combine_bwd_launch(const void *dout, const void *y, moe_dtype dt, con
 moe_status gemm_launch(const moe_gemm_desc *d, hipStream_t s);
 moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
                                  int axis, const int32_t *group_offsets, int n_groups,
-                                 uint8_t *q, uint8_t *scale, hipStream_t s);
+                                 const int32_t *row_map, uint8_t *q, uint8_t *scale,
+                                 hipStream_t s);
+size_t mxfp8_col_blocks(int64_t rows, int n_groups);
 
 int num_cus() {
     static int cache[64] = {0};
@@ -50,6 +52,31 @@ static bool routing_shape_ok(int64_t T, int32_t E, int32_t k) {
 static bool width_ok(int32_t w) { return w >= 32 && w <= 16384 && w % 32 == 0; }
 
 static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+static bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+// sub-buffers of the MXFP8 backward workspace (byte offsets, 256-aligned):
+// region A holds one row-quantised operand at a time, region B two
+// column-block operands at a time (the call reuses them in sequence)
+struct MxBwdLayout {
+    size_t a_q, a_s, b0_q, b0_s, b1_q, b1_s, total;
+};
+static MxBwdLayout mx_bwd_layout(int64_t R, int d, int h, int E) {
+    MxBwdLayout L;
+    const size_t wmax = (size_t)(2 * h > d ? 2 * h : d);
+    const size_t nbc = mxfp8_col_blocks(R, E);
+    L.a_q = 0;
+    L.a_s = round256((size_t)R * wmax);
+    const size_t regA = L.a_s + round256((size_t)R * wmax / 32);
+    // B: (dy rows along d, H' rows along h) then (dAB rows along 2h, x rows along d)
+    const size_t c0 = nbc * 32 * wmax, c1 = nbc * 32 * (size_t)d;
+    L.b0_q = regA;
+    L.b0_s = L.b0_q + round256(c0);
+    L.b1_q = L.b0_s + round256(c0 / 32);
+    L.b1_s = L.b1_q + round256(c1);
+    L.total = L.b1_s + round256(c1 / 32);
+    return L;
+}
 
 }  // namespace moe
 
@@ -123,7 +150,13 @@ moe_status moe_combine(const void *y_perm, moe_dtype dt, const float *topk_gate,
 static moe_status check_gemm(const moe_gemm_desc *g) {
     if (!g) return MOE_ERR_NULL;
     if (g->mode < MOE_GG_FWD || g->mode > MOE_GG_WGRAD) return MOE_ERR_DTYPE;
-    if (g->dtype != MOE_F32 && g->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (g->dtype != MOE_F32 && g->dtype != MOE_BF16 && g->dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+    if (g->dtype == MOE_MXFP8) {
+        if (g->aux_out_scale) return MOE_ERR_DTYPE;
+        if (g->mode != MOE_GG_WGRAD && g->K % 128) return MOE_ERR_SHAPE;
+        if (!g->a_scale || !g->b_scale) return MOE_ERR_NULL;
+        if (!aligned4(g->a_scale) || !aligned4(g->b_scale)) return MOE_ERR_ALIGN;
+    }
     if (g->epilogue == MOE_EPI_SWIGLU_FWD && g->mode != MOE_GG_FWD) return MOE_ERR_DTYPE;
     if (g->epilogue == MOE_EPI_SWIGLU_BWD && g->mode != MOE_GG_DGRAD) return MOE_ERR_DTYPE;
     if (g->epilogue < MOE_EPI_NONE || g->epilogue > MOE_EPI_SWIGLU_BWD) return MOE_ERR_DTYPE;
@@ -165,12 +198,15 @@ moe_status moe_grouped_gemm(const moe_gemm_desc *g, void *stream) {
 }
 
 size_t moe_backward_workspace_size(const moe_bwd_desc *b) {
-    (void)b;
-    return 0;
+    if (!b || b->dtype != MOE_MXFP8) return 0;
+    return mx_bwd_layout(b->T * b->k, b->d, b->h, b->E).total;
 }
+
+static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s);
 
 moe_status moe_backward(const moe_bwd_desc *b, void *stream) {
     if (!b) return MOE_ERR_NULL;
+    if (b->dtype == MOE_MXFP8) return backward_mxfp8(b, (hipStream_t)stream);
     if (b->dtype != MOE_F32 && b->dtype != MOE_BF16) return MOE_ERR_DTYPE;
     if (!routing_shape_ok(b->T, b->E, b->k) || !width_ok(b->d) || !width_ok(b->h))
         return MOE_ERR_SHAPE;
@@ -219,9 +255,92 @@ moe_status moe_backward(const moe_bwd_desc *b, void *stream) {
                           true, s);
 }
 
+static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
+    if (!routing_shape_ok(b->T, b->E, b->k) || !width_ok(b->d) || !width_ok(b->h) ||
+        b->d % 128 || b->h % 128)
+        return MOE_ERR_SHAPE;
+    if (!b->dw1 || !b->dw2 || !b->offsets || !b->w1t || !b->w1t_scale || !b->w2t ||
+        !b->w2t_scale)
+        return MOE_ERR_NULL;
+    const bool any = b->T > 0;
+    if (any && (!b->x || !b->sorted_token || !b->ab || !b->hp || !b->y_perm || !b->topk_gate ||
+                !b->topk_idx || !b->token_pos || !b->dout || !b->dx || !b->dlogits ||
+                !b->dy_perm || !b->dab || !b->dx_perm || !b->ws))
+        return MOE_ERR_NULL;
+    const void *al[] = {b->x, b->ab, b->hp, b->y_perm, b->dout, b->dx, b->dw1, b->dw2,
+                        b->dy_perm, b->dab, b->dx_perm, b->w1t, b->w2t, b->ws};
+    for (const void *p : al)
+        if (p && !aligned16(p)) return MOE_ERR_ALIGN;
+    if (!aligned4(b->w1t_scale) || !aligned4(b->w2t_scale)) return MOE_ERR_ALIGN;
+    const int64_t R = b->T * b->k;
+    const int d = b->d, h = b->h, E = b->E;
+    const MxBwdLayout L = mx_bwd_layout(R, d, h, E);
+    if (b->ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    char *ws = reinterpret_cast<char *>(b->ws);
+    uint8_t *aq = (uint8_t *)(ws + L.a_q), *as = (uint8_t *)(ws + L.a_s);
+    uint8_t *b0q = (uint8_t *)(ws + L.b0_q), *b0s = (uint8_t *)(ws + L.b0_s);
+    uint8_t *b1q = (uint8_t *)(ws + L.b1_q), *b1s = (uint8_t *)(ws + L.b1_s);
+    moe_status st;
+    // combine backward + router backward (bf16)
+    if ((st = combine_bwd_launch(b->dout, b->y_perm, MOE_BF16, b->topk_gate, b->topk_idx,
+                                 b->token_pos, b->T, d, b->k, E, b->dy_perm, b->dlogits,
+                                 b->dgate, s)) != MOE_OK)
+        return st;
+    moe_gemm_desc g;
+    memset(&g, 0, sizeof(g));
+    g.dtype = MOE_MXFP8;
+    g.n_groups = E;
+    g.rows = R;
+    g.offsets = b->offsets;
+    if (R > 0) {
+        // GEMM2 dgrad + SwiGLU backward: dy (along d) . W2t
+        if ((st = mxfp8_quantize_launch(b->dy_perm, MOE_BF16, R, d, 1, nullptr, 1, nullptr, aq,
+                                        as, s)) != MOE_OK)
+            return st;
+        g.mode = MOE_GG_DGRAD; g.epilogue = MOE_EPI_SWIGLU_BWD; g.N = h; g.K = d;
+        g.A = aq; g.a_scale = as; g.B = b->w2t; g.b_scale = b->w2t_scale;
+        g.C = b->dab; g.aux = b->ab;
+        if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
+    }
+    // GEMM2 wgrad: dy and H' along rows, per expert
+    if ((st = mxfp8_quantize_launch(b->dy_perm, MOE_BF16, R, d, 0, b->offsets, E, nullptr, b0q,
+                                    b0s, s)) != MOE_OK)
+        return st;
+    if ((st = mxfp8_quantize_launch(b->hp, MOE_BF16, R, h, 0, b->offsets, E, nullptr, b1q, b1s,
+                                    s)) != MOE_OK)
+        return st;
+    g.mode = MOE_GG_WGRAD; g.epilogue = MOE_EPI_NONE; g.aux = nullptr; g.M = d; g.N = h; g.K = 0;
+    g.A = b0q; g.a_scale = b0s; g.B = b1q; g.b_scale = b1s; g.C = b->dw2;
+    if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
+    if (R > 0) {
+        // GEMM1 dgrad: dAB (along 2h) . W1t
+        if ((st = mxfp8_quantize_launch(b->dab, MOE_BF16, R, 2 * h, 1, nullptr, 1, nullptr, aq,
+                                        as, s)) != MOE_OK)
+            return st;
+        g.mode = MOE_GG_DGRAD; g.M = 0; g.N = d; g.K = 2 * h;
+        g.A = aq; g.a_scale = as; g.B = b->w1t; g.b_scale = b->w1t_scale; g.C = b->dx_perm;
+        if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
+    }
+    // GEMM1 wgrad: dAB and x[sorted_token] along rows, per expert
+    if ((st = mxfp8_quantize_launch(b->dab, MOE_BF16, R, 2 * h, 0, b->offsets, E, nullptr, b0q,
+                                    b0s, s)) != MOE_OK)
+        return st;
+    if ((st = mxfp8_quantize_launch(b->x, MOE_BF16, R, d, 0, b->offsets, E, b->sorted_token, b1q,
+                                    b1s, s)) != MOE_OK)
+        return st;
+    g.mode = MOE_GG_WGRAD; g.M = 2 * h; g.N = d; g.K = 0;
+    g.A = b0q; g.a_scale = b0s; g.B = b1q; g.b_scale = b1s; g.C = b->dw1;
+    if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
+    // unpermute backward
+    return combine_launch(b->dx_perm, MOE_BF16, nullptr, b->token_pos, b->T, d, b->k, b->dx, true,
+                          s);
+}
+
+size_t mxfp8_col_blocks(int64_t rows, int32_t n_groups) { return moe::mxfp8_col_blocks(rows, n_groups); }
+
 moe_status mxfp8_quantize(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
                           int32_t axis, const int32_t *group_offsets, int32_t n_groups,
-                          uint8_t *q, uint8_t *scale, void *stream) {
+                          const int32_t *row_map, uint8_t *q, uint8_t *scale, void *stream) {
     if (in_dt != MOE_F32 && in_dt != MOE_BF16) return MOE_ERR_DTYPE;
     if (rows < 0 || cols < 32 || cols % 32 || rows >= ((int64_t)1 << 31) ||
         cols >= ((int64_t)1 << 20))
@@ -232,7 +351,8 @@ moe_status mxfp8_quantize(const void *in, moe_dtype in_dt, int64_t rows, int64_t
     if (!in || !q || !scale) return MOE_ERR_NULL;
     if (!aligned16(in) || !aligned16(q)) return MOE_ERR_ALIGN;
     return mxfp8_quantize_launch(in, in_dt, rows, cols, axis, group_offsets,
-                                 group_offsets ? n_groups : 1, q, scale, (hipStream_t)stream);
+                                 group_offsets ? n_groups : 1, row_map, q, scale,
+                                 (hipStream_t)stream);
 }
 
 }  // extern "C"

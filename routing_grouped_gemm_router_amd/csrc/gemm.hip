@@ -42,6 +42,8 @@ struct GemmArgs {
     const void *aux;
     void *aux_out;
     const int32_t *offsets;
+    const uint8_t *a_scale;   // MXFP8 E8M0 scales
+    const uint8_t *b_scale;
     int64_t rows;
     int M, N, K;
     int E;
@@ -171,9 +173,11 @@ MOE_DEV void decode_row_tile(const RowSchedule &rs, const int32_t *s_chunk,
 }
 
 // ---------------------------------------------------------------------------
-// bf16 MFMA kernel
+// MFMA kernel: bf16 (v_mfma_f32_32x32x16_bf16) and MXFP8
+// (v_mfma_scale_f32_32x32x64_f8f6f4 with E8M0 block scales)
 
-constexpr int kBK = 64;
+// Each pipeline step covers 128 bytes of K per row: 64 bf16 or 128 fp8.
+constexpr int kStepBytes = 128;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define MOE_LDS __attribute__((address_space(3)))
@@ -182,22 +186,22 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // tail, columns past N): zero-initialised device memory.
 __device__ uint4 g_zero_chunk[64] = {};
 
-// K-layout LDS tile: [R rows][64 k] bf16 (128-byte rows). LDS has 64 4-byte
-// banks, i.e. two 128-byte rows per bank cycle; XOR-swizzling the 16-byte
-// chunks with (row/2) % 8 puts the 16 rows that a ds_read_b128 serves per
-// cycle on 16 different 16-byte bank groups (measured: 2x the read rate of a
-// row % 8 swizzle, 7x that of no swizzle).
+// K-layout LDS tile: [R rows][128 bytes]. LDS has 64 4-byte banks, i.e. two
+// 128-byte rows per bank cycle; XOR-swizzling the 16-byte chunks with
+// (row/2) % 8 puts the 16 rows that a ds_read_b128 serves per cycle on 16
+// different 16-byte bank groups (measured: 2x the read rate of a row % 8
+// swizzle, 7x that of no swizzle).
 MOE_DEV int kl_swz(int row) { return (row >> 1) & 7; }
 MOE_DEV int kl_chunk(int row, int kc) { return row * 8 + (kc ^ kl_swz(row)); }
 
-// MN-layout LDS tile: [64 k][R] bf16, i.e. the global tile copied as is.
-// Chunk c of row k sits at c ^ ((k & 3) << 2): the four k rows that one
+// MN-layout LDS tile (bf16 only): [64 k][R] bf16, i.e. the global tile copied
+// as is. Chunk c of row k sits at c ^ ((k & 3) << 2): the four k rows that one
 // transpose read touches fall in four different 64-byte bank windows.
 template <int R>
 MOE_DEV int mn_chunk(int k, int c) { return k * (R / 8) + (c ^ ((k & 3) << 2)); }
 
 // Wait until at most N vector-memory instructions of this wave are in flight
-// (loads complete in issue order).
+// (they complete in issue order).
 template <int N>
 MOE_DEV void wait_vmem() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -214,15 +218,22 @@ MOE_DEV void lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Copy 16 bytes per lane from global memory straight into LDS: lane l's
-// bytes land at lds_wave_base + 16 * l (lds_wave_base is wave-uniform, passed
-// in M0). Issued through inline asm so that the only waits on these copies
-// are the explicit ones of the pipeline below (wait_vmem + lds_sync); the
-// instruction has no result registers, and the "memory" clobber keeps LDS
-// reads from moving across it.
-MOE_DEV void dma16(const void *src, const uint4 *lds_wave_base) {
+// Copy 16 (dma16) or 4 (dma4) bytes per lane from global memory straight into
+// LDS: lane l's bytes land at lds_wave_base + size * l (lds_wave_base is
+// wave-uniform, passed in M0). Issued through inline asm so that the only
+// waits on these copies are the explicit ones of the pipeline below
+// (wait_vmem + lds_sync); the instructions have no result registers, and the
+// "memory" clobber keeps LDS reads from moving across them.
+MOE_DEV void dma16(const void *src, const void *lds_wave_base) {
     const uint32_t m0v = (uint32_t)(uintptr_t)(const MOE_LDS void *)lds_wave_base;
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(m0v)
+                 : "memory", "m0");
+}
+MOE_DEV void dma4(const void *src, const void *lds_wave_base) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)(const MOE_LDS void *)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                  :
                  : "v"(src), "s"(m0v)
                  : "memory", "m0");
@@ -233,57 +244,57 @@ MOE_DEV void dma16(const void *src, const uint4 *lds_wave_base) {
 // so each lane picks the global chunk that belongs at its LDS position.
 // NW waves share the copy; IPW instructions per wave.
 //
-// KL = true : K-layout tile [R rows][64 k]; src rows are K-contiguous.
-// KL = false: MN-layout tile [64 k][R cols]; src is [k][ld], cols contiguous.
+// KL = true : K-layout tile [R rows][128 bytes]; src rows are K-contiguous.
+// KL = false: MN-layout tile [64 k][R cols] bf16; src is [k][ld], cols contiguous.
 template <int R, bool KL, int NW>
 struct DmaTile {
     static constexpr int CHUNKS = R * 8;
     static constexpr int IPW = CHUNKS / 64 / NW;
     static_assert(IPW >= 1 && CHUNKS % (64 * NW) == 0, "tile/wave mismatch");
     static_assert(KL || R >= 128, "MN-layout swizzle needs >= 16 chunks per row");
-    // per lane and instruction: source of k-step 0 (nullptr = always zero) and
-    // the k offset (KL: chunk's k; MN: chunk's row) for the K-range check
-    const uint16_t *src[IPW];
+    // per lane and instruction: source of step 0 (nullptr = always zero) and
+    // the chunk's K position (KL: byte offset in the step; MN: k row)
+    const char *src[IPW];
     int kofs[IPW];
-    int64_t kstride;        // elements to advance per k-step of 64
+    int64_t kstride;        // bytes to advance per step
 
-    // KL: row_ptr(r) -> address of element k = 0 of tile row r, or nullptr
+    // KL: row_ptr(r) -> address of byte 0 of tile row r's K run, or nullptr
     template <typename RowFn>
     MOE_DEV void setup_kl(RowFn row_ptr, int wave, int lane) {
 #pragma unroll
         for (int i = 0; i < IPW; i++) {
             const int p = (wave * IPW + i) * 64 + lane;
             const int row = p >> 3, kc = (p & 7) ^ kl_swz(row);
-            const uint16_t *rp = row_ptr(row);
-            src[i] = rp ? rp + kc * 8 : nullptr;
-            kofs[i] = kc * 8;
+            const char *rp = row_ptr(row);
+            src[i] = rp ? rp + kc * 16 : nullptr;
+            kofs[i] = kc * 16;
         }
-        kstride = kBK;
+        kstride = kStepBytes;
     }
-    // MN: base = element (k = 0, col 0) of the tile, ld = row pitch,
+    // MN: base = element (k = 0, col 0) of the tile, ld = row pitch in bytes,
     // cvalid = valid columns
-    MOE_DEV void setup_mn(const uint16_t *base, int64_t ld, int cvalid, int wave, int lane) {
+    MOE_DEV void setup_mn(const char *base, int64_t ld, int cvalid, int wave, int lane) {
 #pragma unroll
         for (int i = 0; i < IPW; i++) {
             const int p = (wave * IPW + i) * 64 + lane;
             const int k = p / (R / 8), c = (p % (R / 8)) ^ ((k & 3) << 2);
-            src[i] = c * 8 < cvalid ? base + (int64_t)k * ld + c * 8 : nullptr;
+            src[i] = c * 8 < cvalid ? base + (int64_t)k * ld + c * 16 : nullptr;
             kofs[i] = k;
         }
-        kstride = kBK * ld;
+        kstride = 64 * ld;
     }
-    // enqueue the copy of k-step kt (k range limit klen) into stage buffer lds
-    MOE_DEV void issue(uint4 *lds, int kt, int klen, int wave) const {
-        const int k0 = kt * kBK;
+    // enqueue the copy of step kt; klim = K bytes (KL) or K rows (MN)
+    MOE_DEV void issue(uint4 *lds, int kt, int klim, int wave) const {
+        const int k0 = kt * (KL ? kStepBytes : 64);
 #pragma unroll
         for (int i = 0; i < IPW; i++) {
-            const bool ok = src[i] != nullptr && k0 + kofs[i] < klen;
+            const bool ok = src[i] != nullptr && k0 + kofs[i] < klim;
             const void *s = ok ? (const void *)(src[i] + kt * kstride)
                                : (const void *)&g_zero_chunk[threadIdx.x & 63];
             dma16(s, lds + (wave * IPW + i) * 64);
         }
     }
-    // MFMA operand for rows/cols r0..r0+31, k slice kk (16 wide):
+    // bf16 MFMA operand for rows/cols r0..r0+31, k slice kk (16 wide):
     // lanes 0-31 get k 16*kk..+7, lanes 32-63 k 16*kk+8..+15
     MOE_DEV static bf16x8 frag(const uint4 *lds, int r0, int kk, int lane) {
         if constexpr (KL) {
@@ -306,30 +317,48 @@ struct DmaTile {
             return __builtin_bit_cast(bf16x8, r);
         }
     }
+    // fp8 MFMA operand (32x32x64) for rows r0..r0+31, K slice s (64 wide) of the
+    // step: lane l holds K 16*(l/32)..+15 of the slice in dwords 0-3 and
+    // 32+16*(l/32)..+15 in dwords 4-7 (layout measured on the GPU)
+    MOE_DEV static i32x8 frag8(const uint4 *lds, int r0, int s, int lane) {
+        static_assert(KL, "fp8 operands are K-contiguous");
+        const int row = r0 + (lane & 31), half = lane >> 5;
+        const uint4 c0 = lds[kl_chunk(row, s * 4 + half)];
+        const uint4 c1 = lds[kl_chunk(row, s * 4 + 2 + half)];
+        i32x8 r = {(int)c0.x, (int)c0.y, (int)c0.z, (int)c0.w,
+                   (int)c1.x, (int)c1.y, (int)c1.z, (int)c1.w};
+        return r;
+    }
 };
 
-// STAGES LDS buffers; the copy of k-step kt+STAGES-1 is enqueued while k-step
-// kt is multiplied, so STAGES-1 copies are in flight behind the MFMAs.
-template <int MODE, int EPI, int BM, int BN, int WM, int WN, int STAGES, int WPE>
+// STAGES LDS buffers; the copy of step kt+STAGES-1 is enqueued while step kt
+// is multiplied, so STAGES-1 copies are in flight behind the MFMAs.
+// FP8: operands are MXFP8 (E4M3 bytes, K-contiguous in every mode) and each
+// stage also holds the E8M0 scale words (4 blocks = one 128-byte step) of its
+// A rows and B rows, copied with one 4-byte LDS-DMA per wave.
+template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int WPE>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void gg_bf16(GemmArgs g) {
+void gg_mfma(GemmArgs g) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(TM >= 1 && TN >= 1, "wave tile");
-    static_assert(STAGES >= 2, "pipeline depth");
+    static_assert(STAGES >= 2 && STAGES <= 3, "pipeline depth");
     static_assert(EPI != MOE_EPI_SWIGLU_FWD || TN % 2 == 0, "SwiGLU pairs gate/up sub-tiles");
-    constexpr bool A_KL = MODE != MOE_GG_WGRAD;
-    constexpr bool B_KL = MODE == MOE_GG_FWD;
+    static_assert(!FP8 || NW * 64 >= BM + BN, "one scale word per lane and stage");
+    constexpr int ESZ = FP8 ? 1 : 2;
+    constexpr bool A_KL = FP8 || MODE != MOE_GG_WGRAD;
+    constexpr bool B_KL = FP8 || MODE == MOE_GG_FWD;
     using AT = DmaTile<BM, A_KL, NW>;
     using BT = DmaTile<BN, B_KL, NW>;
-    constexpr int IPS = AT::IPW + BT::IPW;     // copy instructions per wave per stage
+    constexpr int IPS = AT::IPW + BT::IPW + (FP8 ? 1 : 0);  // copy instructions / wave / stage
 
-    // LDS pool: STAGES x (A tile | B tile) during the K loop; reused after it
-    // to stage the output tile for coalesced stores (the copies into LDS are
-    // issued through inline asm, so the compiler tracks no LDS writes of its
-    // own here and a single array serves every stage)
-    constexpr int STAGE_U4 = (BM + BN) * 8;
+    // LDS pool: STAGES x (A tile | B tile | scale words) during the K loop;
+    // reused after it to stage the output tile for coalesced stores (the
+    // copies into LDS are issued through inline asm, so the compiler tracks no
+    // LDS writes of its own here and a single array serves every stage)
+    constexpr int SCALE_U4 = FP8 ? NW * 64 * 4 / 16 : 0;
+    constexpr int STAGE_U4 = (BM + BN) * 8 + SCALE_U4;
     constexpr bool F32_STAGE = MODE == MOE_GG_WGRAD || EPI == MOE_EPI_SWIGLU_BWD;
     constexpr int PF = BN * 4 + 32;      // fp32 staging pitch (bytes)
     constexpr int PB = BN * 2 + 16;      // bf16 staging pitch (bytes)
@@ -339,7 +368,6 @@ void gg_bf16(GemmArgs g) {
     constexpr int POOL_U4 = STAGES * STAGE_U4 > (EPI_BYTES + 15) / 16 ? STAGES * STAGE_U4
                                                                        : (EPI_BYTES + 15) / 16;
     __shared__ __attribute__((aligned(1024))) uint4 lds_pool[POOL_U4];
-    static_assert(STAGES <= 3, "at most three stages");
     __shared__ int32_t s_off[257];
     __shared__ int32_t s_tile[257];
     __shared__ int32_t s_chunk[257];
@@ -354,9 +382,14 @@ void gg_bf16(GemmArgs g) {
     int n_tiles, total;
     RowSchedule rs;
     if constexpr (MODE == MOE_GG_WGRAD) {
-        // whole experts per XCD: expert e on XCD e % 8, its tiles n-fastest
-        if (tid <= E) s_off[tid] = g.offsets[tid];
-        __syncthreads();
+        // whole experts per XCD: expert e on XCD e % 8, its tiles n-fastest.
+        // FP8: s_tile[e] = sum_{e'<e} ceil(c_e'/128), the 128-row step base of
+        // each expert in the column-block MXFP8 layout.
+        if constexpr (FP8) build_tile_table(g.offsets, E, 128, s_off, s_tile);
+        else {
+            if (tid <= E) s_off[tid] = g.offsets[tid];
+            __syncthreads();
+        }
         n_tiles = (g.N + BN - 1) / BN;
         const int per_e = ((g.M + BM - 1) / BM) * n_tiles;
         total = (E > xcd ? (E - xcd + 7) / 8 : 0) * per_e;
@@ -368,12 +401,15 @@ void gg_bf16(GemmArgs g) {
         total = rs.total;
     }
 
-    const uint16_t *A = reinterpret_cast<const uint16_t *>(g.A);
-    const uint16_t *B = reinterpret_cast<const uint16_t *>(g.B);
+    const char *A = reinterpret_cast<const char *>(g.A);
+    const char *B = reinterpret_cast<const char *>(g.B);
+    const uint8_t *AS = g.a_scale;
+    const uint8_t *BS = g.b_scale;
 
     for (int pos = worker; pos < total; pos += workers) {
         // ---- decode the tile
-        int e, row0 = 0, row_end = 0, m0 = 0, n0, nt, klen;
+        int e, row0 = 0, row_end = 0, m0 = 0, n0, nt, klim;
+        int kpad = 0, sb0 = 0;     // FP8 WGRAD: padded K rows, step base of the expert
         if constexpr (MODE == MOE_GG_WGRAD) {
             const int mtiles = (g.M + BM - 1) / BM;
             const int per_e = mtiles * n_tiles;
@@ -382,46 +418,99 @@ void gg_bf16(GemmArgs g) {
             nt = t % n_tiles;
             m0 = (t / n_tiles) * BM;
             row0 = s_off[e];
-            klen = s_off[e + 1] - row0;     // reduction over the group's rows
+            if constexpr (FP8) {
+                sb0 = s_tile[e];
+                kpad = (s_tile[e + 1] - sb0) * 128;
+                klim = kpad;                     // bytes of K per row
+            } else {
+                klim = s_off[e + 1] - row0;      // reduction over the group's rows
+            }
         } else {
             int mt_e;
             decode_row_tile(rs, s_chunk, s_xpre, E, xcd, pos, e, mt_e, nt);
             row0 = s_off[e] + mt_e * BM;
             row_end = s_off[e + 1];
-            klen = g.K;
+            klim = g.K * ESZ;
         }
         n0 = nt * BN;
 
+        // B row index (in B's N rows) of tile column n, or -1
+        auto b_row_index = [&](int n) -> int {
+            if constexpr (MODE == MOE_GG_FWD && EPI == MOE_EPI_SWIGLU_FWD) {
+                // each wave's panel is laid out as [gate rows | up rows] of the
+                // same hidden units
+                const int wc = n / WTN, off = n % WTN, half = WTN / 2;
+                const int j = nt * (BN / 2) + wc * half + (off % half);
+                if (j >= g.h) return -1;
+                return off < half ? j : g.h + j;
+            } else {
+                const int r = n0 + n;
+                return r < g.N ? r : -1;
+            }
+        };
+
         AT ta;
         BT tb;
-        if constexpr (A_KL) {
-            ta.setup_kl([&](int r) -> const uint16_t * {
+        if constexpr (MODE == MOE_GG_WGRAD) {
+            if constexpr (FP8) {
+                // column-block layout: expert e's A is [M][kpad] at byte sb0*128*M
+                const char *abase = A + (int64_t)sb0 * 128 * g.M;
+                const char *bbase = B + (int64_t)sb0 * 128 * g.N;
+                ta.setup_kl([&](int r) -> const char * {
+                    const int m = m0 + r;
+                    return m < g.M ? abase + (int64_t)m * kpad : nullptr;
+                }, wave, lane);
+                tb.setup_kl([&](int n) -> const char * {
+                    const int c = n0 + n;
+                    return c < g.N ? bbase + (int64_t)c * kpad : nullptr;
+                }, wave, lane);
+            } else {
+                ta.setup_mn(A + ((int64_t)row0 * g.M + m0) * 2, (int64_t)g.M * 2, g.M - m0, wave, lane);
+                tb.setup_mn(B + ((int64_t)row0 * g.N + n0) * 2, (int64_t)g.N * 2, g.N - n0, wave, lane);
+            }
+        } else {
+            ta.setup_kl([&](int r) -> const char * {
                 const int gr = row0 + r;
-                return gr < row_end ? A + (int64_t)gr * g.K : nullptr;
+                return gr < row_end ? A + (int64_t)gr * g.K * ESZ : nullptr;
             }, wave, lane);
-        } else {
-            ta.setup_mn(A + (int64_t)row0 * g.M + m0, g.M, g.M - m0, wave, lane);
+            if constexpr (B_KL) {
+                tb.setup_kl([&](int n) -> const char * {
+                    const int br = b_row_index(n);
+                    return br >= 0 ? B + ((int64_t)e * g.N + br) * g.K * ESZ : nullptr;
+                }, wave, lane);
+            } else {
+                tb.setup_mn(B + ((int64_t)e * g.K * g.N + n0) * 2, (int64_t)g.N * 2, g.N - n0, wave,
+                            lane);
+            }
         }
-        if constexpr (MODE == MOE_GG_FWD) {
-            tb.setup_kl([&](int n) -> const uint16_t * {
-                // B[e] is [N, K]; with SwiGLU each wave's panel is laid out as
-                // [gate rows | up rows] of the same hidden units
-                int wrow;
-                if constexpr (EPI == MOE_EPI_SWIGLU_FWD) {
-                    const int wc = n / WTN, off = n % WTN, half = WTN / 2;
-                    const int j = nt * (BN / 2) + wc * half + (off % half);
-                    if (j >= g.h) return nullptr;
-                    wrow = off < half ? j : g.h + j;
-                } else {
-                    wrow = n0 + n;
-                    if (wrow >= g.N) return nullptr;
+
+        // FP8: source of this lane's scale word (row sr of the stage's
+        // [A rows | B rows | unused] scale array) for step 0
+        const char *ssrc = nullptr;
+        int64_t sstride = 0;
+        if constexpr (FP8) {
+            const int sr = wave * 64 + lane;
+            if constexpr (MODE == MOE_GG_WGRAD) {
+                const int nbk = kpad / 32;                 // scale blocks per row
+                sstride = 4;
+                if (sr < BM) {
+                    const int m = m0 + sr;
+                    if (m < g.M) ssrc = (const char *)AS + (int64_t)sb0 * 4 * g.M + (int64_t)m * nbk;
+                } else if (sr < BM + BN) {
+                    const int c = n0 + sr - BM;
+                    if (c < g.N) ssrc = (const char *)BS + (int64_t)sb0 * 4 * g.N + (int64_t)c * nbk;
                 }
-                return B + ((int64_t)e * g.N + wrow) * g.K;
-            }, wave, lane);
-        } else if constexpr (MODE == MOE_GG_DGRAD) {
-            tb.setup_mn(B + (int64_t)e * g.K * g.N + n0, g.N, g.N - n0, wave, lane);
-        } else {
-            tb.setup_mn(B + (int64_t)row0 * g.N + n0, g.N, g.N - n0, wave, lane);
+            } else {
+                const int nbk = g.K / 32;
+                sstride = 4;
+                if (sr < BM) {
+                    const int gr = row0 + sr;
+                    if (gr < row_end) ssrc = (const char *)AS + (int64_t)gr * nbk;
+                } else if (sr < BM + BN) {
+                    const int br = b_row_index(sr - BM);
+                    if (br >= 0) ssrc = (const char *)BS + ((int64_t)e * g.N + br) * nbk;
+                }
+            }
         }
 
         f32x16 acc[TM][TN];
@@ -432,40 +521,70 @@ void gg_bf16(GemmArgs g) {
 #pragma unroll
                 for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-        const int nk = (klen + kBK - 1) / kBK;
-        auto bufs = [&](auto I) {
+        const int nk = (klim + (A_KL ? kStepBytes : 64) - 1) / (A_KL ? kStepBytes : 64);
+        auto stage = [&](auto I) {
             constexpr int i = decltype(I)::value;
-            return std::make_pair(lds_pool + i * STAGE_U4, lds_pool + i * STAGE_U4 + BM * 8);
+            return lds_pool + i * STAGE_U4;
         };
         auto issue = [&](auto I, int kt) {
-            auto bb = bufs(I);
-            ta.issue(bb.first, kt, klen, wave);
-            tb.issue(bb.second, kt, klen, wave);
+            uint4 *st = stage(I);
+            ta.issue(st, kt, klim, wave);
+            tb.issue(st + BM * 8, kt, klim, wave);
+            if constexpr (FP8) {
+                const void *s = ssrc ? (const void *)(ssrc + kt * sstride)
+                                     : (const void *)&g_zero_chunk[threadIdx.x & 63];
+                dma4(s, st + (BM + BN) * 8 + wave * 16);
+            }
         };
         // one K step with stage buffer CUR (compile time)
         auto step = [&](auto CUR, int kt) {
             constexpr int cur = decltype(CUR)::value;
             constexpr int nb = (cur + STAGES - 1) % STAGES;
-            // copies of later stages may stay in flight; k-step kt's must be done
+            // copies of later stages may stay in flight; step kt's must be done
             if (kt + STAGES - 2 < nk) wait_vmem<(STAGES - 2) * IPS>();
             else wait_vmem<0>();
             lds_sync();
             if (kt + STAGES - 1 < nk) issue(std::integral_constant<int, nb>(), kt + STAGES - 1);
-            auto bb = bufs(CUR);
-            const uint4 *sa = bb.first;
-            const uint4 *sb = bb.second;
+            const uint4 *sa = stage(CUR);
+            const uint4 *sb = sa + BM * 8;
+            if constexpr (FP8) {
+                const uint32_t *sw = reinterpret_cast<const uint32_t *>(sb + BN * 8);
+                uint32_t swa[TM], swb[TN];
 #pragma unroll
-            for (int kk = 0; kk < kBK / 16; kk++) {
-                bf16x8 fa[TM], fb[TN];
+                for (int i = 0; i < TM; i++) swa[i] = sw[wm * WTM + i * 32 + (lane & 31)];
 #pragma unroll
-                for (int i = 0; i < TM; i++) fa[i] = AT::frag(sa, wm * WTM + i * 32, kk, lane);
+                for (int j = 0; j < TN; j++) swb[j] = sw[BM + wn * WTN + j * 32 + (lane & 31)];
 #pragma unroll
-                for (int j = 0; j < TN; j++) fb[j] = BT::frag(sb, wn * WTN + j * 32, kk, lane);
+                for (int sl = 0; sl < 2; sl++) {
+                    // lane l supplies the scale of (row l%32, block 2*sl + l/32)
+                    const int sh = 8 * (2 * sl + (lane >> 5));
+                    i32x8 fa[TM], fb[TN];
 #pragma unroll
-                for (int i = 0; i < TM; i++)
+                    for (int i = 0; i < TM; i++) fa[i] = AT::frag8(sa, wm * WTM + i * 32, sl, lane);
 #pragma unroll
-                    for (int j = 0; j < TN; j++)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < TN; j++) fb[j] = BT::frag8(sb, wn * WTN + j * 32, sl, lane);
+#pragma unroll
+                    for (int i = 0; i < TM; i++)
+#pragma unroll
+                        for (int j = 0; j < TN; j++)
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                fa[i], fb[j], acc[i][j], 0, 0, 0, (int)((swa[i] >> sh) & 0xff), 0,
+                                (int)((swb[j] >> sh) & 0xff));
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < 4; kk++) {
+                    bf16x8 fa[TM], fb[TN];
+#pragma unroll
+                    for (int i = 0; i < TM; i++) fa[i] = AT::frag(sa, wm * WTM + i * 32, kk, lane);
+#pragma unroll
+                    for (int j = 0; j < TN; j++) fb[j] = BT::frag(sb, wn * WTN + j * 32, kk, lane);
+#pragma unroll
+                    for (int i = 0; i < TM; i++)
+#pragma unroll
+                        for (int j = 0; j < TN; j++)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                }
             }
         };
         // the previous tile's LDS reads must be over before its buffers refill
@@ -791,15 +910,15 @@ __global__ __launch_bounds__(256) void gg_f32(GemmArgs g) {
 #define MOE_WG_WN 4
 #endif
 
-template <int MODE, int EPI>
-static void launch_bf16(const GemmArgs &a, hipStream_t s) {
+template <int MODE, int EPI, bool FP8>
+static void launch_mfma(const GemmArgs &a, hipStream_t s) {
     if constexpr (MODE == MOE_GG_WGRAD) {
         const int grid = (num_cus() * MOE_WG_OCC + 7) / 8 * 8;
-        gg_bf16<MODE, EPI, MOE_WG_BM, MOE_WG_BN, MOE_WG_WM, MOE_WG_WN, MOE_WG_STAGES, MOE_WG_WPE>
-            <<<grid, MOE_WG_WM * MOE_WG_WN * 64, 0, s>>>(a);
+        gg_mfma<MODE, EPI, FP8, MOE_WG_BM, MOE_WG_BN, MOE_WG_WM, MOE_WG_WN, MOE_WG_STAGES,
+                MOE_WG_WPE><<<grid, MOE_WG_WM * MOE_WG_WN * 64, 0, s>>>(a);
     } else {
         const int grid = (num_cus() * MOE_ROW_OCC + 7) / 8 * 8;
-        gg_bf16<MODE, EPI, MOE_ROW_BM, MOE_ROW_BN, MOE_ROW_WM, MOE_ROW_WN, MOE_ROW_STAGES,
+        gg_mfma<MODE, EPI, FP8, MOE_ROW_BM, MOE_ROW_BN, MOE_ROW_WM, MOE_ROW_WN, MOE_ROW_STAGES,
                 MOE_ROW_WPE><<<grid, MOE_ROW_WM * MOE_ROW_WN * 64, 0, s>>>(a);
     }
 }
@@ -814,10 +933,13 @@ moe_status gemm_launch(const moe_gemm_desc *d, hipStream_t s) {
     GemmArgs a;
     a.A = d->A; a.B = d->B; a.C = d->C; a.aux = d->aux; a.aux_out = d->aux_out;
     a.offsets = d->offsets; a.rows = d->rows; a.M = d->M; a.N = d->N; a.K = d->K;
+    a.a_scale = d->a_scale; a.b_scale = d->b_scale;
     a.E = d->n_groups;
     a.h = d->epilogue == MOE_EPI_SWIGLU_FWD ? d->N / 2 : d->N;
-    const bool bf = d->dtype == MOE_BF16;
-#define GO(MODE, EPI) (bf ? launch_bf16<MODE, EPI>(a, s) : launch_f32<MODE, EPI>(a, s))
+#define GO(MODE, EPI)                                                          \
+    (d->dtype == MOE_BF16    ? launch_mfma<MODE, EPI, false>(a, s)             \
+     : d->dtype == MOE_MXFP8 ? launch_mfma<MODE, EPI, true>(a, s)              \
+                             : launch_f32<MODE, EPI>(a, s))
     if (d->mode == MOE_GG_FWD) {
         if (d->epilogue == MOE_EPI_SWIGLU_FWD) GO(MOE_GG_FWD, MOE_EPI_SWIGLU_FWD);
         else GO(MOE_GG_FWD, MOE_EPI_NONE);

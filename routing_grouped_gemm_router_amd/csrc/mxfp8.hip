@@ -50,21 +50,28 @@ MOE_DEV float load_elem(const void *p, int64_t i) {
 // axis 1: 4 threads per 32-element block, 8 consecutive elements each.
 template <bool BF16>
 __global__ __launch_bounds__(256) void mx_quant_rows(const void *__restrict__ in, int64_t n_blocks,
+                                                     int64_t cols,
+                                                     const int32_t *__restrict__ row_map,
                                                      uint8_t *__restrict__ q,
                                                      uint8_t *__restrict__ scale) {
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t blk = gid >> 2;
     const bool ok = blk < n_blocks;
-    const int64_t e0 = gid * 8;
+    // input chunk of 8 elements: same position, or the mapped row
+    int64_t src = gid;
+    if (row_map && ok) {
+        const int64_t r = gid * 8 / cols, c8 = gid - r * (cols / 8);
+        src = (int64_t)row_map[r] * (cols / 8) + c8;
+    }
     float f[8];
     if (ok) {
         if constexpr (BF16) {
-            const uint4 v = reinterpret_cast<const uint4 *>(in)[gid];
+            const uint4 v = reinterpret_cast<const uint4 *>(in)[src];
             f[0] = lo_bf16(v.x); f[1] = hi_bf16(v.x); f[2] = lo_bf16(v.y); f[3] = hi_bf16(v.y);
             f[4] = lo_bf16(v.z); f[5] = hi_bf16(v.z); f[6] = lo_bf16(v.w); f[7] = hi_bf16(v.w);
         } else {
-            const float4 a = reinterpret_cast<const float4 *>(in)[gid * 2];
-            const float4 b = reinterpret_cast<const float4 *>(in)[gid * 2 + 1];
+            const float4 a = reinterpret_cast<const float4 *>(in)[src * 2];
+            const float4 b = reinterpret_cast<const float4 *>(in)[src * 2 + 1];
             f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
             f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
         }
@@ -88,7 +95,6 @@ __global__ __launch_bounds__(256) void mx_quant_rows(const void *__restrict__ in
     }
     reinterpret_cast<uint2 *>(q)[gid] = make_uint2(lo, hi);
     if ((threadIdx.x & 3) == 0) scale[blk] = (uint8_t)sb;
-    (void)e0;
 }
 
 // axis 0, grouped and transposed: one workgroup per 32-row block (global
@@ -97,7 +103,9 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void mx_quant_cols(const void *__restrict__ in, int64_t rows,
                                                      int64_t cols,
                                                      const int32_t *__restrict__ group_offsets,
-                                                     int n_groups, uint8_t *__restrict__ q,
+                                                     int n_groups,
+                                                     const int32_t *__restrict__ row_map,
+                                                     uint8_t *__restrict__ q,
                                                      uint8_t *__restrict__ scale) {
     __shared__ int32_t s_bb[1025];   // block base of each group
     __shared__ int32_t s_go[1025];
@@ -109,7 +117,7 @@ __global__ __launch_bounds__(256) void mx_quant_cols(const void *__restrict__ in
         int32_t acc = 0;
         for (int g = 0; g < n_groups; g++) {
             s_bb[g] = acc;
-            acc += (s_go[g + 1] - s_go[g] + 31) / 32;
+            acc += 4 * ((s_go[g + 1] - s_go[g] + 127) / 128);   // groups padded to 128 rows
         }
         s_bb[n_groups] = acc;
     }
@@ -125,10 +133,10 @@ __global__ __launch_bounds__(256) void mx_quant_cols(const void *__restrict__ in
     while (lo + 1 < n_groups && s_bb[lo + 1] <= B) lo++;
     const int g = lo;
     const int64_t len = s_go[g + 1] - s_go[g];
-    const int nb = (int)((len + 31) / 32);
+    const int nb = s_bb[g + 1] - s_bb[g];
     const int b = B - s_bb[g];
     const int64_t r0 = s_go[g] + (int64_t)b * 32;
-    const int n = (int)min<int64_t>(32, len - (int64_t)b * 32);
+    const int n = (int)max<int64_t>(0, min<int64_t>(32, len - (int64_t)b * 32));
     uint8_t *qg = q + (int64_t)s_bb[g] * 32 * cols;
     uint8_t *sg = scale + (int64_t)s_bb[g] * cols;
     for (int64_t c = tid; c < cols; c += 256) {
@@ -136,7 +144,8 @@ __global__ __launch_bounds__(256) void mx_quant_cols(const void *__restrict__ in
         float amax = 0.f;
 #pragma unroll
         for (int i = 0; i < 32; i++) {
-            f[i] = i < n ? load_elem<BF16>(in, (r0 + i) * cols + c) : 0.f;
+            const int64_t rr = row_map ? (int64_t)(i < n ? row_map[r0 + i] : 0) : r0 + i;
+            f[i] = i < n ? load_elem<BF16>(in, rr * cols + c) : 0.f;
             amax = fmaxf(amax, fabsf(f[i]));
         }
         const uint32_t sb = mx_scale_byte(amax);
@@ -158,19 +167,27 @@ __global__ __launch_bounds__(256) void mx_quant_cols(const void *__restrict__ in
 
 moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
                                  int axis, const int32_t *group_offsets, int n_groups,
-                                 uint8_t *q, uint8_t *scale, hipStream_t s) {
+                                 const int32_t *row_map, uint8_t *q, uint8_t *scale,
+                                 hipStream_t s) {
     const bool bf = in_dt == MOE_BF16;
     if (axis == 1) {
         const int64_t n_blocks = rows * cols / 32;
         const unsigned grid = (unsigned)((n_blocks * 4 + 255) / 256);
-        if (bf) mx_quant_rows<true><<<grid, 256, 0, s>>>(in, n_blocks, q, scale);
-        else mx_quant_rows<false><<<grid, 256, 0, s>>>(in, n_blocks, q, scale);
+        if (bf) mx_quant_rows<true><<<grid, 256, 0, s>>>(in, n_blocks, cols, row_map, q, scale);
+        else mx_quant_rows<false><<<grid, 256, 0, s>>>(in, n_blocks, cols, row_map, q, scale);
     } else {
-        const unsigned grid = (unsigned)(rows / 32 + n_groups + 1);
-        if (bf) mx_quant_cols<true><<<grid, 256, 0, s>>>(in, rows, cols, group_offsets, n_groups, q, scale);
-        else mx_quant_cols<false><<<grid, 256, 0, s>>>(in, rows, cols, group_offsets, n_groups, q, scale);
+        // upper bound of the padded block count: sum_g 4*ceil(len_g/128)
+        const unsigned grid = (unsigned)(rows / 32 + 4 * (int64_t)n_groups + 4);
+        if (bf) mx_quant_cols<true><<<grid, 256, 0, s>>>(in, rows, cols, group_offsets, n_groups, row_map, q, scale);
+        else mx_quant_cols<false><<<grid, 256, 0, s>>>(in, rows, cols, group_offsets, n_groups, row_map, q, scale);
     }
     return launch_status();
+}
+
+// size in bytes of the column-block layout's element array (scale array =
+// this / 32) for `rows` rows in n_groups groups: (rows/32 + 4*n_groups + 4) blocks
+size_t mxfp8_col_blocks(int64_t rows, int n_groups) {
+    return (size_t)(rows / 32 + 4 * (int64_t)n_groups + 4);
 }
 
 }  // namespace moe

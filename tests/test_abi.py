@@ -73,9 +73,9 @@ def test_validation_without_gpu(lib):
     assert lib.moe_permute(nul, nul, 1, 0, 64, 2, nul, nul, nul, nul) == 0       # T = 0: no-op
     lib.moe_combine.argtypes = [P, I32, P, P, I64, I32, I32, P, P]
     assert lib.moe_combine(fake, 2, fake, fake, 16, 64, 2, fake, nul) == 3       # no MXFP8 combine
-    lib.mxfp8_quantize.argtypes = [P, I32, I64, I64, I32, P, I32, P, P, P]
-    assert lib.mxfp8_quantize(fake, 1, 64, 40, 1, nul, 0, fake, fake, nul) == 2
-    assert lib.mxfp8_quantize(fake, 1, 64, 64, 2, nul, 0, fake, fake, nul) == 2
+    lib.mxfp8_quantize.argtypes = [P, I32, I64, I64, I32, P, I32, P, P, P, P]
+    assert lib.mxfp8_quantize(fake, 1, 64, 40, 1, nul, 0, nul, fake, fake, nul) == 2
+    assert lib.mxfp8_quantize(fake, 1, 64, 64, 2, nul, 0, nul, fake, fake, nul) == 2
 
 
 def test_gemm_descriptor_validation(lib):
@@ -110,5 +110,34 @@ def test_gemm_descriptor_validation(lib):
     b = BwdDesc()
     b.dtype, b.d, b.h, b.E, b.k, b.T = 1, 64, 64, 8, 2, 16
     assert lib.moe_backward(ctypes.byref(b), None) == 1
-    b.dtype = 2
+    b.dtype = 7
     assert lib.moe_backward(ctypes.byref(b), None) == 3
+    b.dtype = 2                               # MXFP8 needs d % 128 == 0
+    assert lib.moe_backward(ctypes.byref(b), None) == 2
+    b.d = b.h = 128
+    assert lib.moe_backward(ctypes.byref(b), None) == 1       # missing weights / workspace
+
+
+def test_mxfp8_gemm_validation(lib):
+    import sys
+    sys.path.insert(0, ROOT)
+    from routing_grouped_gemm_router_amd import GemmDesc
+    lib.moe_grouped_gemm.argtypes = [ctypes.POINTER(GemmDesc), ctypes.c_void_p]
+    g = GemmDesc()
+    g.mode, g.dtype, g.epilogue, g.n_groups, g.rows = 0, 2, 0, 8, 64
+    g.N, g.K = 64, 128
+    g.offsets = g.A = g.B = g.C = 0x100000
+    assert lib.moe_grouped_gemm(ctypes.byref(g), None) == 1          # scales missing
+    g.a_scale = g.b_scale = 0x100000
+    bad = GemmDesc.from_buffer_copy(g)
+    bad.K = 96                                                       # K % 128
+    assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 2
+    bad = GemmDesc.from_buffer_copy(g)
+    bad.a_scale = 0x100002                                           # scale words 4-byte aligned
+    assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 4
+    bad = GemmDesc.from_buffer_copy(g)
+    bad.aux_out_scale = 0x100000                                     # reserved
+    assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 3
+    lib.mxfp8_col_blocks.argtypes = [ctypes.c_int64, ctypes.c_int32]
+    lib.mxfp8_col_blocks.restype = ctypes.c_size_t
+    assert lib.mxfp8_col_blocks(65536, 128) == 65536 // 32 + 4 * 128 + 4
