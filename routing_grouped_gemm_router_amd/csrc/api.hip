@@ -28,6 +28,9 @@ moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, 
                                  int axis, const int32_t *group_offsets, int n_groups,
                                  const int32_t *row_map, uint8_t *q, uint8_t *scale,
                                  hipStream_t s);
+moe_status mxfp8_quantize_both_launch(const void *in, int64_t rows, int64_t cols,
+                                      const int32_t *group_offsets, int n_groups, uint8_t *q1,
+                                      uint8_t *s1, uint8_t *q0, uint8_t *s0, hipStream_t s);
 size_t mxfp8_col_blocks(int64_t rows, int n_groups);
 
 int num_cus() {
@@ -292,39 +295,39 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
     g.n_groups = E;
     g.rows = R;
     g.offsets = b->offsets;
+    // dy along d (GEMM2 dgrad) and along rows per expert (GEMM2 wgrad), one read
+    if ((st = R > 0 ? mxfp8_quantize_both_launch(b->dy_perm, R, d, b->offsets, E, aq, as, b0q,
+                                                  b0s, s)
+                    : mxfp8_quantize_launch(b->dy_perm, MOE_BF16, R, d, 0, b->offsets, E,
+                                            nullptr, b0q, b0s, s)) != MOE_OK)
+        return st;
     if (R > 0) {
-        // GEMM2 dgrad + SwiGLU backward: dy (along d) . W2t
-        if ((st = mxfp8_quantize_launch(b->dy_perm, MOE_BF16, R, d, 1, nullptr, 1, nullptr, aq,
-                                        as, s)) != MOE_OK)
-            return st;
+        // GEMM2 dgrad + SwiGLU backward: dy . W2t
         g.mode = MOE_GG_DGRAD; g.epilogue = MOE_EPI_SWIGLU_BWD; g.N = h; g.K = d;
         g.A = aq; g.a_scale = as; g.B = b->w2t; g.b_scale = b->w2t_scale;
         g.C = b->dab; g.aux = b->ab;
         if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
     }
     // GEMM2 wgrad: dy and H' along rows, per expert
-    if ((st = mxfp8_quantize_launch(b->dy_perm, MOE_BF16, R, d, 0, b->offsets, E, nullptr, b0q,
-                                    b0s, s)) != MOE_OK)
-        return st;
     if ((st = mxfp8_quantize_launch(b->hp, MOE_BF16, R, h, 0, b->offsets, E, nullptr, b1q, b1s,
                                     s)) != MOE_OK)
         return st;
     g.mode = MOE_GG_WGRAD; g.epilogue = MOE_EPI_NONE; g.aux = nullptr; g.M = d; g.N = h; g.K = 0;
     g.A = b0q; g.a_scale = b0s; g.B = b1q; g.b_scale = b1s; g.C = b->dw2;
     if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
+    // dAB along 2h (GEMM1 dgrad) and along rows per expert (GEMM1 wgrad), one read
+    if ((st = R > 0 ? mxfp8_quantize_both_launch(b->dab, R, 2 * h, b->offsets, E, aq, as, b0q,
+                                                  b0s, s)
+                    : mxfp8_quantize_launch(b->dab, MOE_BF16, R, 2 * h, 0, b->offsets, E,
+                                            nullptr, b0q, b0s, s)) != MOE_OK)
+        return st;
     if (R > 0) {
-        // GEMM1 dgrad: dAB (along 2h) . W1t
-        if ((st = mxfp8_quantize_launch(b->dab, MOE_BF16, R, 2 * h, 1, nullptr, 1, nullptr, aq,
-                                        as, s)) != MOE_OK)
-            return st;
+        // GEMM1 dgrad: dAB . W1t
         g.mode = MOE_GG_DGRAD; g.M = 0; g.N = d; g.K = 2 * h;
         g.A = aq; g.a_scale = as; g.B = b->w1t; g.b_scale = b->w1t_scale; g.C = b->dx_perm;
         if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
     }
     // GEMM1 wgrad: dAB and x[sorted_token] along rows, per expert
-    if ((st = mxfp8_quantize_launch(b->dab, MOE_BF16, R, 2 * h, 0, b->offsets, E, nullptr, b0q,
-                                    b0s, s)) != MOE_OK)
-        return st;
     if ((st = mxfp8_quantize_launch(b->x, MOE_BF16, R, d, 0, b->offsets, E, b->sorted_token, b1q,
                                     b1s, s)) != MOE_OK)
         return st;

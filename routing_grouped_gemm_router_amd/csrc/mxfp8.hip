@@ -47,122 +47,332 @@ MOE_DEV float load_elem(const void *p, int64_t i) {
     else return reinterpret_cast<const float *>(p)[i];
 }
 
-// axis 1: 4 threads per 32-element block, 8 consecutive elements each.
+// axis 1: 2 threads per 32-element block, 16 consecutive elements each
+// (32 B of bf16 in, one 16-B store out).
 template <bool BF16>
 __global__ __launch_bounds__(256) void mx_quant_rows(const void *__restrict__ in, int64_t n_blocks,
                                                      int64_t cols,
                                                      const int32_t *__restrict__ row_map,
                                                      uint8_t *__restrict__ q,
                                                      uint8_t *__restrict__ scale) {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t blk = gid >> 2;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 16-element chunk
+    const int64_t blk = gid >> 1;
     const bool ok = blk < n_blocks;
-    // input chunk of 8 elements: same position, or the mapped row
-    int64_t src = gid;
+    int64_t src = gid * 16;                                          // element offset of the chunk
     if (row_map && ok) {
-        const int64_t r = gid * 8 / cols, c8 = gid - r * (cols / 8);
-        src = (int64_t)row_map[r] * (cols / 8) + c8;
+        const int64_t r = src / cols;
+        src = (int64_t)row_map[r] * cols + (src - r * cols);
     }
-    float f[8];
+    float f[16];
     if (ok) {
         if constexpr (BF16) {
-            const uint4 v = reinterpret_cast<const uint4 *>(in)[src];
-            f[0] = lo_bf16(v.x); f[1] = hi_bf16(v.x); f[2] = lo_bf16(v.y); f[3] = hi_bf16(v.y);
-            f[4] = lo_bf16(v.z); f[5] = hi_bf16(v.z); f[6] = lo_bf16(v.w); f[7] = hi_bf16(v.w);
+            const uint4 *p = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(in) + src);
+            const uint4 v0 = p[0], v1 = p[1];
+            const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int i = 0; i < 8; i++) { f[2 * i] = lo_bf16(w[i]); f[2 * i + 1] = hi_bf16(w[i]); }
         } else {
-            const float4 a = reinterpret_cast<const float4 *>(in)[src * 2];
-            const float4 b = reinterpret_cast<const float4 *>(in)[src * 2 + 1];
-            f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-            f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+            const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(in) + src);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float4 a = p[i];
+                f[4 * i] = a.x; f[4 * i + 1] = a.y; f[4 * i + 2] = a.z; f[4 * i + 3] = a.w;
+            }
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; i++) f[i] = 0.f;
+        for (int i = 0; i < 16; i++) f[i] = 0.f;
     }
     float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(f[i]));
+    for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(f[i]));
     amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
     const uint32_t sb = mx_scale_byte(amax);
     if (!ok) return;
     const int sh = 127 - (int)sb;
-    uint32_t lo = 0, hi = 0;
+    uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        lo |= e4m3_rne_sat(ldexpf(f[i], sh)) << (8 * i);
-        hi |= e4m3_rne_sat(ldexpf(f[i + 4], sh)) << (8 * i);
+        w[i] = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) w[i] |= e4m3_rne_sat(ldexpf(f[4 * i + j], sh)) << (8 * j);
     }
-    reinterpret_cast<uint2 *>(q)[gid] = make_uint2(lo, hi);
-    if ((threadIdx.x & 3) == 0) scale[blk] = (uint8_t)sb;
+    reinterpret_cast<uint4 *>(q)[gid] = make_uint4(w[0], w[1], w[2], w[3]);
+    if ((threadIdx.x & 1) == 0) scale[blk] = (uint8_t)sb;
 }
 
-// axis 0, grouped and transposed: one workgroup per 32-row block (global
-// block index over all groups), one thread per column.
-template <bool BF16>
-__global__ __launch_bounds__(256) void mx_quant_cols(const void *__restrict__ in, int64_t rows,
-                                                     int64_t cols,
-                                                     const int32_t *__restrict__ group_offsets,
-                                                     int n_groups,
-                                                     const int32_t *__restrict__ row_map,
-                                                     uint8_t *__restrict__ q,
-                                                     uint8_t *__restrict__ scale) {
-    __shared__ int32_t s_bb[1025];   // block base of each group
-    __shared__ int32_t s_go[1025];
+// Inclusive prefix sum over a 256-thread workgroup (s_w: 4 ints of LDS).
+MOE_DEV int block_incl_scan(int v, int *s_w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    if (lane == 63) s_w[wave] = v;
+    __syncthreads();
+    for (int w = 0; w < wave; w++) v += s_w[w];
+    return v;
+}
+
+// Unit geometry of the grouped column-block layout. A group's output is a
+// sequence of 128-row units (4 blocks of 32 rows); units are numbered over all
+// groups. Every workgroup first builds s_ub (first unit of each group, by a
+// parallel prefix sum of ceil(len/128)) and s_go (the offsets).
+struct ColUnits {
+    int32_t ub[1025];
+    int32_t go[1025];
+    int w[4];
+};
+
+MOE_DEV int col_units_init(ColUnits &cu, const int32_t *group_offsets, int ng, int64_t rows) {
     const int tid = threadIdx.x;
-    for (int g = tid; g <= n_groups; g += 256)
-        s_go[g] = group_offsets ? group_offsets[g] : (g == 0 ? 0 : (int32_t)rows);
-    __syncthreads();
-    if (tid == 0) {
-        int32_t acc = 0;
-        for (int g = 0; g < n_groups; g++) {
-            s_bb[g] = acc;
-            acc += 4 * ((s_go[g + 1] - s_go[g] + 127) / 128);   // groups padded to 128 rows
+    int u[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int g = 4 * tid + i;
+        u[i] = 0;
+        if (g < ng) {
+            const int32_t a = group_offsets ? group_offsets[g] : 0;
+            const int32_t b = group_offsets ? group_offsets[g + 1] : (int32_t)rows;
+            cu.go[g] = a;
+            if (g == ng - 1) cu.go[ng] = b;
+            u[i] = (b - a + 127) / 128;
         }
-        s_bb[n_groups] = acc;
+        sum += u[i];
+    }
+    int ex = block_incl_scan(sum, cu.w) - sum;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int g = 4 * tid + i;
+        if (g < ng) cu.ub[g] = ex;
+        ex += u[i];
+        if (g == ng - 1) cu.ub[ng] = ex;
     }
     __syncthreads();
-    const int B = blockIdx.x;
-    if (B >= s_bb[n_groups]) return;
-    int lo = 0, hi = n_groups - 1;     // group: largest g with s_bb[g] <= B and a block
+    return cu.ub[ng];
+}
+
+struct UnitGeom {
+    int64_t r0, nb, bb;   // first input row, blocks of the group, first block of the group
+    int j, n;             // unit within the group, valid rows (1..128)
+};
+
+MOE_DEV UnitGeom unit_geom(const ColUnits &cu, int ng, int unit) {
+    int lo = 0, hi = ng - 1;              // largest g with ub[g] <= unit (it has units)
     while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (s_bb[mid] <= B) lo = mid; else hi = mid - 1;
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu.ub[mid] <= unit) lo = mid; else hi = mid - 1;
     }
-    // skip empty groups that share the same base
-    while (lo + 1 < n_groups && s_bb[lo + 1] <= B) lo++;
-    const int g = lo;
-    const int64_t len = s_go[g + 1] - s_go[g];
-    const int nb = s_bb[g + 1] - s_bb[g];
-    const int b = B - s_bb[g];
-    const int64_t r0 = s_go[g] + (int64_t)b * 32;
-    const int n = (int)max<int64_t>(0, min<int64_t>(32, len - (int64_t)b * 32));
-    uint8_t *qg = q + (int64_t)s_bb[g] * 32 * cols;
-    uint8_t *sg = scale + (int64_t)s_bb[g] * cols;
-    for (int64_t c = tid; c < cols; c += 256) {
-        float f[32];
-        float amax = 0.f;
+    UnitGeom u;
+    u.j = unit - cu.ub[lo];
+    u.nb = 4 * (int64_t)(cu.ub[lo + 1] - cu.ub[lo]);
+    u.bb = 4 * (int64_t)cu.ub[lo];
+    u.r0 = (int64_t)cu.go[lo] + 128 * (int64_t)u.j;
+    u.n = (int)min<int64_t>(128, (int64_t)cu.go[lo + 1] - u.r0);
+    return u;
+}
+
+// Encode 32 values (one column block) to 32 E4M3 bytes at dst (16-B aligned)
+// and return the scale byte.
+MOE_DEV uint32_t encode_block32(const float *f, uint8_t *dst) {
+    float amax = 0.f;
 #pragma unroll
-        for (int i = 0; i < 32; i++) {
-            const int64_t rr = row_map ? (int64_t)(i < n ? row_map[r0 + i] : 0) : r0 + i;
-            f[i] = i < n ? load_elem<BF16>(in, rr * cols + c) : 0.f;
-            amax = fmaxf(amax, fabsf(f[i]));
-        }
-        const uint32_t sb = mx_scale_byte(amax);
-        const int sh = 127 - (int)sb;
-        uint32_t w[8];
+    for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(f[i]));
+    const uint32_t sb = mx_scale_byte(amax);
+    const int sh = 127 - (int)sb;
+    uint32_t w[8];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            w[i] = 0;
+    for (int i = 0; i < 8; i++) {
+        w[i] = 0;
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-                w[i] |= (4 * i + j < n ? e4m3_rne_sat(ldexpf(f[4 * i + j], sh)) : 0u) << (8 * j);
-        }
-        uint4 *dst = reinterpret_cast<uint4 *>(qg + c * (int64_t)nb * 32 + (int64_t)b * 32);
-        dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-        sg[c * nb + b] = (uint8_t)sb;
+        for (int e = 0; e < 4; e++) w[i] |= e4m3_rne_sat(ldexpf(f[4 * i + e], sh)) << (8 * e);
     }
+    uint4 *d = reinterpret_cast<uint4 *>(dst);
+    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    return sb;
+}
+
+// axis 0, fp32 input (weights; once per weight update): one workgroup per
+// (unit, 64 columns). The 128 x 64 tile is read with 16-B row loads,
+// transposed through LDS, and each thread encodes one 32-row block of one
+// column; 4 neighbouring threads write the column's 128 contiguous bytes.
+__global__ __launch_bounds__(256) void mx_quant_cols_f32(const float *__restrict__ in, int64_t rows,
+                                                         int64_t cols,
+                                                         const int32_t *__restrict__ group_offsets,
+                                                         int n_groups,
+                                                         const int32_t *__restrict__ row_map,
+                                                         uint8_t *__restrict__ q,
+                                                         uint8_t *__restrict__ scale) {
+    constexpr int TP = 129;               // LDS pitch (floats) of one column: conflict-free writes
+    __shared__ float s_t[64 * TP];
+    __shared__ ColUnits cu;
+    const int tid = threadIdx.x;
+    const int ng = group_offsets ? n_groups : 1;
+    const int n_units = col_units_init(cu, group_offsets, ng, rows);
+    const int64_t c0 = (int64_t)blockIdx.x * 64;
+    for (int unit = blockIdx.y; unit < n_units; unit += gridDim.y) {   // uniform over the workgroup
+        const UnitGeom u = unit_geom(cu, ng, unit);
+        const int ch = tid & 15, rr = tid >> 4;   // 4 columns per load, 16 loads per row
+        const bool cok = c0 + 4 * ch < cols;
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            const int r = rr + 16 * p;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r < u.n && cok) {
+                const int64_t src = row_map ? (int64_t)row_map[u.r0 + r] : u.r0 + r;
+                v = *reinterpret_cast<const float4 *>(in + src * cols + c0 + 4 * ch);
+            }
+            s_t[(4 * ch) * TP + r] = v.x;
+            s_t[(4 * ch + 1) * TP + r] = v.y;
+            s_t[(4 * ch + 2) * TP + r] = v.z;
+            s_t[(4 * ch + 3) * TP + r] = v.w;
+        }
+        __syncthreads();
+        const int cc = tid >> 2, b = tid & 3;
+        const int64_t c = c0 + cc;
+        if (c < cols) {
+            float f[32];
+#pragma unroll
+            for (int i = 0; i < 32; i++) f[i] = s_t[cc * TP + 32 * b + i];
+            const uint32_t sb = encode_block32(f, q + u.bb * 32 * cols + c * u.nb * 32 + 128 * (int64_t)u.j + 32 * b);
+            scale[u.bb * cols + c * u.nb + 4 * u.j + b] = (uint8_t)sb;
+        }
+        __syncthreads();                  // s_t is rewritten by the next unit
+    }
+}
+
+// axis 0, bf16 input (activations and gradients, every step). Persistent over
+// units: a workgroup owns 64 columns and walks units blockIdx.y,
+// blockIdx.y + gridDim.y, ...; the next unit's 16 KiB tile is loaded into
+// registers while the current one is encoded. Thread (ch = tid % 8,
+// rp = tid / 8) loads 8 columns of rows 2rp, 2rp+1 and 2rp+64, 2rp+65; LDS
+// holds the tile transposed as packed row pairs (dword = rows 2i, 2i+1 of one
+// column, pitch 65 dwords), conflict-free for both the writes and the
+// column-block reads. Column tiles vary fastest over the grid, so
+// neighbouring workgroups stream the same input rows.
+// BOTH: the tile is also quantised along its rows into the row-major axis-1
+// layout (q1, s1), row index = position in the grouped order, which saves a
+// second read of tensors needed in both orientations.
+template <bool BOTH>
+__global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__restrict__ in,
+                                                          int64_t rows, int64_t cols,
+                                                          const int32_t *__restrict__ group_offsets,
+                                                          int n_groups,
+                                                          const int32_t *__restrict__ row_map,
+                                                          uint8_t *__restrict__ q,
+                                                          uint8_t *__restrict__ scale,
+                                                          uint8_t *__restrict__ q1,
+                                                          uint8_t *__restrict__ s1) {
+    constexpr int TP = 65;
+    __shared__ uint32_t s_t[64 * TP];
+    __shared__ ColUnits cu;
+    const int tid = threadIdx.x;
+    const int ng = group_offsets ? n_groups : 1;
+    const int n_units = col_units_init(cu, group_offsets, ng, rows);
+    const int64_t c0 = (int64_t)blockIdx.x * 64;
+    const int ch = tid & 7, rp = tid >> 3;
+    const bool cok = c0 + 8 * ch < cols;
+
+    uint4 v[4];                           // rows 2rp, 2rp+1, 2rp+64, 2rp+65
+    auto load = [&](const UnitGeom &u) {
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            const int r = 2 * rp + (p & 1) + 64 * (p >> 1);
+            v[p] = make_uint4(0, 0, 0, 0);
+            if (r < u.n && cok) {
+                const int64_t src = row_map ? (int64_t)row_map[u.r0 + r] : u.r0 + r;
+                v[p] = *reinterpret_cast<const uint4 *>(in + src * cols + c0 + 8 * ch);
+            }
+        }
+    };
+    int unit = blockIdx.y;
+    if (unit >= n_units) return;          // uniform over the workgroup
+    UnitGeom u = unit_geom(cu, ng, unit);
+    load(u);
+    while (true) {
+        // registers -> LDS (packed row pairs), and the row-wise blocks
+#pragma unroll
+        for (int h2 = 0; h2 < 2; h2++) {
+            const uint4 a = v[2 * h2], b = v[2 * h2 + 1];   // rows r, r+1
+            const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+            const int pr = rp + 32 * h2;                     // row pair index
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                s_t[(8 * ch + 2 * e) * TP + pr] = (wa[e] & 0xffffu) | (wb[e] << 16);
+                s_t[(8 * ch + 2 * e + 1) * TP + pr] = (wa[e] >> 16) | (wb[e] & 0xffff0000u);
+            }
+        }
+        if constexpr (BOTH) {             // 32-column block = 4 neighbouring lanes of one row
+#pragma unroll
+            for (int p = 0; p < 4; p++) {
+                const int r = 2 * rp + (p & 1) + 64 * (p >> 1);
+                const uint32_t w[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+                float f[8];
+#pragma unroll
+                for (int e = 0; e < 4; e++) { f[2 * e] = lo_bf16(w[e]); f[2 * e + 1] = hi_bf16(w[e]); }
+                float am = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; e++) am = fmaxf(am, fabsf(f[e]));
+                am = fmaxf(am, __shfl_xor(am, 1, 64));
+                am = fmaxf(am, __shfl_xor(am, 2, 64));
+                if (r < u.n && cok) {
+                    const uint32_t sb = mx_scale_byte(am);
+                    const int sh = 127 - (int)sb;
+                    uint32_t lo4 = 0, hi4 = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        lo4 |= e4m3_rne_sat(ldexpf(f[e], sh)) << (8 * e);
+                        hi4 |= e4m3_rne_sat(ldexpf(f[e + 4], sh)) << (8 * e);
+                    }
+                    *reinterpret_cast<uint2 *>(q1 + (u.r0 + r) * cols + c0 + 8 * ch) = make_uint2(lo4, hi4);
+                    if ((ch & 3) == 0) s1[(u.r0 + r) * (cols / 32) + (c0 + 8 * ch) / 32] = (uint8_t)sb;
+                }
+            }
+        }
+        __syncthreads();
+        const UnitGeom cur = u;
+        const int next = unit + gridDim.y;
+        if (next < n_units) {             // prefetch the next tile while this one is encoded
+            u = unit_geom(cu, ng, next);
+            load(u);
+        }
+        const int cc = tid >> 2, b = tid & 3;
+        const int64_t c = c0 + cc;
+        if (c < cols) {
+            float f[32];
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const uint32_t w = s_t[cc * TP + 16 * b + i];
+                f[2 * i] = lo_bf16(w);
+                f[2 * i + 1] = hi_bf16(w);
+            }
+            const uint32_t sb = encode_block32(f, q + cur.bb * 32 * cols + c * cur.nb * 32 + 128 * (int64_t)cur.j + 32 * b);
+            scale[cur.bb * cols + c * cur.nb + 4 * cur.j + b] = (uint8_t)sb;
+        }
+        if (next >= n_units) break;
+        unit = next;
+        __syncthreads();                  // s_t is rewritten by the next unit
+    }
+}
+
+#ifndef MOE_COLS_PER_CU
+#define MOE_COLS_PER_CU 8
+#endif
+constexpr int kColsPerCU = MOE_COLS_PER_CU;
+
+// column tiles along x; units (upper bound sum_g ceil(len_g/128) <= rows/128 + groups) along
+// y, `per_cu` workgroups per CU in all when the kernel walks several units
+static dim3 cols_grid(int64_t rows, int64_t cols, int ng, int per_cu) {
+    const int64_t xt = (cols + 63) / 64;
+    int64_t y = rows / 128 + ng + 1;
+    if (per_cu > 0) {
+        const int64_t want = ((int64_t)num_cus() * per_cu + xt - 1) / xt;
+        if (want < y) y = want;
+    }
+    if (y > 65535) y = 65535;
+    return dim3((unsigned)xt, (unsigned)(y < 1 ? 1 : y));
 }
 
 moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
@@ -172,15 +382,29 @@ moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, 
     const bool bf = in_dt == MOE_BF16;
     if (axis == 1) {
         const int64_t n_blocks = rows * cols / 32;
-        const unsigned grid = (unsigned)((n_blocks * 4 + 255) / 256);
+        const unsigned grid = (unsigned)((n_blocks * 2 + 255) / 256);
         if (bf) mx_quant_rows<true><<<grid, 256, 0, s>>>(in, n_blocks, cols, row_map, q, scale);
         else mx_quant_rows<false><<<grid, 256, 0, s>>>(in, n_blocks, cols, row_map, q, scale);
     } else {
-        // upper bound of the padded block count: sum_g 4*ceil(len_g/128)
-        const unsigned grid = (unsigned)(rows / 32 + 4 * (int64_t)n_groups + 4);
-        if (bf) mx_quant_cols<true><<<grid, 256, 0, s>>>(in, rows, cols, group_offsets, n_groups, row_map, q, scale);
-        else mx_quant_cols<false><<<grid, 256, 0, s>>>(in, rows, cols, group_offsets, n_groups, row_map, q, scale);
+        const int ng = group_offsets ? n_groups : 1;
+        if (bf)
+            mx_quant_cols_bf16<false><<<cols_grid(rows, cols, ng, kColsPerCU), 256, 0, s>>>(
+                (const uint16_t *)in, rows, cols, group_offsets, n_groups, row_map, q, scale,
+                nullptr, nullptr);
+        else
+            mx_quant_cols_f32<<<cols_grid(rows, cols, ng, 0), 256, 0, s>>>(
+                (const float *)in, rows, cols, group_offsets, n_groups, row_map, q, scale);
     }
+    return launch_status();
+}
+
+// bf16 [rows, cols] in grouped row order -> both the row-major axis-1 layout
+// (q1, s1) and the grouped column-block layout (q0, s0), from one read.
+moe_status mxfp8_quantize_both_launch(const void *in, int64_t rows, int64_t cols,
+                                      const int32_t *group_offsets, int n_groups, uint8_t *q1,
+                                      uint8_t *s1, uint8_t *q0, uint8_t *s0, hipStream_t s) {
+    mx_quant_cols_bf16<true><<<cols_grid(rows, cols, n_groups, kColsPerCU), 256, 0, s>>>(
+        (const uint16_t *)in, rows, cols, group_offsets, n_groups, nullptr, q0, s0, q1, s1);
     return launch_status();
 }
 
