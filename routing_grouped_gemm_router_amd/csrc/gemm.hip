@@ -9,11 +9,9 @@
 // Design for gfx950:
 //  * persistent grid (a fixed number of workgroups per CU). Each workgroup
 //    reads the group offsets from device memory into LDS, scans ceil(c_e/BM)
-//    into a tile table, and walks tile ids t = blockIdx.x, += gridDim.x. A
-//    tile id maps to (m-tile, n-tile) with the n-tile fastest; with a grid
-//    that is a multiple of 8, tile t runs on XCD t % 8, so a given weight
-//    panel (expert, n-tile) is always read by the same XCD and reused from
-//    that XCD's L2 across the expert's m-tiles.
+//    into a tile table, and walks an XCD-aware tile list (below): a weight
+//    panel (expert, n-tile) is read by one XCD and reused from that XCD's L2
+//    across the expert's m-tiles.
 //  * bf16 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulators; each wave owns a
 //    (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.
 //  * both operands are staged into LDS K-contiguous ([rows][64] bf16, 16-byte
@@ -91,16 +89,30 @@ MOE_DEV float silu_f(float a) { return a / (1.f + __expf(-a)); }
 // MI355X has 8 XCDs with a private L2 each, and consecutive workgroup ids go
 // to consecutive XCDs. The persistent grid (a multiple of 8 workgroups) is
 // therefore split per XCD: workgroup b serves XCD x = b % 8 as its (b / 8)-th
-// worker. Each expert's m-tiles are cut into chunks of at most CHM m-tiles;
-// chunk c belongs to XCD c % 8, and an XCD walks its chunks' tiles in order
-// with the n-tile fastest. The ~32 CUs of an XCD thus work on a few m-tiles
-// of one expert at a time: every activation tile and every weight panel is
-// fetched into that XCD's L2 once and served from there to all tiles that
-// need it, instead of being fetched by every XCD.
+// worker. Each expert's m-tiles are cut into chunks of at most CHM m-tiles
+// (an expert of up to kChunkM m-tiles is one chunk); chunk c belongs to XCD
+// c % 8, and an XCD walks its chunks' tiles in order with the m-tile fastest.
+// The ~32 CUs of an XCD thus work on all m-tiles of one chunk and a few of its
+// weight panels at a time: each weight panel is fetched into that XCD's L2
+// once and shared by all of the chunk's m-tiles, and the chunk's activation
+// rows are shared by the concurrent panels. (With the n-tile fastest, the
+// concurrent tiles would touch every panel of the expert and stream the whole
+// weight matrix, larger than the L2, once per pair of m-tiles.)
+// WGRAD gives whole experts to XCDs and orders an expert's output tiles in
+// groups of kWgGroupM m-tiles, m-tile fastest within a group, so the
+// concurrent tiles form a block that shares both operand panels.
 // Correctness does not depend on the XCD mapping: every tile id is owned by
 // exactly one workgroup.
 
 constexpr int kMaxChunks = 2048;
+#ifndef MOE_CHUNK_M
+#define MOE_CHUNK_M 16
+#endif
+constexpr int kChunkM = MOE_CHUNK_M;   // m-tiles per chunk (an expert of up to this many stays on one XCD)
+#ifndef MOE_WG_GROUP_M
+#define MOE_WG_GROUP_M 8
+#endif
+constexpr int kWgGroupM = MOE_WG_GROUP_M;   // WGRAD: m-tiles per tile group
 
 struct RowSchedule {
     int n_tiles;      // n-tiles per m-tile
@@ -115,8 +127,8 @@ MOE_DEV RowSchedule build_row_schedule(const int32_t *s_tile, int E, int n_tiles
                                        int32_t *s_chunk, int32_t *s_xpre) {
     const int tid = threadIdx.x;
     const int mt_total = s_tile[E];
-    // chunk size: at least 8 m-tiles, more when needed to stay within kMaxChunks
-    const int chm = max(8, (mt_total + (kMaxChunks - 256) - 1) / (kMaxChunks - 256));
+    // chunk size: at least kChunkM m-tiles, more when needed to stay within kMaxChunks
+    const int chm = max(kChunkM, (mt_total + (kMaxChunks - 256) - 1) / (kMaxChunks - 256));
     int32_t nc = 0;
     if (tid < E) nc = (s_tile[tid + 1] - s_tile[tid] + chm - 1) / chm;
     if (tid < 256) s_chunk[tid + 1] = nc;
@@ -156,7 +168,7 @@ MOE_DEV RowSchedule build_row_schedule(const int32_t *s_tile, int E, int n_tiles
 }
 
 // position p of this XCD's list -> (group e, m-tile index within e, n-tile)
-MOE_DEV void decode_row_tile(const RowSchedule &rs, const int32_t *s_chunk,
+MOE_DEV void decode_row_tile(const RowSchedule &rs, const int32_t *s_tile, const int32_t *s_chunk,
                              const int32_t *s_xpre, int E, int xcd, int p, int &e, int &mt_e,
                              int &nt) {
     int lo = 0, hi = kMaxChunks / 8;      // largest lc with s_xpre[lc] <= p
@@ -168,8 +180,13 @@ MOE_DEV void decode_row_tile(const RowSchedule &rs, const int32_t *s_chunk,
     const int c = xcd + 8 * lo;
     const int o = p - s_xpre[lo];
     e = find_group(s_chunk, E, c);
-    mt_e = (c - s_chunk[e]) * rs.chm + o / rs.n_tiles;
-    nt = o % rs.n_tiles;
+    // m-tile fastest within the chunk: the XCD's concurrent tiles cover all
+    // of the chunk's m-tiles and a few weight panels, so each weight panel
+    // is fetched into the XCD's L2 once and shared by the chunk's m-tiles
+    const int ci = c - s_chunk[e];
+    const int cm = min(rs.chm, s_tile[e + 1] - s_tile[e] - ci * rs.chm);
+    mt_e = ci * rs.chm + o % cm;
+    nt = o / cm;
 }
 
 // ---------------------------------------------------------------------------
@@ -345,26 +362,35 @@ void gg_mfma(GemmArgs g) {
     static_assert(TM >= 1 && TN >= 1, "wave tile");
     static_assert(STAGES >= 2 && STAGES <= 3, "pipeline depth");
     static_assert(EPI != MOE_EPI_SWIGLU_FWD || TN % 2 == 0, "SwiGLU pairs gate/up sub-tiles");
-    static_assert(!FP8 || NW * 64 >= BM + BN, "one scale word per lane and stage");
+    // FP8: the stage's BM + BN scale words are copied SPW per lane
+    constexpr int SPW = FP8 ? (BM + BN + NW * 64 - 1) / (NW * 64) : 0;
     constexpr int ESZ = FP8 ? 1 : 2;
     constexpr bool A_KL = FP8 || MODE != MOE_GG_WGRAD;
     constexpr bool B_KL = FP8 || MODE == MOE_GG_FWD;
     using AT = DmaTile<BM, A_KL, NW>;
     using BT = DmaTile<BN, B_KL, NW>;
-    constexpr int IPS = AT::IPW + BT::IPW + (FP8 ? 1 : 0);  // copy instructions / wave / stage
+    constexpr int IPS = AT::IPW + BT::IPW + SPW;  // copy instructions / wave / stage
 
     // LDS pool: STAGES x (A tile | B tile | scale words) during the K loop;
     // reused after it to stage the output tile for coalesced stores (the
     // copies into LDS are issued through inline asm, so the compiler tracks no
     // LDS writes of its own here and a single array serves every stage)
-    constexpr int SCALE_U4 = FP8 ? NW * 64 * 4 / 16 : 0;
+    constexpr int SCALE_U4 = SPW * NW * 64 * 4 / 16;
     constexpr int STAGE_U4 = (BM + BN) * 8 + SCALE_U4;
     constexpr bool F32_STAGE = MODE == MOE_GG_WGRAD || EPI == MOE_EPI_SWIGLU_BWD;
     constexpr int PF = BN * 4 + 32;      // fp32 staging pitch (bytes)
     constexpr int PB = BN * 2 + 16;      // bf16 staging pitch (bytes)
     constexpr int PH = BN + 16;          // H' staging pitch (bytes)
-    constexpr int EPI_BYTES = F32_STAGE ? BM * PF
-                            : (EPI == MOE_EPI_SWIGLU_FWD ? BM * PB + BM * PH : BM * PB);
+    // the output tile is staged in passes of EP_ROWS rows, as many rows per
+    // pass as fit in the LDS budget of the pool
+    constexpr int EP_ROW_BYTES = F32_STAGE ? PF : (EPI == MOE_EPI_SWIGLU_FWD ? PB + PH : PB);
+    constexpr int POOL_BUDGET = 152 * 1024;
+    constexpr int EP_ROWS = BM * EP_ROW_BYTES <= POOL_BUDGET       ? BM
+                          : (BM / 2) * EP_ROW_BYTES <= POOL_BUDGET ? BM / 2
+                                                                   : BM / 4;
+    constexpr int EP_PASSES = BM / EP_ROWS;
+    static_assert(EP_ROWS % 32 == 0 && EP_ROWS * EP_ROW_BYTES <= POOL_BUDGET, "epilogue staging");
+    constexpr int EPI_BYTES = EP_ROWS * EP_ROW_BYTES;
     constexpr int POOL_U4 = STAGES * STAGE_U4 > (EPI_BYTES + 15) / 16 ? STAGES * STAGE_U4
                                                                        : (EPI_BYTES + 15) / 16;
     __shared__ __attribute__((aligned(1024))) uint4 lds_pool[POOL_U4];
@@ -415,8 +441,14 @@ void gg_mfma(GemmArgs g) {
             const int per_e = mtiles * n_tiles;
             e = xcd + 8 * (pos / per_e);
             const int t = pos % per_e;
-            nt = t % n_tiles;
-            m0 = (t / n_tiles) * BM;
+            // groups of kWgGroupM m-tiles, m-tile fastest within a group: the
+            // XCD's concurrent tiles form a block of m-tiles x n-tiles, so both
+            // operand panels are shared from L2 by several tiles
+            const int grp = t / (kWgGroupM * n_tiles), first_m = grp * kWgGroupM;
+            const int gm = min(mtiles - first_m, kWgGroupM);
+            const int tg = t - grp * kWgGroupM * n_tiles;
+            nt = tg / gm;
+            m0 = (first_m + tg % gm) * BM;
             row0 = s_off[e];
             if constexpr (FP8) {
                 sb0 = s_tile[e];
@@ -427,7 +459,7 @@ void gg_mfma(GemmArgs g) {
             }
         } else {
             int mt_e;
-            decode_row_tile(rs, s_chunk, s_xpre, E, xcd, pos, e, mt_e, nt);
+            decode_row_tile(rs, s_tile, s_chunk, s_xpre, E, xcd, pos, e, mt_e, nt);
             row0 = s_off[e] + mt_e * BM;
             row_end = s_off[e + 1];
             klim = g.K * ESZ;
@@ -484,31 +516,32 @@ void gg_mfma(GemmArgs g) {
             }
         }
 
-        // FP8: source of this lane's scale word (row sr of the stage's
-        // [A rows | B rows | unused] scale array) for step 0
-        const char *ssrc = nullptr;
-        int64_t sstride = 0;
+        // FP8: sources of this lane's scale words (rows sr of the stage's
+        // [A rows | B rows | unused] scale array) for step 0; 4 bytes per step
+        const char *ssrc[SPW > 0 ? SPW : 1];
         if constexpr (FP8) {
-            const int sr = wave * 64 + lane;
-            if constexpr (MODE == MOE_GG_WGRAD) {
-                const int nbk = kpad / 32;                 // scale blocks per row
-                sstride = 4;
-                if (sr < BM) {
-                    const int m = m0 + sr;
-                    if (m < g.M) ssrc = (const char *)AS + (int64_t)sb0 * 4 * g.M + (int64_t)m * nbk;
-                } else if (sr < BM + BN) {
-                    const int c = n0 + sr - BM;
-                    if (c < g.N) ssrc = (const char *)BS + (int64_t)sb0 * 4 * g.N + (int64_t)c * nbk;
-                }
-            } else {
-                const int nbk = g.K / 32;
-                sstride = 4;
-                if (sr < BM) {
-                    const int gr = row0 + sr;
-                    if (gr < row_end) ssrc = (const char *)AS + (int64_t)gr * nbk;
-                } else if (sr < BM + BN) {
-                    const int br = b_row_index(sr - BM);
-                    if (br >= 0) ssrc = (const char *)BS + ((int64_t)e * g.N + br) * nbk;
+#pragma unroll
+            for (int q = 0; q < SPW; q++) {
+                const int sr = (q * NW + wave) * 64 + lane;
+                ssrc[q] = nullptr;
+                if constexpr (MODE == MOE_GG_WGRAD) {
+                    const int nbk = kpad / 32;             // scale blocks per row
+                    if (sr < BM) {
+                        const int m = m0 + sr;
+                        if (m < g.M) ssrc[q] = (const char *)AS + (int64_t)sb0 * 4 * g.M + (int64_t)m * nbk;
+                    } else if (sr < BM + BN) {
+                        const int c = n0 + sr - BM;
+                        if (c < g.N) ssrc[q] = (const char *)BS + (int64_t)sb0 * 4 * g.N + (int64_t)c * nbk;
+                    }
+                } else {
+                    const int nbk = g.K / 32;
+                    if (sr < BM) {
+                        const int gr = row0 + sr;
+                        if (gr < row_end) ssrc[q] = (const char *)AS + (int64_t)gr * nbk;
+                    } else if (sr < BM + BN) {
+                        const int br = b_row_index(sr - BM);
+                        if (br >= 0) ssrc[q] = (const char *)BS + ((int64_t)e * g.N + br) * nbk;
+                    }
                 }
             }
         }
@@ -531,9 +564,12 @@ void gg_mfma(GemmArgs g) {
             ta.issue(st, kt, klim, wave);
             tb.issue(st + BM * 8, kt, klim, wave);
             if constexpr (FP8) {
-                const void *s = ssrc ? (const void *)(ssrc + kt * sstride)
-                                     : (const void *)&g_zero_chunk[threadIdx.x & 63];
-                dma4(s, st + (BM + BN) * 8 + wave * 16);
+#pragma unroll
+                for (int q = 0; q < SPW; q++) {
+                    const void *s = ssrc[q] ? (const void *)(ssrc[q] + kt * 4)
+                                            : (const void *)&g_zero_chunk[threadIdx.x & 63];
+                    dma4(s, st + (BM + BN) * 8 + (q * NW + wave) * 16);
+                }
             }
         };
         // one K step with stage buffer CUR (compile time)
@@ -554,36 +590,57 @@ void gg_mfma(GemmArgs g) {
                 for (int i = 0; i < TM; i++) swa[i] = sw[wm * WTM + i * 32 + (lane & 31)];
 #pragma unroll
                 for (int j = 0; j < TN; j++) swb[j] = sw[BM + wn * WTN + j * 32 + (lane & 31)];
+                // operand fragments double-buffered in registers: the LDS reads
+                // of K slice sl+1 are issued before the MFMAs of slice sl
+                i32x8 fa[2][TM], fb[2][TN];
+#pragma unroll
+                for (int i = 0; i < TM; i++) fa[0][i] = AT::frag8(sa, wm * WTM + i * 32, 0, lane);
+#pragma unroll
+                for (int j = 0; j < TN; j++) fb[0][j] = BT::frag8(sb, wn * WTN + j * 32, 0, lane);
 #pragma unroll
                 for (int sl = 0; sl < 2; sl++) {
+                    if (sl + 1 < 2) {
+#pragma unroll
+                        for (int i = 0; i < TM; i++) fa[1][i] = AT::frag8(sa, wm * WTM + i * 32, 1, lane);
+#pragma unroll
+                        for (int j = 0; j < TN; j++) fb[1][j] = BT::frag8(sb, wn * WTN + j * 32, 1, lane);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch above the MFMAs
                     // lane l supplies the scale of (row l%32, block 2*sl + l/32)
                     const int sh = 8 * (2 * sl + (lane >> 5));
-                    i32x8 fa[TM], fb[TN];
-#pragma unroll
-                    for (int i = 0; i < TM; i++) fa[i] = AT::frag8(sa, wm * WTM + i * 32, sl, lane);
-#pragma unroll
-                    for (int j = 0; j < TN; j++) fb[j] = BT::frag8(sb, wn * WTN + j * 32, sl, lane);
 #pragma unroll
                     for (int i = 0; i < TM; i++)
 #pragma unroll
                         for (int j = 0; j < TN; j++)
                             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                fa[i], fb[j], acc[i][j], 0, 0, 0, (int)((swa[i] >> sh) & 0xff), 0,
-                                (int)((swb[j] >> sh) & 0xff));
+                                fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0,
+                                (int)((swa[i] >> sh) & 0xff), 0, (int)((swb[j] >> sh) & 0xff));
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
+                // operand fragments double-buffered in registers: the LDS reads
+                // of K slice kk+1 are issued before the MFMAs of slice kk
+                bf16x8 fa[2][TM], fb[2][TN];
+#pragma unroll
+                for (int i = 0; i < TM; i++) fa[0][i] = AT::frag(sa, wm * WTM + i * 32, 0, lane);
+#pragma unroll
+                for (int j = 0; j < TN; j++) fb[0][j] = BT::frag(sb, wn * WTN + j * 32, 0, lane);
 #pragma unroll
                 for (int kk = 0; kk < 4; kk++) {
-                    bf16x8 fa[TM], fb[TN];
+                    const int cb = kk & 1, nb2 = cb ^ 1;
+                    if (kk + 1 < 4) {
 #pragma unroll
-                    for (int i = 0; i < TM; i++) fa[i] = AT::frag(sa, wm * WTM + i * 32, kk, lane);
+                        for (int i = 0; i < TM; i++) fa[nb2][i] = AT::frag(sa, wm * WTM + i * 32, kk + 1, lane);
 #pragma unroll
-                    for (int j = 0; j < TN; j++) fb[j] = BT::frag(sb, wn * WTN + j * 32, kk, lane);
+                        for (int j = 0; j < TN; j++) fb[nb2][j] = BT::frag(sb, wn * WTN + j * 32, kk + 1, lane);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch above the MFMAs
 #pragma unroll
                     for (int i = 0; i < TM; i++)
 #pragma unroll
                         for (int j = 0; j < TN; j++)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
@@ -600,112 +657,120 @@ void gg_mfma(GemmArgs g) {
         }
 
         // ---- epilogue. acc[i][j][v] holds row (v/4)*8 + (lane/32)*4 + v%4 and
-        // column lane%32 of the wave's (i, j) 32x32 tile. The tile is first
-        // written to LDS, then copied out by rows with 16-byte accesses.
-        lds_sync();                                   // stage buffers no longer read
+        // column lane%32 of the wave's (i, j) 32x32 tile. Each pass writes the
+        // 32-row sub-tiles that fall in rows [pr0, pr0 + EP_ROWS) of the tile
+        // to LDS, then copies those rows out with 16-byte accesses.
         char *stg = reinterpret_cast<char *>(lds_pool);
         const int col_l = lane & 31;
-#pragma unroll
-        for (int i = 0; i < TM; i++)
-#pragma unroll
-            for (int j = 0; j < (EPI == MOE_EPI_SWIGLU_FWD ? TN / 2 : TN); j++)
-#pragma unroll
-                for (int v = 0; v < 16; v++) {
-                    const int r = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-                    if constexpr (F32_STAGE) {
-                        const int c = wn * WTN + j * 32 + col_l;
-                        *reinterpret_cast<float *>(stg + r * PF + c * 4) = acc[i][j][v];
-                    } else if constexpr (EPI == MOE_EPI_SWIGLU_FWD) {
-                        const int jt = wn * (WTN / 2) + j * 32 + col_l;
-                        const float a = acc[i][j][v], b = acc[i][j + TN / 2][v];
-                        uint16_t *abr = reinterpret_cast<uint16_t *>(stg + r * PB);
-                        abr[jt] = f32_to_bf16(a);
-                        abr[BN / 2 + jt] = f32_to_bf16(b);
-                        reinterpret_cast<uint16_t *>(stg + BM * PB + r * PH)[jt] =
-                            f32_to_bf16(silu_f(a) * b);
-                    } else {
-                        const int c = wn * WTN + j * 32 + col_l;
-                        reinterpret_cast<uint16_t *>(stg + r * PB)[c] = f32_to_bf16(acc[i][j][v]);
-                    }
-                }
-        lds_sync();
         constexpr int NT = NW * 64;
-        if constexpr (MODE == MOE_GG_WGRAD) {
-            float *C = reinterpret_cast<float *>(g.C) + (int64_t)e * g.M * g.N;
-            constexpr int CPR = BN / 4;
-            for (int it = tid; it < BM * CPR; it += NT) {
-                const int r = it / CPR, c = it % CPR;
-                const int m = m0 + r, n = n0 + c * 4;
-                if (m < g.M && n < g.N)
-                    *reinterpret_cast<uint4 *>(C + (int64_t)m * g.N + n) =
-                        *reinterpret_cast<const uint4 *>(stg + r * PF + c * 16);
-            }
-        } else if constexpr (EPI == MOE_EPI_SWIGLU_BWD) {
-            const uint16_t *AB = reinterpret_cast<const uint16_t *>(g.aux);
-            uint16_t *dAB = reinterpret_cast<uint16_t *>(g.C);
-            const int h = g.h;
-            constexpr int CPR = BN / 8;
-            for (int it = tid; it < BM * CPR; it += NT) {
-                const int r = it / CPR, c = it % CPR;
-                const int grow = row0 + r, jj = n0 + c * 8;
-                if (grow >= row_end || jj >= h) continue;
-                const uint16_t *abr = AB + (int64_t)grow * 2 * h;
-                const uint4 ua = *reinterpret_cast<const uint4 *>(abr + jj);
-                const uint4 ub = *reinterpret_cast<const uint4 *>(abr + h + jj);
-                const float4 d0 = *reinterpret_cast<const float4 *>(stg + r * PF + c * 32);
-                const float4 d1 = *reinterpret_cast<const float4 *>(stg + r * PF + c * 32 + 16);
-                const float dh[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-                const uint32_t wa[4] = {ua.x, ua.y, ua.z, ua.w}, wb[4] = {ub.x, ub.y, ub.z, ub.w};
-                uint32_t oa[4], ob[4];
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    float da2[2], db2[2];
+        for (int pass = 0; pass < EP_PASSES; pass++) {
+            const int pr0 = pass * EP_ROWS;
+            lds_sync();                               // stage buffers / previous pass no longer read
 #pragma unroll
-                    for (int hh = 0; hh < 2; hh++) {
-                        const float a = hh ? hi_bf16(wa[q]) : lo_bf16(wa[q]);
-                        const float b = hh ? hi_bf16(wb[q]) : lo_bf16(wb[q]);
-                        const float sg = 1.f / (1.f + __expf(-a));
-                        const float d = dh[2 * q + hh];
-                        da2[hh] = d * b * sg * (1.f + a * (1.f - sg));
-                        db2[hh] = d * a * sg;
+            for (int i = 0; i < TM; i++) {
+                const int rb = wm * WTM + i * 32;     // wave-uniform
+                if (rb < pr0 || rb >= pr0 + EP_ROWS) continue;
+#pragma unroll
+                for (int j = 0; j < (EPI == MOE_EPI_SWIGLU_FWD ? TN / 2 : TN); j++)
+#pragma unroll
+                    for (int v = 0; v < 16; v++) {
+                        const int r = rb - pr0 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                        if constexpr (F32_STAGE) {
+                            const int c = wn * WTN + j * 32 + col_l;
+                            *reinterpret_cast<float *>(stg + r * PF + c * 4) = acc[i][j][v];
+                        } else if constexpr (EPI == MOE_EPI_SWIGLU_FWD) {
+                            const int jt = wn * (WTN / 2) + j * 32 + col_l;
+                            const float a = acc[i][j][v], b = acc[i][j + TN / 2][v];
+                            uint16_t *abr = reinterpret_cast<uint16_t *>(stg + r * PB);
+                            abr[jt] = f32_to_bf16(a);
+                            abr[BN / 2 + jt] = f32_to_bf16(b);
+                            reinterpret_cast<uint16_t *>(stg + EP_ROWS * PB + r * PH)[jt] =
+                                f32_to_bf16(silu_f(a) * b);
+                        } else {
+                            const int c = wn * WTN + j * 32 + col_l;
+                            reinterpret_cast<uint16_t *>(stg + r * PB)[c] = f32_to_bf16(acc[i][j][v]);
+                        }
                     }
-                    oa[q] = pack_bf16x2(da2[0], da2[1]);
-                    ob[q] = pack_bf16x2(db2[0], db2[1]);
+            }
+            lds_sync();
+            if constexpr (MODE == MOE_GG_WGRAD) {
+                float *C = reinterpret_cast<float *>(g.C) + (int64_t)e * g.M * g.N;
+                constexpr int CPR = BN / 4;
+                for (int it = tid; it < EP_ROWS * CPR; it += NT) {
+                    const int r = it / CPR, c = it % CPR;
+                    const int m = m0 + pr0 + r, n = n0 + c * 4;
+                    if (m < g.M && n < g.N)
+                        *reinterpret_cast<uint4 *>(C + (int64_t)m * g.N + n) =
+                            *reinterpret_cast<const uint4 *>(stg + r * PF + c * 16);
                 }
-                uint16_t *dr = dAB + (int64_t)grow * 2 * h;
-                *reinterpret_cast<uint4 *>(dr + jj) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
-                *reinterpret_cast<uint4 *>(dr + h + jj) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
-            }
-        } else if constexpr (EPI == MOE_EPI_SWIGLU_FWD) {
-            uint16_t *AB = reinterpret_cast<uint16_t *>(g.C);
-            uint16_t *HP = reinterpret_cast<uint16_t *>(g.aux_out);
-            const int h = g.h, j0 = nt * (BN / 2);
-            constexpr int CPR = BN / 8;               // gate half then up half
-            for (int it = tid; it < BM * CPR; it += NT) {
-                const int r = it / CPR, c = it % CPR;
-                const int grow = row0 + r;
-                const int half = c >= CPR / 2, jj = j0 + (c - half * (CPR / 2)) * 8;
-                if (grow >= row_end || jj >= h) continue;
-                *reinterpret_cast<uint4 *>(AB + (int64_t)grow * 2 * h + half * h + jj) =
-                    *reinterpret_cast<const uint4 *>(stg + r * PB + c * 16);
-            }
-            constexpr int CPH = BN / 16;
-            for (int it = tid; it < BM * CPH; it += NT) {
-                const int r = it / CPH, c = it % CPH;
-                const int grow = row0 + r, jj = j0 + c * 8;
-                if (grow >= row_end || jj >= h) continue;
-                *reinterpret_cast<uint4 *>(HP + (int64_t)grow * h + jj) =
-                    *reinterpret_cast<const uint4 *>(stg + BM * PB + r * PH + c * 16);
-            }
-        } else {
-            uint16_t *C = reinterpret_cast<uint16_t *>(g.C);
-            constexpr int CPR = BN / 8;
-            for (int it = tid; it < BM * CPR; it += NT) {
-                const int r = it / CPR, c = it % CPR;
-                const int grow = row0 + r, n = n0 + c * 8;
-                if (grow < row_end && n < g.N)
-                    *reinterpret_cast<uint4 *>(C + (int64_t)grow * g.N + n) =
+            } else if constexpr (EPI == MOE_EPI_SWIGLU_BWD) {
+                const uint16_t *AB = reinterpret_cast<const uint16_t *>(g.aux);
+                uint16_t *dAB = reinterpret_cast<uint16_t *>(g.C);
+                const int h = g.h;
+                constexpr int CPR = BN / 8;
+                for (int it = tid; it < EP_ROWS * CPR; it += NT) {
+                    const int r = it / CPR, c = it % CPR;
+                    const int grow = row0 + pr0 + r, jj = n0 + c * 8;
+                    if (grow >= row_end || jj >= h) continue;
+                    const uint16_t *abr = AB + (int64_t)grow * 2 * h;
+                    const uint4 ua = *reinterpret_cast<const uint4 *>(abr + jj);
+                    const uint4 ub = *reinterpret_cast<const uint4 *>(abr + h + jj);
+                    const float4 d0 = *reinterpret_cast<const float4 *>(stg + r * PF + c * 32);
+                    const float4 d1 = *reinterpret_cast<const float4 *>(stg + r * PF + c * 32 + 16);
+                    const float dh[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                    const uint32_t wa[4] = {ua.x, ua.y, ua.z, ua.w}, wb[4] = {ub.x, ub.y, ub.z, ub.w};
+                    uint32_t oa[4], ob[4];
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        float da2[2], db2[2];
+#pragma unroll
+                        for (int hh = 0; hh < 2; hh++) {
+                            const float a = hh ? hi_bf16(wa[q]) : lo_bf16(wa[q]);
+                            const float b = hh ? hi_bf16(wb[q]) : lo_bf16(wb[q]);
+                            const float sg = 1.f / (1.f + __expf(-a));
+                            const float d = dh[2 * q + hh];
+                            da2[hh] = d * b * sg * (1.f + a * (1.f - sg));
+                            db2[hh] = d * a * sg;
+                        }
+                        oa[q] = pack_bf16x2(da2[0], da2[1]);
+                        ob[q] = pack_bf16x2(db2[0], db2[1]);
+                    }
+                    uint16_t *dr = dAB + (int64_t)grow * 2 * h;
+                    *reinterpret_cast<uint4 *>(dr + jj) = make_uint4(oa[0], oa[1], oa[2], oa[3]);
+                    *reinterpret_cast<uint4 *>(dr + h + jj) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
+                }
+            } else if constexpr (EPI == MOE_EPI_SWIGLU_FWD) {
+                uint16_t *AB = reinterpret_cast<uint16_t *>(g.C);
+                uint16_t *HP = reinterpret_cast<uint16_t *>(g.aux_out);
+                const int h = g.h, j0 = nt * (BN / 2);
+                constexpr int CPR = BN / 8;           // gate half then up half
+                for (int it = tid; it < EP_ROWS * CPR; it += NT) {
+                    const int r = it / CPR, c = it % CPR;
+                    const int grow = row0 + pr0 + r;
+                    const int half = c >= CPR / 2, jj = j0 + (c - half * (CPR / 2)) * 8;
+                    if (grow >= row_end || jj >= h) continue;
+                    *reinterpret_cast<uint4 *>(AB + (int64_t)grow * 2 * h + half * h + jj) =
                         *reinterpret_cast<const uint4 *>(stg + r * PB + c * 16);
+                }
+                constexpr int CPH = BN / 16;
+                for (int it = tid; it < EP_ROWS * CPH; it += NT) {
+                    const int r = it / CPH, c = it % CPH;
+                    const int grow = row0 + pr0 + r, jj = j0 + c * 8;
+                    if (grow >= row_end || jj >= h) continue;
+                    *reinterpret_cast<uint4 *>(HP + (int64_t)grow * h + jj) =
+                        *reinterpret_cast<const uint4 *>(stg + EP_ROWS * PB + r * PH + c * 16);
+                }
+            } else {
+                uint16_t *C = reinterpret_cast<uint16_t *>(g.C);
+                constexpr int CPR = BN / 8;
+                for (int it = tid; it < EP_ROWS * CPR; it += NT) {
+                    const int r = it / CPR, c = it % CPR;
+                    const int grow = row0 + pr0 + r, n = n0 + c * 8;
+                    if (grow < row_end && n < g.N)
+                        *reinterpret_cast<uint4 *>(C + (int64_t)grow * g.N + n) =
+                            *reinterpret_cast<const uint4 *>(stg + r * PB + c * 16);
+                }
             }
         }
     }
