@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="e128_bf16")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-padded", action="store_true",
+                    help="skip the padded-capacity comparison (bf16 fwd+bwd workloads)")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens in the oracle's bounded sample")
     ap.add_argument("--breakdown", action="store_true",
@@ -141,6 +143,10 @@ def main():
     flops = w.fwd_bwd_flops() if w.backward else w.fwd_flops()
     peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
 
+    padded = None
+    if not mx and w.backward and not a.no_padded:
+        padded = padded_baseline(moe, torch, inp, w, a.steps, a.warmup)
+        padded["dropless_speedup"] = padded["ms_per_step"] / ms
     if a.breakdown and not mx:
         breakdown(moe, torch, layer, x, logits, dout, w)
     if a.copy_calib:
@@ -186,9 +192,38 @@ def main():
             "flops_per_launch": g1_flops,
         },
     }
+    if padded is not None:
+        res["padded_baseline"] = padded
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, w, a.cpu_tokens)
     print(json.dumps(res), flush=True)
+
+
+def padded_baseline(moe, torch, inp, w, steps, warmup):
+    """The padded-capacity alternative on the same inputs: the same kernels,
+    every expert padded to ceil(1.25 T*k / E) rows, overflow rows dropped.
+    Timed like the main loop, after it (outside the main timed region)."""
+    import synth
+
+    C = synth.capacity(w)
+    layer = moe.MoELayerPadded(inp["w1"], inp["w2"], w.k, C)
+
+    def step():
+        layer.forward(inp["x"], inp["logits"])
+        layer.backward(inp["dout"])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    dropped = int((layer.pad["token_pos"] < 0).sum().item())
+    return {"capacity": C, "computed_rows": w.E * C, "routed_rows": w.R,
+            "dropped_frac": dropped / w.R, "ms_per_step": el * 1e3 / steps,
+            "tokens_per_s": w.T * steps / el}
 
 
 def cpu_baseline(inp, w, n_tok):

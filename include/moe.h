@@ -292,6 +292,36 @@ moe_status mxfp8_quantize(const void *in, moe_dtype in_dt, int64_t rows, int64_t
 /* Worst-case block count of the column-block layout: rows/32 + 4*n_groups + 4. */
 size_t mxfp8_col_blocks(int64_t rows, int32_t n_groups);
 
+/* ------------------------------------------------------------------ */
+/* Padded-capacity alternative (for comparison)                         */
+
+/* The report measures the device-scheduled grouped GEMM against padding every
+ * expert's batch to one uniform capacity (Ai2 Olmo-core 3, kongchang.com,
+ * "routing is a systems problem"). These two calls turn the dropless routing
+ * metadata of moe_route into that layout, so that moe_permute, the grouped
+ * GEMM, moe_combine and moe_backward run on it unchanged:
+ *   expert e owns rows [e*C, (e+1)*C) of [E*C, .] buffers; its routed rows
+ *   keep their rank in ascending token order, the ones of rank >= C are
+ *   dropped (position -1: not dispatched, no contribution to the output, no
+ *   gradient, gates not renormalised).
+ *
+ * moe_capacity_pad: token_pos_pad[t, j] = e*C + r if r < C, else -1, where
+ * e = topk_idx[t, j] and r = token_pos[t, j] - offsets[e]; offsets_pad[e] =
+ * e*C for e = 0..E (device, E+1 entries). Inputs are moe_route's outputs.
+ * Needs E*C < 2^31.
+ *
+ * moe_capacity_zero_rows: zeroes the unused capacity rows of a [E*C, cols]
+ * buffer (dt = MOE_F32 or MOE_BF16, 16-byte aligned), i.e. rows
+ * [e*C + min(c_e, C), (e+1)*C) of every expert, with c_e from the dropless
+ * offsets. Call it on the dispatch buffer after moe_permute and on dy_perm
+ * before moe_backward, so empty rows contribute nothing to dW. */
+moe_status moe_capacity_pad(const int32_t *topk_idx, const int32_t *token_pos,
+                            const int32_t *offsets, int64_t T, int32_t E, int32_t k,
+                            int32_t capacity, int32_t *token_pos_pad, int32_t *offsets_pad,
+                            void *stream);
+moe_status moe_capacity_zero_rows(void *buf, moe_dtype dt, const int32_t *offsets, int32_t E,
+                                  int32_t capacity, int32_t cols, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

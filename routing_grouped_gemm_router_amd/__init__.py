@@ -86,6 +86,10 @@ def _load():
     lib.mxfp8_quantize.restype = _I32
     lib.mxfp8_col_blocks.argtypes = [_I64, _I32]
     lib.mxfp8_col_blocks.restype = _SZ
+    lib.moe_capacity_pad.argtypes = [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P]
+    lib.moe_capacity_pad.restype = _I32
+    lib.moe_capacity_zero_rows.argtypes = [_P, _I32, _P, _I32, _I32, _I32, _P]
+    lib.moe_capacity_zero_rows.restype = _I32
     return lib
 
 
@@ -286,6 +290,30 @@ def mxfp8_quantize(x: torch.Tensor, axis: int = 1, group_offsets: torch.Tensor |
     return q, scale
 
 
+def moe_capacity_pad(route: dict, capacity: int, out: dict | None = None) -> dict:
+    """Padded-capacity layout of moe_route's dropless metadata (see moe.h):
+    token_pos [T, k] with dropped slots at -1, offsets [E+1] = e * capacity."""
+    T, k = route["topk_idx"].shape
+    E = route["offsets"].numel() - 1
+    dev = route["offsets"].device
+    if out is None:
+        out = dict(token_pos=torch.empty((T, k), dtype=torch.int32, device=dev),
+                   offsets=torch.empty(E + 1, dtype=torch.int32, device=dev))
+    _check("moe_capacity_pad", _lib.moe_capacity_pad(
+        _p(route["topk_idx"]), _p(route["token_pos"]), _p(route["offsets"]), T, E, k, capacity,
+        _p(out["token_pos"]), _p(out["offsets"]), _stream()))
+    return out
+
+
+def moe_capacity_zero_rows(buf: torch.Tensor, offsets: torch.Tensor, capacity: int) -> torch.Tensor:
+    """Zero the unused capacity rows of a [E*capacity, cols] buffer; offsets
+    are the dropless ones (see moe.h)."""
+    E = offsets.numel() - 1
+    _check("moe_capacity_zero_rows", _lib.moe_capacity_zero_rows(
+        _p(buf), _dt(buf), _p(offsets), E, capacity, buf.shape[-1], _stream()))
+    return buf
+
+
 # ---------------------------------------------------------------------------
 # the layer
 
@@ -344,6 +372,64 @@ class MoELayer:
         self.grads = moe_backward(self.saved(), dout, self.E, self.k, self.d, self.h,
                                   out=self.grads)
         return self.grads
+
+
+class MoELayerPadded(MoELayer):
+    """The padded-capacity alternative the report compares the dropless layer
+    against: every expert owns `capacity` rows of [E*capacity, .] buffers,
+    rows past an expert's capacity are dropped (no output, no gradient, gates
+    not renormalised) and its unused rows are zero. Routing, dispatch, the
+    grouped GEMMs, combine and the backward are the dropless layer's own
+    kernels, run on the padded metadata, so only the padding differs."""
+
+    def __init__(self, w1: torch.Tensor, w2: torch.Tensor, k: int, capacity: int):
+        super().__init__(w1, w2, k)
+        self.capacity = capacity
+
+    def _alloc(self, T, dev, dt):
+        if self._T == T:
+            return
+        super()._alloc(T, dev, dt)
+        E, k, d, h, C = self.E, self.k, self.d, self.h, self.capacity
+        P = max(E * C, 1)   # capacity 0 drops everything; keep the buffers non-null
+        self.pad = dict(token_pos=torch.empty((T, k), dtype=torch.int32, device=dev),
+                        offsets=torch.empty(E + 1, dtype=torch.int32, device=dev))
+        self.x_perm = torch.empty((P, d), dtype=dt, device=dev)
+        self.ab = torch.empty((P, 2 * h), dtype=dt, device=dev)
+        self.hp = torch.empty((P, h), dtype=dt, device=dev)
+        self.y_perm = torch.empty((P, d), dtype=dt, device=dev)
+        self.grads = dict(dx=torch.empty((T, d), dtype=dt, device=dev),
+                          dlogits=torch.empty((T, E), dtype=torch.float32, device=dev),
+                          dw1=torch.empty((E, 2 * h, d), dtype=torch.float32, device=dev),
+                          dw2=torch.empty((E, d, h), dtype=torch.float32, device=dev),
+                          dgate=torch.empty((T, k), dtype=torch.float32, device=dev),
+                          dy_perm=torch.empty((P, d), dtype=dt, device=dev),
+                          dab=torch.empty((P, 2 * h), dtype=dt, device=dev),
+                          dx_perm=torch.empty((P, d), dtype=dt, device=dev))
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor) -> torch.Tensor:
+        T, d = x.shape
+        C = self.capacity
+        self._alloc(T, x.device, x.dtype)
+        r = moe_route(logits, self.k, out=self.route, ws=self.route_ws)
+        p = moe_capacity_pad(r, C, out=self.pad)
+        moe_permute(x, p["token_pos"], self.x_perm)
+        moe_capacity_zero_rows(self.x_perm, r["offsets"], C)
+        moe_grouped_gemm(MOE_GG_FWD, self.x_perm, self.w1, self.ab, p["offsets"],
+                         MOE_EPI_SWIGLU_FWD, N=2 * self.h, K=d, aux_out=self.hp)
+        moe_grouped_gemm(MOE_GG_FWD, self.hp, self.w2, self.y_perm, p["offsets"], N=d, K=self.h)
+        moe_combine(self.y_perm, r["topk_gate"], p["token_pos"], self.out)
+        return self.out
+
+    def saved(self) -> dict:
+        sv = super().saved()
+        sv["token_pos"] = self.pad["token_pos"]
+        sv["offsets"] = self.pad["offsets"]
+        return sv
+
+    def backward(self, dout: torch.Tensor) -> dict:
+        moe_capacity_zero_rows(self.grads["dy_perm"], self.route["offsets"], self.capacity)
+        return super().backward(dout)
 
 
 class MoELayerMX:

@@ -32,6 +32,11 @@ moe_status mxfp8_quantize_both_launch(const void *in, int64_t rows, int64_t cols
                                       const int32_t *group_offsets, int n_groups, uint8_t *q1,
                                       uint8_t *s1, uint8_t *q0, uint8_t *s0, hipStream_t s);
 size_t mxfp8_col_blocks(int64_t rows, int n_groups);
+moe_status capacity_pad_launch(const int32_t *topk_idx, const int32_t *token_pos,
+                               const int32_t *offsets, int64_t T, int E, int k, int C,
+                               int32_t *token_pos_pad, int32_t *offsets_pad, hipStream_t s);
+moe_status capacity_zero_launch(void *buf, moe_dtype dt, const int32_t *offsets, int E, int C,
+                                int cols, hipStream_t s);
 
 int num_cus() {
     static int cache[64] = {0};
@@ -340,6 +345,31 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
 }
 
 size_t mxfp8_col_blocks(int64_t rows, int32_t n_groups) { return moe::mxfp8_col_blocks(rows, n_groups); }
+
+moe_status moe_capacity_pad(const int32_t *topk_idx, const int32_t *token_pos,
+                            const int32_t *offsets, int64_t T, int32_t E, int32_t k,
+                            int32_t capacity, int32_t *token_pos_pad, int32_t *offsets_pad,
+                            void *stream) {
+    if (!routing_shape_ok(T, E, k) || capacity < 0 ||
+        (int64_t)E * capacity >= ((int64_t)1 << 31))
+        return MOE_ERR_SHAPE;
+    if (!offsets_pad) return MOE_ERR_NULL;
+    if (T > 0 && (!topk_idx || !token_pos || !offsets || !token_pos_pad)) return MOE_ERR_NULL;
+    return capacity_pad_launch(topk_idx, token_pos, offsets, T, E, k, capacity, token_pos_pad,
+                               offsets_pad, (hipStream_t)stream);
+}
+
+moe_status moe_capacity_zero_rows(void *buf, moe_dtype dt, const int32_t *offsets, int32_t E,
+                                  int32_t capacity, int32_t cols, void *stream) {
+    if (dt != MOE_F32 && dt != MOE_BF16) return MOE_ERR_DTYPE;
+    if (E < 1 || E > 256 || capacity < 0 || !width_ok(cols) ||
+        (int64_t)E * capacity >= ((int64_t)1 << 31))
+        return MOE_ERR_SHAPE;
+    if (capacity == 0) return MOE_OK;
+    if (!buf || !offsets) return MOE_ERR_NULL;
+    if (!aligned16(buf)) return MOE_ERR_ALIGN;
+    return capacity_zero_launch(buf, dt, offsets, E, capacity, cols, (hipStream_t)stream);
+}
 
 moe_status mxfp8_quantize(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
                           int32_t axis, const int32_t *group_offsets, int32_t n_groups,

@@ -23,8 +23,13 @@ def declared():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from routing_grouped_gemm_router_amd.build import build
-        build()
+        # load the build script by path (importing the package needs the library)
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_moe_build", os.path.join(ROOT, "routing_grouped_gemm_router_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     return ctypes.CDLL(LIB)
 
 
@@ -141,3 +146,24 @@ def test_mxfp8_gemm_validation(lib):
     lib.mxfp8_col_blocks.argtypes = [ctypes.c_int64, ctypes.c_int32]
     lib.mxfp8_col_blocks.restype = ctypes.c_size_t
     assert lib.mxfp8_col_blocks(65536, 128) == 65536 // 32 + 4 * 128 + 4
+
+
+def test_capacity_validation(lib):
+    """Host-side checks of the padded-capacity calls (nothing is launched)."""
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.moe_capacity_pad.argtypes = [P, P, P, I64, I32, I32, I32, P, P, P]
+    lib.moe_capacity_zero_rows.argtypes = [P, I32, P, I32, I32, I32, P]
+    buf = ctypes.create_string_buffer(4096)
+    a = ctypes.addressof(buf)
+    a16 = (a + 15) // 16 * 16
+    assert lib.moe_capacity_pad(a, a, a, 16, 300, 2, 8, a, a, None) == 2        # E > 256
+    assert lib.moe_capacity_pad(a, a, a, 16, 8, 2, -1, a, a, None) == 2         # capacity < 0
+    assert lib.moe_capacity_pad(a, a, a, 16, 256, 2, 1 << 24, a, a, None) == 2  # E*C >= 2^31
+    assert lib.moe_capacity_pad(a, a, a, 16, 8, 2, 8, a, None, None) == 1       # offsets_pad
+    assert lib.moe_capacity_pad(None, a, a, 16, 8, 2, 8, a, a, None) == 1       # topk_idx
+    assert lib.moe_capacity_zero_rows(a16, 2, a, 8, 8, 64, None) == 3           # MXFP8 buffer
+    assert lib.moe_capacity_zero_rows(a16, 1, a, 8, 8, 33, None) == 2           # cols % 32
+    assert lib.moe_capacity_zero_rows(a16, 1, a, 0, 8, 64, None) == 2           # E < 1
+    assert lib.moe_capacity_zero_rows(None, 1, a, 8, 8, 64, None) == 1
+    assert lib.moe_capacity_zero_rows(a16 + 4, 1, a, 8, 8, 64, None) == 4       # alignment
+    assert lib.moe_capacity_zero_rows(None, 1, None, 8, 0, 64, None) == 0       # nothing to do
