@@ -98,9 +98,10 @@ MOE_DEV float silu_f(float a) { return a / (1.f + __expf(-a)); }
 // rows are shared by the concurrent panels. (With the n-tile fastest, the
 // concurrent tiles would touch every panel of the expert and stream the whole
 // weight matrix, larger than the L2, once per pair of m-tiles.)
-// WGRAD gives whole experts to XCDs and orders an expert's output tiles in
-// groups of kWgGroupM m-tiles, m-tile fastest within a group, so the
-// concurrent tiles form a block that shares both operand panels.
+// WGRAD gives whole experts to XCDs (hot experts are split over all XCDs, see
+// build_wgrad_schedule) and orders an expert's output tiles in groups of
+// kWgGroupM m-tiles, m-tile fastest within a group, so the concurrent tiles
+// form a block that shares both operand panels.
 // Correctness does not depend on the XCD mapping: every tile id is owned by
 // exactly one workgroup.
 
@@ -187,6 +188,56 @@ MOE_DEV void decode_row_tile(const RowSchedule &rs, const int32_t *s_tile, const
     const int cm = min(rs.chm, s_tile[e + 1] - s_tile[e] - ci * rs.chm);
     mt_e = ci * rs.chm + o % cm;
     nt = o / cm;
+}
+
+// WGRAD schedule. Every expert has the same number of output tiles (per_e);
+// its cost grows with its row count. An expert with more than twice the mean
+// rows is split into 8 equal tile chunks, chunk x on XCD x, at the head of
+// every XCD's list (the longest work starts first); the other experts stay
+// whole and are dealt round-robin over the XCDs in index order, so their
+// operands are read by a single XCD. Without the split, one very hot expert
+// (skewed routing) would keep a single XCD busy long after the others.
+// s_scan: 257 ints of scratch; s_list: split experts at [0, 128), this XCD's
+// whole experts at [128, 160). (At most E/2 experts can exceed twice the mean.)
+struct WgSchedule {
+    int n_split, n_light, cs, total;
+};
+
+MOE_DEV WgSchedule build_wgrad_schedule(const int32_t *s_off, int E, int per_e, int xcd,
+                                        int32_t *s_scan, int32_t *s_list) {
+    const int tid = threadIdx.x;
+    const int R = s_off[E];
+    const int thresh = 2 * ((R + E - 1) / E);
+    const bool can_split = per_e % 8 == 0;
+    int fl = 0;
+    if (tid < E && can_split) fl = (s_off[tid + 1] - s_off[tid] > thresh) ? 1 : 0;
+    if (tid < 256) s_scan[tid + 1] = fl;
+    if (tid == 0) s_scan[0] = 0;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        int32_t v = (tid < 256 && tid >= o) ? s_scan[tid + 1 - o] : 0;
+        __syncthreads();
+        if (tid < 256) s_scan[tid + 1] += v;
+        __syncthreads();
+    }
+    const int n_split = s_scan[E];
+    if (tid < E) {
+        const int before = s_scan[tid];
+        if (fl) {
+            s_list[before] = tid;
+        } else {
+            const int lr = tid - before;         // rank among the whole experts
+            if ((lr & 7) == xcd) s_list[128 + (lr >> 3)] = tid;
+        }
+    }
+    __syncthreads();
+    WgSchedule w;
+    w.n_split = n_split;
+    const int n_whole = E - n_split;
+    w.n_light = n_whole > xcd ? (n_whole - xcd + 7) / 8 : 0;
+    w.cs = per_e / 8;
+    w.total = n_split * w.cs + w.n_light * per_e;
+    return w;
 }
 
 // ---------------------------------------------------------------------------
@@ -407,9 +458,10 @@ void gg_mfma(GemmArgs g) {
     const int xcd = blockIdx.x & 7, worker = blockIdx.x >> 3, workers = gridDim.x >> 3;
     int n_tiles, total;
     RowSchedule rs;
+    WgSchedule ws;
     if constexpr (MODE == MOE_GG_WGRAD) {
-        // whole experts per XCD: expert e on XCD e % 8, its tiles n-fastest.
-        // FP8: s_tile[e] = sum_{e'<e} ceil(c_e'/128), the 128-row step base of
+        // experts to XCDs by build_wgrad_schedule (hot experts split over all
+        // XCDs, the others whole). FP8: s_tile[e] = sum_{e'<e} ceil(c_e'/128), the 128-row step base of
         // each expert in the column-block MXFP8 layout.
         if constexpr (FP8) build_tile_table(g.offsets, E, 128, s_off, s_tile);
         else {
@@ -418,7 +470,8 @@ void gg_mfma(GemmArgs g) {
         }
         n_tiles = (g.N + BN - 1) / BN;
         const int per_e = ((g.M + BM - 1) / BM) * n_tiles;
-        total = (E > xcd ? (E - xcd + 7) / 8 : 0) * per_e;
+        ws = build_wgrad_schedule(s_off, E, per_e, xcd, s_chunk, s_xpre);
+        total = ws.total;
     } else {
         build_tile_table(g.offsets, E, BM, s_off, s_tile);
         n_tiles = (EPI == MOE_EPI_SWIGLU_FWD) ? (g.h + BN / 2 - 1) / (BN / 2)
@@ -439,8 +492,15 @@ void gg_mfma(GemmArgs g) {
         if constexpr (MODE == MOE_GG_WGRAD) {
             const int mtiles = (g.M + BM - 1) / BM;
             const int per_e = mtiles * n_tiles;
-            e = xcd + 8 * (pos / per_e);
-            const int t = pos % per_e;
+            int t;
+            if (pos < ws.n_split * ws.cs) {        // this XCD's chunk of a split expert
+                e = s_xpre[pos / ws.cs];
+                t = xcd * ws.cs + pos % ws.cs;
+            } else {                               // a whole expert of this XCD
+                const int p2 = pos - ws.n_split * ws.cs;
+                e = s_xpre[128 + p2 / per_e];
+                t = p2 % per_e;
+            }
             // groups of kWgGroupM m-tiles, m-tile fastest within a group: the
             // XCD's concurrent tiles form a block of m-tiles x n-tiles, so both
             // operand panels are shared from L2 by several tiles
