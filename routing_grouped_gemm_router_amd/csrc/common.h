@@ -23,10 +23,10 @@ MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 
 
 // fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
 MOE_DEV uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;   // nearest, ties to even
+    const uint32_t q = (u >> 16) | 0x40u;                          // NaN stays a quiet NaN
+    return (uint16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? q : r);  // a select, no branch
 }
 
 MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
