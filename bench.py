@@ -157,6 +157,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    # HBM bytes per launch of this kernel from the committed counter summary,
+    # only while the kernel's sources are the ones it was measured on
+    from routing_grouped_gemm_router_amd import rocprof_summary as rps
+    tr = rps.read_traffic(os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                       f"gemm1_swiglu_{w.name}_pmc.md"))
+    traffic = tr[0] if tr is not None and tr[1] == rps.gemm_source_hash() else None
+
     res = {
         "metric": METRIC,
         "value": T * a.steps / elapsed,
@@ -187,7 +194,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": g1_tflops / peak,
-            "traffic": None,
+            "traffic": traffic,
             "avg_launch_ms": g1_ms,
             "flops_per_launch": g1_flops,
         },
