@@ -15,6 +15,7 @@
 namespace moe {
 
 constexpr int kRowWaves = 4;
+constexpr int kUnroll = 4;   // combine kernels: 16-byte column chunks per lane in flight together
 
 // ---------------------------------------------------------------------------
 // dispatch: x_perm[token_pos[t, j]] = x[t]
@@ -110,23 +111,34 @@ __global__ __launch_bounds__(256) void combine_rows(const uint4 *__restrict__ y,
         pos[j] = j < k ? token_pos[t * k + j] : -1;
         g[j] = (j < k && !UNIT) ? gate[t * k + j] : 1.f;
     }
-    for (int c = lane; c < n16; c += 64) {
-        uint4 v[KMAX];
+    // kUnroll column chunks per lane at a time: all their row loads are in
+    // flight before the first sum
+    for (int c0 = lane; c0 < n16; c0 += 64 * kUnroll) {
+        uint4 v[kUnroll][KMAX];
 #pragma unroll
-        for (int j = 0; j < KMAX; j++)
-            if (pos[j] >= 0) v[j] = y[(int64_t)pos[j] * n16 + c];
-        float acc[EPV];
+        for (int u = 0; u < kUnroll; u++) {
+            const int c = c0 + 64 * u;
 #pragma unroll
-        for (int i = 0; i < EPV; i++) acc[i] = 0.f;
-#pragma unroll
-        for (int j = 0; j < KMAX; j++) {
-            if (pos[j] < 0) continue;
-            float f[EPV];
-            load_f32<BF16>(v[j], f);
-#pragma unroll
-            for (int i = 0; i < EPV; i++) acc[i] = UNIT ? acc[i] + f[i] : fmaf(g[j], f[i], acc[i]);
+            for (int j = 0; j < KMAX; j++)
+                if (c < n16 && pos[j] >= 0) v[u][j] = y[(int64_t)pos[j] * n16 + c];
         }
-        out[t * n16 + c] = store_f32<BF16>(acc);
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            const int c = c0 + 64 * u;
+            if (c >= n16) break;
+            float acc[EPV];
+#pragma unroll
+            for (int i = 0; i < EPV; i++) acc[i] = 0.f;
+#pragma unroll
+            for (int j = 0; j < KMAX; j++) {
+                if (pos[j] < 0) continue;
+                float f[EPV];
+                load_f32<BF16>(v[u][j], f);
+#pragma unroll
+                for (int i = 0; i < EPV; i++) acc[i] = UNIT ? acc[i] + f[i] : fmaf(g[j], f[i], acc[i]);
+            }
+            out[t * n16 + c] = store_f32<BF16>(acc);
+        }
     }
 }
 
@@ -154,24 +166,34 @@ __global__ __launch_bounds__(256) void combine_bwd_rows(
         g[j] = j < k ? gate[t * k + j] : 0.f;
         dot[j] = 0.f;
     }
-    for (int c = lane; c < n16; c += 64) {
-        float fo[EPV];
-        load_f32<BF16>(dout[t * n16 + c], fo);
-        uint4 v[KMAX];
+    for (int c0 = lane; c0 < n16; c0 += 64 * kUnroll) {
+        uint4 vo[kUnroll], v[kUnroll][KMAX];
 #pragma unroll
-        for (int j = 0; j < KMAX; j++)
-            if (pos[j] >= 0) v[j] = y[(int64_t)pos[j] * n16 + c];
+        for (int u = 0; u < kUnroll; u++) {
+            const int c = c0 + 64 * u;
+            if (c < n16) vo[u] = dout[t * n16 + c];
 #pragma unroll
-        for (int j = 0; j < KMAX; j++) {
-            if (pos[j] < 0) continue;
-            float fy[EPV], fd[EPV];
-            load_f32<BF16>(v[j], fy);
+            for (int j = 0; j < KMAX; j++)
+                if (c < n16 && pos[j] >= 0) v[u][j] = y[(int64_t)pos[j] * n16 + c];
+        }
 #pragma unroll
-            for (int i = 0; i < EPV; i++) {
-                dot[j] = fmaf(fo[i], fy[i], dot[j]);
-                fd[i] = g[j] * fo[i];
+        for (int u = 0; u < kUnroll; u++) {
+            const int c = c0 + 64 * u;
+            if (c >= n16) break;
+            float fo[EPV];
+            load_f32<BF16>(vo[u], fo);
+#pragma unroll
+            for (int j = 0; j < KMAX; j++) {
+                if (pos[j] < 0) continue;
+                float fy[EPV], fd[EPV];
+                load_f32<BF16>(v[u][j], fy);
+#pragma unroll
+                for (int i = 0; i < EPV; i++) {
+                    dot[j] = fmaf(fo[i], fy[i], dot[j]);
+                    fd[i] = g[j] * fo[i];
+                }
+                dy[(int64_t)pos[j] * n16 + c] = store_f32<BF16>(fd);
             }
-            dy[(int64_t)pos[j] * n16 + c] = store_f32<BF16>(fd);
         }
     }
     float s = 0.f;
