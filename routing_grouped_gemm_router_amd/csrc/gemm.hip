@@ -105,7 +105,8 @@ MOE_DEV float silu_f(float a) { return a / (1.f + __expf(-a)); }
 // Correctness does not depend on the XCD mapping: every tile id is owned by
 // exactly one workgroup.
 
-constexpr int kMaxChunks = 2048;
+constexpr int kMaxChunks = 1920;      // chunk list: kMaxChunks/8 entries per XCD (+1)
+constexpr int kXcdChunks = kMaxChunks / 8;
 #ifndef MOE_CHUNK_M
 #define MOE_CHUNK_M 16
 #endif
@@ -151,13 +152,14 @@ MOE_DEV RowSchedule build_row_schedule(const int32_t *s_tile, int E, int n_tiles
         const int mt_e = s_tile[e + 1] - s_tile[e];
         t = min(chm, mt_e - ci * chm) * n_tiles;
     }
-    if (tid < 256) s_xpre[tid + 1] = t;
+    // (C <= kMaxChunks by the choice of chm, so cx <= kXcdChunks)
+    if (tid < kXcdChunks) s_xpre[tid + 1] = t;
     if (tid == 0) s_xpre[0] = 0;
     __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-        int32_t v = (tid < 256 && tid >= o) ? s_xpre[tid + 1 - o] : 0;
+    for (int o = 1; o < kXcdChunks; o <<= 1) {
+        int32_t v = (tid < kXcdChunks && tid >= o) ? s_xpre[tid + 1 - o] : 0;
         __syncthreads();
-        if (tid < 256) s_xpre[tid + 1] += v;
+        if (tid < kXcdChunks) s_xpre[tid + 1] += v;
         __syncthreads();
     }
     RowSchedule r;
@@ -172,7 +174,7 @@ MOE_DEV RowSchedule build_row_schedule(const int32_t *s_tile, int E, int n_tiles
 MOE_DEV void decode_row_tile(const RowSchedule &rs, const int32_t *s_tile, const int32_t *s_chunk,
                              const int32_t *s_xpre, int E, int xcd, int p, int &e, int &mt_e,
                              int &nt) {
-    int lo = 0, hi = kMaxChunks / 8;      // largest lc with s_xpre[lc] <= p
+    int lo = 0, hi = kXcdChunks;          // largest lc with s_xpre[lc] <= p
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
         if (s_xpre[mid] <= p) lo = mid; else hi = mid - 1;
@@ -441,14 +443,23 @@ void gg_mfma(GemmArgs g) {
     constexpr bool B_KL = FP8 || MODE == MOE_GG_FWD;
     using AT = DmaTile<BM, A_KL, NW>;
     using BT = DmaTile<BN, B_KL, NW>;
-    constexpr int IPS = AT::IPW + BT::IPW + SPW;  // copy instructions / wave / stage
+    constexpr int IPS_MAIN = AT::IPW + BT::IPW;   // operand copy instructions / wave / stage
+    constexpr int IPS = IPS_MAIN + SPW;           // with one scale word per step
 
     // LDS pool: STAGES x (A tile | B tile | scale words) during the K loop;
     // reused after it to stage the output tile for coalesced stores (the
     // copies into LDS are issued through inline asm, so the compiler tracks no
     // LDS writes of its own here and a single array serves every stage)
-    constexpr int SCALE_U4 = SPW * NW * 64 * 4 / 16;
-    constexpr int STAGE_U4 = (BM + BN) * 8 + SCALE_U4;
+    // FP8 scale words, after the stages: either per step (SPW 4-byte copies
+    // per lane into a per-stage area) or, when every row's scales come in
+    // whole 16-byte groups (K % 512 == 0), 16 bytes per row covering 4 steps,
+    // copied every 4th step into one slot of a 2-slot ring. A 4-byte copy
+    // touches 64 cache lines for 256 bytes, so the ring cuts the L1 work of
+    // the scales 4x.
+    constexpr int SCALE_U4 = SPW * NW * 64 * 4 / 16;              // per-stage area
+    constexpr int SROWS = FP8 ? ((BM + BN + 63) / 64) * 64 : 0;   // ring rows per slot
+    constexpr int SREG_U4 = FP8 ? (2 * SROWS > STAGES * SCALE_U4 ? 2 * SROWS : STAGES * SCALE_U4) : 0;
+    constexpr int STAGE_U4 = (BM + BN) * 8;
     constexpr bool F32_STAGE = MODE == MOE_GG_WGRAD || EPI == MOE_EPI_SWIGLU_BWD;
     constexpr int PF = BN * 4 + 32;      // fp32 staging pitch (bytes)
     constexpr int PB = BN * 2 + 16;      // bf16 staging pitch (bytes)
@@ -463,13 +474,14 @@ void gg_mfma(GemmArgs g) {
     constexpr int EP_PASSES = BM / EP_ROWS;
     static_assert(EP_ROWS % 32 == 0 && EP_ROWS * EP_ROW_BYTES <= POOL_BUDGET, "epilogue staging");
     constexpr int EPI_BYTES = EP_ROWS * EP_ROW_BYTES;
-    constexpr int POOL_U4 = STAGES * STAGE_U4 > (EPI_BYTES + 15) / 16 ? STAGES * STAGE_U4
-                                                                       : (EPI_BYTES + 15) / 16;
+    constexpr int POOL_U4 = STAGES * STAGE_U4 + SREG_U4 > (EPI_BYTES + 15) / 16
+                                ? STAGES * STAGE_U4 + SREG_U4
+                                : (EPI_BYTES + 15) / 16;
     __shared__ __attribute__((aligned(1024))) uint4 lds_pool[POOL_U4];
     __shared__ int32_t s_off[257];
     __shared__ int32_t s_tile[257];
     __shared__ int32_t s_chunk[257];
-    __shared__ int32_t s_xpre[kMaxChunks / 8 + 1];
+    __shared__ int32_t s_xpre[kXcdChunks + 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -505,6 +517,10 @@ void gg_mfma(GemmArgs g) {
     const char *B = reinterpret_cast<const char *>(g.B);
     const uint8_t *AS = g.a_scale;
     const uint8_t *BS = g.b_scale;
+
+    // FP8 FWD/DGRAD with whole 16-byte scale groups per row: batched scales
+    const bool sbatch = FP8 && MODE != MOE_GG_WGRAD && (g.K / 32) % 16 == 0;
+    (void)sbatch;
 
     // coordinates of one output tile
     struct TileC {
@@ -640,15 +656,33 @@ void gg_mfma(GemmArgs g) {
     };
     // enqueue the copies of K step kt of the tile set up last (klim: its K extent)
     auto issue = [&](auto I, int kt, int klim) {
+        constexpr int si = decltype(I)::value;
         uint4 *st = stage(I);
+        if constexpr (FP8) {
+            // batched scales first: a later wait for this stage's operands then
+            // also covers them (copies complete in issue order)
+            if (sbatch && (kt & 3) == 0) {
+                uint4 *ring = lds_pool + STAGES * STAGE_U4 + ((kt >> 2) & 1) * SROWS;
+#pragma unroll
+                for (int q = 0; q < SPW; q++) {
+                    if ((q * NW + wave) * 64 >= BM + BN) continue;   // wave-uniform
+                    const void *s = ssrc[q] ? (const void *)(ssrc[q] + (kt >> 2) * 16)
+                                            : (const void *)&g_zero_chunk[threadIdx.x & 63];
+                    dma16(s, ring + (q * NW + wave) * 64);
+                }
+            }
+        }
         ta.issue(st, kt, klim, wave);
         tb.issue(st + BM * 8, kt, klim, wave);
         if constexpr (FP8) {
+            if (!sbatch) {
+                uint4 *sarea = lds_pool + STAGES * STAGE_U4 + si * SCALE_U4;
 #pragma unroll
-            for (int q = 0; q < SPW; q++) {
-                const void *s = ssrc[q] ? (const void *)(ssrc[q] + kt * 4)
-                                        : (const void *)&g_zero_chunk[threadIdx.x & 63];
-                dma4(s, st + (BM + BN) * 8 + (q * NW + wave) * 16);
+                for (int q = 0; q < SPW; q++) {
+                    const void *s = ssrc[q] ? (const void *)(ssrc[q] + kt * 4)
+                                            : (const void *)&g_zero_chunk[threadIdx.x & 63];
+                    dma4(s, sarea + (q * NW + wave) * 16);
+                }
             }
         }
     };
@@ -689,19 +723,35 @@ void gg_mfma(GemmArgs g) {
             constexpr int cur = decltype(CUR)::value;
             constexpr int nb = (cur + STAGES - 1) % STAGES;
             // copies of later stages may stay in flight; step kt's must be done
-            if (kt + STAGES - 2 < nk) wait_vmem<(STAGES - 2) * IPS>();
-            else wait_vmem<0>();
+            // (batched scales: per-stage counts vary; IPS_MAIN only over-waits)
+            if (kt + STAGES - 2 < nk) {
+                if (sbatch) wait_vmem<(STAGES - 2) * IPS_MAIN>();
+                else wait_vmem<(STAGES - 2) * IPS>();
+            } else {
+                wait_vmem<0>();
+            }
             lds_sync();
             if (kt + STAGES - 1 < nk) issue(std::integral_constant<int, nb>(), kt + STAGES - 1, klim);
             const uint4 *sa = stage(CUR);
             const uint4 *sb = sa + BM * 8;
             if constexpr (FP8) {
-                const uint32_t *sw = reinterpret_cast<const uint32_t *>(sb + BN * 8);
                 uint32_t swa[TM], swb[TN];
+                if (sbatch) {
+                    const uint32_t *rw = reinterpret_cast<const uint32_t *>(
+                        lds_pool + STAGES * STAGE_U4 + ((kt >> 2) & 1) * SROWS);
+                    const int w = kt & 3;
 #pragma unroll
-                for (int i = 0; i < TM; i++) swa[i] = sw[wm * WTM + i * 32 + (lane & 31)];
+                    for (int i = 0; i < TM; i++) swa[i] = rw[(wm * WTM + i * 32 + (lane & 31)) * 4 + w];
 #pragma unroll
-                for (int j = 0; j < TN; j++) swb[j] = sw[BM + wn * WTN + j * 32 + (lane & 31)];
+                    for (int j = 0; j < TN; j++) swb[j] = rw[(BM + wn * WTN + j * 32 + (lane & 31)) * 4 + w];
+                } else {
+                    const uint32_t *sw = reinterpret_cast<const uint32_t *>(
+                        lds_pool + STAGES * STAGE_U4 + cur * SCALE_U4);
+#pragma unroll
+                    for (int i = 0; i < TM; i++) swa[i] = sw[wm * WTM + i * 32 + (lane & 31)];
+#pragma unroll
+                    for (int j = 0; j < TN; j++) swb[j] = sw[BM + wn * WTN + j * 32 + (lane & 31)];
+                }
                 // operand fragments double-buffered in registers: the LDS reads
                 // of K slice sl+1 are issued before the MFMAs of slice sl
                 i32x8 fa[2][TM], fb[2][TN];
