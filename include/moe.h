@@ -168,7 +168,9 @@ enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU_FWD = 1, MOE_EPI_SWIGLU_BWD = 2 };
  *     C (and AB / H' / dAB of the epilogues) is bf16;
  *   WGRAD: A and B in the column-block layout of mxfp8_quantize (axis 0,
  *     groups = offsets): A holds the [rows, M] operand, B the [rows, N]
- *     operand; C [E, M, N] fp32.
+ *     operand; C [E, M, N] fp32. Their scale arrays must be sized by
+ *     mxfp8_col_blocks (the kernel may read up to 12 bytes past the last
+ *     used scale byte, into the spare blocks).
  * (aux_out_scale is reserved and must be null.)
  */
 typedef struct moe_gemm_desc {

@@ -518,8 +518,12 @@ void gg_mfma(GemmArgs g) {
     const uint8_t *AS = g.a_scale;
     const uint8_t *BS = g.b_scale;
 
-    // FP8 FWD/DGRAD with whole 16-byte scale groups per row: batched scales
-    const bool sbatch = FP8 && MODE != MOE_GG_WGRAD && (g.K / 32) % 16 == 0;
+    // FP8 with batched scales: FWD/DGRAD when every row's scales come in whole
+    // 16-byte groups; WGRAD always -- the column-block scale array is sized by
+    // mxfp8_col_blocks, whose spare blocks keep a 16-byte read past the end of
+    // a column's last (partial) group in bounds, and those bytes belong to
+    // steps that do not exist
+    const bool sbatch = FP8 && (MODE == MOE_GG_WGRAD || (g.K / 32) % 16 == 0);
     (void)sbatch;
 
     // coordinates of one output tile
