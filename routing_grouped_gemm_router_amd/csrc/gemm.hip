@@ -316,14 +316,18 @@ MOE_DEV void lds_sync() {
 // (wait_vmem + lds_sync); the instructions have no result registers, and the
 // "memory" clobber keeps LDS reads from moving across them.
 MOE_DEV void dma16(const void *src, const void *lds_wave_base) {
-    const uint32_t m0v = (uint32_t)(uintptr_t)(const MOE_LDS void *)lds_wave_base;
+    // wave-uniform by construction; readfirstlane keeps it in an SGPR for M0
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const MOE_LDS void *)lds_wave_base);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(src), "s"(m0v)
                  : "memory", "m0");
 }
 MOE_DEV void dma4(const void *src, const void *lds_wave_base) {
-    const uint32_t m0v = (uint32_t)(uintptr_t)(const MOE_LDS void *)lds_wave_base;
+    // wave-uniform by construction; readfirstlane keeps it in an SGPR for M0
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const MOE_LDS void *)lds_wave_base);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                  :
                  : "v"(src), "s"(m0v)
