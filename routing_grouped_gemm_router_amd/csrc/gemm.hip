@@ -769,6 +769,23 @@ void gg_mfma(GemmArgs g) {
                 for (int j = 0; j < TN; j++) fb[0][j] = BT::frag8(sb, wn * WTN + j * 32, 0, lane);
 #pragma unroll
                 for (int sl = 0; sl < 2; sl++) {
+                    if (MODE != MOE_GG_WGRAD && sl == 0) {
+                        // row GEMMs: the reads of slice 1 go one between each
+                        // two MFMAs of slice 0, as in the bf16 path
+                        const int sh = 8 * (lane >> 5);
+#pragma unroll
+                        for (int t = 0; t < TM * TN; t++) {
+                            if (t < TM) fa[1][t] = AT::frag8(sa, wm * WTM + t * 32, 1, lane);
+                            else if (t < TM + TN) fb[1][t - TM] = BT::frag8(sb, wn * WTN + (t - TM) * 32, 1, lane);
+                            __builtin_amdgcn_sched_barrier(0);
+                            const int i = t / TN, j = t % TN;
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                fa[0][i], fb[0][j], acc[i][j], 0, 0, 0,
+                                (int)((swa[i] >> sh) & 0xff), 0, (int)((swb[j] >> sh) & 0xff));
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        continue;
+                    }
                     if (sl + 1 < 2) {
 #pragma unroll
                         for (int i = 0; i < TM; i++) fa[1][i] = AT::frag8(sa, wm * WTM + i * 32, 1, lane);
@@ -789,7 +806,7 @@ void gg_mfma(GemmArgs g) {
                 }
             } else {
                 // operand fragments double-buffered in registers: the LDS reads
-                // of K slice kk+1 are issued before the MFMAs of slice kk
+                // of K slice kk+1 are issued while the MFMAs of slice kk run
                 bf16x8 fa[2][TM], fb[2][TN];
 #pragma unroll
                 for (int i = 0; i < TM; i++) fa[0][i] = AT::frag(sa, wm * WTM + i * 32, 0, lane);
@@ -798,19 +815,39 @@ void gg_mfma(GemmArgs g) {
 #pragma unroll
                 for (int kk = 0; kk < 4; kk++) {
                     const int cb = kk & 1, nb2 = cb ^ 1;
-                    if (kk + 1 < 4) {
+                    if constexpr (MODE != MOE_GG_WGRAD) {
+                        // one fragment read between consecutive MFMAs: the LDS
+                        // requests of the CU arrive spread over the slice
+                        // (measured 2-4% faster on the row GEMMs; the weight
+                        // gradients run 2-6% slower this way)
+                        static_assert(TM + TN <= TM * TN, "one read per MFMA slot");
 #pragma unroll
-                        for (int i = 0; i < TM; i++) fa[nb2][i] = AT::frag(sa, wm * WTM + i * 32, kk + 1, lane);
+                        for (int t = 0; t < TM * TN; t++) {
+                            if (kk + 1 < 4) {
+                                if (t < TM) fa[nb2][t] = AT::frag(sa, wm * WTM + t * 32, kk + 1, lane);
+                                else if (t < TM + TN)
+                                    fb[nb2][t - TM] = BT::frag(sb, wn * WTN + (t - TM) * 32, kk + 1, lane);
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                            acc[t / TN][t % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                fa[cb][t / TN], fb[cb][t % TN], acc[t / TN][t % TN], 0, 0, 0);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    } else {
+                        if (kk + 1 < 4) {
 #pragma unroll
-                        for (int j = 0; j < TN; j++) fb[nb2][j] = BT::frag(sb, wn * WTN + j * 32, kk + 1, lane);
+                            for (int i = 0; i < TM; i++) fa[nb2][i] = AT::frag(sa, wm * WTM + i * 32, kk + 1, lane);
+#pragma unroll
+                            for (int j = 0; j < TN; j++) fb[nb2][j] = BT::frag(sb, wn * WTN + j * 32, kk + 1, lane);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);   // keep the prefetch above the MFMAs
+#pragma unroll
+                        for (int i = 0; i < TM; i++)
+#pragma unroll
+                            for (int j = 0; j < TN; j++)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch above the MFMAs
-#pragma unroll
-                    for (int i = 0; i < TM; i++)
-#pragma unroll
-                        for (int j = 0; j < TN; j++)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
