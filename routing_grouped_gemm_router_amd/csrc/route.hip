@@ -6,13 +6,17 @@
 // problem"; bytechap.com, "How it works").
 //
 // Three kernels, no host round trip and no order-dependent atomics:
-//  1. route_select: one wave per 64-token chunk. The chunk's [64, E] logits
-//     are read with coalesced 16-byte loads into LDS; each lane then selects
-//     its token's top k (descending fp32 logit, equal logits -> lower index),
-//     computes the gates (softmax over the k selected logits), and the wave
-//     ranks every (token, expert) pair inside the chunk with one ballot per
-//     expert: rank = popcount(ballot & lanes-below). Per-chunk expert counts
-//     go to the workspace.
+//  1. route_select: one workgroup per 64-token chunk, G = 8 lanes per token.
+//     Each lane reads every G-th 16-byte piece of its token's logits (all
+//     loads in flight at once) and keeps their top k (descending fp32 logit,
+//     equal logits -> lower index): each piece is sorted by a four-input
+//     sorting network and bitonic-merged into the lane's list, and the G
+//     lists of a token are bitonic-merged across lanes with DPP moves. Lane j
+//     of the token owns selection j; the gates are the softmax over the k
+//     selected logits. Each wave ranks its (token, slot) pairs inside the
+//     chunk (rank = number of lanes below with the same expert, found with
+//     one ballot per bit of the expert index); the waves' counts are
+//     combined in LDS. Per-chunk expert counts go to the workspace.
 //  2. route_scan: one workgroup per expert scans its counts over chunks
 //     (exclusive), giving each chunk its base inside the expert's group, and
 //     the expert's total.
@@ -23,108 +27,201 @@
 
 namespace moe {
 
-constexpr int kChunk = 64;      // tokens per chunk = one wave
+constexpr int kChunk = 64;      // tokens per chunk
 constexpr int kMaxE = 256;
 
-template <int KMAX>
-__global__ __launch_bounds__(64) void route_select(const float *__restrict__ logits, int64_t T,
-                                                   int E, int k, int32_t *__restrict__ topk_idx,
-                                                   float *__restrict__ topk_gate,
-                                                   int32_t *__restrict__ rank_out,
-                                                   int32_t *__restrict__ chunk_counts) {
-    __shared__ float tile[kChunk * (kMaxE + 1)];
-    __shared__ int32_t cnt[kMaxE];
-    const int lane = threadIdx.x;
+// A candidate is (logit v, expert i); i < 0 marks an empty slot.
+// (v, i) ranks above (bv, bi): it is not empty and (bv, bi) is, or its logit
+// is larger, or the logits are equal (IEEE comparison, so -0 and +0 are
+// equal) and its index is lower. Bitwise, not short-circuit, so that it
+// compiles to selects.
+MOE_DEV bool route_better(float v, int i, float bv, int bi) {
+    return (i >= 0) & ((bi < 0) | (v > bv) | ((v == bv) & (i < bi)));
+}
+
+// compare-exchange: afterwards (v[a], i[a]) ranks at or above (v[b], i[b])
+template <int N>
+MOE_DEV void route_cx(float (&v)[N], int (&i)[N], int a, int b) {
+    const bool sw = route_better(v[b], i[b], v[a], i[a]);
+    const float va = v[a], vb = v[b];
+    const int ia = i[a], ib = i[b];
+    v[a] = sw ? vb : va; i[a] = sw ? ib : ia;
+    v[b] = sw ? va : vb; i[b] = sw ? ia : ib;
+}
+
+// (bv, bi) <- the best KP of the sorted lists (bv, bi) and (ov, oi), sorted.
+// Pairing slot j of one list with slot KP-1-j of the other and keeping the
+// better of each pair leaves exactly the best KP, as a bitonic sequence,
+// which log2(KP) rounds of compare-exchanges sort (Batcher's bitonic merge).
+template <int KP>
+MOE_DEV void route_merge(float (&bv)[KP], int (&bi)[KP], const float (&ov)[KP], const int (&oi)[KP]) {
+#pragma unroll
+    for (int j = 0; j < KP; j++) {
+        const bool t = route_better(ov[KP - 1 - j], oi[KP - 1 - j], bv[j], bi[j]);
+        bv[j] = t ? ov[KP - 1 - j] : bv[j];
+        bi[j] = t ? oi[KP - 1 - j] : bi[j];
+    }
+#pragma unroll
+    for (int st = KP / 2; st > 0; st >>= 1)
+#pragma unroll
+        for (int j = 0; j < KP; j++)
+            if ((j & st) == 0) route_cx<KP>(bv, bi, j, j + st);
+}
+
+// merge four candidates (experts e0 .. e0+3) into the sorted list
+template <int KP>
+MOE_DEV void route_take4(float (&bv)[KP], int (&bi)[KP], float4 x, int e0) {
+    float v[4] = {x.x, x.y, x.z, x.w};
+    int i[4] = {e0, e0 + 1, e0 + 2, e0 + 3};
+    // sorting network on four (Knuth's five comparators)
+    route_cx<4>(v, i, 0, 1); route_cx<4>(v, i, 2, 3);
+    route_cx<4>(v, i, 0, 2); route_cx<4>(v, i, 1, 3);
+    route_cx<4>(v, i, 1, 2);
+    float ov[KP];
+    int oi[KP];
+#pragma unroll
+    for (int j = 0; j < KP; j++) {
+        ov[j] = j < 4 ? v[j < 4 ? j : 0] : -INFINITY;
+        oi[j] = j < 4 ? i[j < 4 ? j : 0] : -1;
+    }
+    route_merge<KP>(bv, bi, ov, oi);
+}
+
+// merge one candidate into the sorted list
+template <int KP>
+MOE_DEV void route_take1(float (&bv)[KP], int (&bi)[KP], float x, int e) {
+    float ov[KP];
+    int oi[KP];
+#pragma unroll
+    for (int j = 0; j < KP; j++) { ov[j] = j ? -INFINITY : x; oi[j] = j ? -1 : e; }
+    route_merge<KP>(bv, bi, ov, oi);
+}
+
+// lane moves inside a row of lanes (DPP, no LDS): xor 1 and xor 2 within
+// quads, then the half-row mirror. Applied in this order, each pairs every
+// lane with one holding the other half of the lists merged so far, so after
+// the three rounds all 8 lanes of an aligned group hold the merge of all 8.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+template <int CTRL>
+MOE_DEV int dpp_move(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+template <int KP, int CTRL>
+MOE_DEV void route_merge_lanes(float (&bv)[KP], int (&bi)[KP]) {
+    float ov[KP];
+    int oi[KP];
+#pragma unroll
+    for (int j = 0; j < KP; j++) {
+        ov[j] = __int_as_float(dpp_move<CTRL>(__float_as_int(bv[j])));
+        oi[j] = dpp_move<CTRL>(bi[j]);
+    }
+    route_merge<KP>(bv, bi, ov, oi);
+}
+
+template <int K>
+__global__ __launch_bounds__(kChunk * 8) void route_select(const float *__restrict__ logits, int64_t T,
+                                                          int E, int k, int32_t *__restrict__ topk_idx,
+                                                          float *__restrict__ topk_gate,
+                                                          int32_t *__restrict__ rank_out,
+                                                          int32_t *__restrict__ chunk_counts) {
+    constexpr int G = 8;                                // lanes per token
+    constexpr int KP = K <= 1 ? 1 : K <= 2 ? 2 : K <= 4 ? 4 : 8;   // list length (power of two)
+    constexpr int NT = kChunk * G, NWAVE = NT / 64;
+    constexpr int NV = kMaxE / 4 / G;                  // 16-byte pieces of a token row per lane (E = 256)
+    __shared__ int32_t cnt[NWAVE][kMaxE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t chunk = blockIdx.x;
     const int64_t t0 = chunk * kChunk;
     const int ntok = (int)min<int64_t>(kChunk, T - t0);
-    const int stride = E + 1;
 
-    // coalesced load of the contiguous [ntok, E] block of logits
-    const float *src = logits + t0 * E;
-    const int total = ntok * E;
-    if ((E & 3) == 0) {
-        const float4 *src4 = reinterpret_cast<const float4 *>(src);
-        for (int i = lane; i < total / 4; i += kChunk) {
-            float4 v = src4[i];
-            int e0 = (i * 4) % E, r = (i * 4) / E;
-            float *dst = tile + r * stride + e0;
-            dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
-        }
-    } else {
-        for (int i = lane; i < total; i += kChunk) tile[(i / E) * stride + (i % E)] = src[i];
-    }
-    __syncthreads();
+    for (int i = tid; i < NWAVE * kMaxE; i += NT) (&cnt[0][0])[i] = 0;
 
-    // per-lane top-k by insertion (kept sorted: value descending, index ascending)
-    float bv[KMAX];
-    int bi[KMAX];
+    // lane `part` of token `tok` holds the logits of experts 4(part + G c) ..
+    // + 3, c = 0, 1, ...: the token's G lanes read its row in 16-byte pieces,
+    // every load in flight before the first comparison
+    const int tok = tid / G, part = tid % G;
+    const bool active = tok < ntok;
+    float bv[KP];
+    int bi[KP];
 #pragma unroll
-    for (int j = 0; j < KMAX; j++) { bv[j] = -INFINITY; bi[j] = -1; }
-    const bool active = lane < ntok;
+    for (int j = 0; j < KP; j++) { bv[j] = -INFINITY; bi[j] = -1; }
     if (active) {
-        const float *row = tile + lane * stride;
-        for (int e = 0; e < E; e++) {
-            float cv = row[e];
-            int ci = e;
-            bool shifting = false;
+        const float *row = logits + (t0 + tok) * E;
+        if ((E & 3) == 0) {
+            float4 v[NV];
 #pragma unroll
-            for (int j = 0; j < KMAX; j++) {
-                if (j < k) {
-                    // a later (higher) index only overtakes a strictly smaller value;
-                    // once inserted, the rest of the list shifts down by one
-                    bool take = shifting || bi[j] < 0 || cv > bv[j];
-                    if (take) {
-                        float tv = bv[j]; int ti = bi[j];
-                        bv[j] = cv; bi[j] = ci;
-                        cv = tv; ci = ti;
-                        shifting = true;
-                    }
-                }
+            for (int c = 0; c < NV; c++) {
+                const int e0 = 4 * (part + G * c);
+                if (e0 < E) v[c] = *reinterpret_cast<const float4 *>(row + e0);
             }
-        }
-        // gates: softmax over the selected logits
-        float m = bv[0], z = 0.f;
-        float ex[KMAX];
 #pragma unroll
-        for (int j = 0; j < KMAX; j++) {
-            ex[j] = (j < k) ? expf(bv[j] - m) : 0.f;
-            z += ex[j];
-        }
-        const int64_t t = t0 + lane;
-#pragma unroll
-        for (int j = 0; j < KMAX; j++) {
-            if (j < k) {
-                topk_idx[t * k + j] = bi[j];
-                topk_gate[t * k + j] = ex[j] / z;
+            for (int c = 0; c < NV; c++) {
+                const int e0 = 4 * (part + G * c);
+                if (e0 < E) route_take4<KP>(bv, bi, v[c], e0);
             }
+        } else {
+            for (int e = part; e < E; e += G) route_take1<KP>(bv, bi, row[e], e);
         }
     }
+    // merge the G = 8 lists of the token (an aligned group of 8 lanes)
+    route_merge_lanes<KP, kDppXor1>(bv, bi);
+    route_merge_lanes<KP, kDppXor2>(bv, bi);
+    route_merge_lanes<KP, kDppHalfMirror>(bv, bi);
 
-    // rank of each (token, expert) inside the chunk: one ballot per expert
+    // this lane's selection: slot `part` of its token; gates = softmax over
+    // the k selected logits
+    const bool owns = active && part < K;
+    int my_e = -1;
+    float my_g = 0.f;
+    {
+        const float m = bv[0];
+        float z = 0.f, mine = 0.f;
+#pragma unroll
+        for (int j = 0; j < K; j++) {
+            const float ex = expf(bv[j] - m);
+            z += ex;
+            if (j == part) { mine = ex; my_e = bi[j]; }
+        }
+        my_g = mine / z;
+    }
+    if (owns) {
+        const int64_t t = t0 + tok;
+        topk_idx[t * k + part] = my_e;
+        topk_gate[t * k + part] = my_g;
+    }
+    __syncthreads();                                   // counts zeroed
+
+    // rank inside the wave: lanes below with the same expert (the lanes of
+    // one token hold distinct experts, so they are exactly earlier tokens).
+    // The lanes with the same expert are found bit by bit of the expert
+    // index: one ballot per bit.
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int rank[KMAX];
-#pragma unroll
-    for (int j = 0; j < KMAX; j++) rank[j] = 0;
-    for (int e = 0; e < E; e++) {
-        bool sel = false;
-#pragma unroll
-        for (int j = 0; j < KMAX; j++) sel |= (j < k) && active && (bi[j] == e);
-        uint64_t m = __ballot(sel);
-        int r = __popcll(m & below);
-#pragma unroll
-        for (int j = 0; j < KMAX; j++)
-            if (j < k && bi[j] == e) rank[j] = r;
-        if (lane == 0) cnt[e] = __popcll(m);
+    const uint64_t own_m = __ballot(owns);
+    uint64_t same = own_m;
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    for (int b = 0; b < nbits; b++) {
+        const bool bit = (my_e >> b) & 1;
+        const uint64_t mb = __ballot(owns && bit);
+        same &= bit ? mb : (own_m & ~mb);
     }
-    if (active) {
-        const int64_t t = t0 + lane;
-#pragma unroll
-        for (int j = 0; j < KMAX; j++)
-            if (j < k) rank_out[t * k + j] = rank[j];
-    }
+    int rank = __popcll(same & below);
+    if (owns && rank == 0) cnt[wave][my_e] = __popcll(same);   // one writer per expert
     __syncthreads();
-    for (int e = lane; e < E; e += kChunk) chunk_counts[chunk * E + e] = cnt[e];
+    if (owns) {
+#pragma unroll
+        for (int w = 0; w < NWAVE; w++)
+            if (w < wave) rank += cnt[w][my_e];
+        rank_out[(t0 + tok) * k + part] = rank;
+    }
+    for (int e = tid; e < E; e += NT) {
+        int32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < NWAVE; w++) c += cnt[w][e];
+        chunk_counts[chunk * E + e] = c;
+    }
 }
 
 // One workgroup per expert: exclusive scan of its per-chunk counts (in place)
@@ -190,10 +287,13 @@ __global__ __launch_bounds__(256) void route_place(
     const int64_t t = (int64_t)blockIdx.x * 256 + tid;
     if (t >= T) return;
     const int64_t chunk = t / kChunk;
+    const int64_t R = T * k;
     for (int j = 0; j < k; j++) {
-        int e = topk_idx[t * k + j];
-        int32_t p = off[e] + chunk_base[chunk * E + e] + token_pos[t * k + j];
+        const int e = topk_idx[t * k + j];
+        if ((unsigned)e >= (unsigned)E) continue;      // never for route_select's output
+        const int32_t p = off[e] + chunk_base[chunk * E + e] + token_pos[t * k + j];
         token_pos[t * k + j] = p;
+        if ((uint64_t)p >= (uint64_t)R) continue;
         sorted_token[p] = (int32_t)t;
         sorted_slot[p] = j;
     }
@@ -206,15 +306,14 @@ moe_status route_launch(const float *logits, int64_t T, int E, int k, int tile_m
     const int64_t nchunks = (T + kChunk - 1) / kChunk;
     int32_t *chunk_counts = reinterpret_cast<int32_t *>(ws);
     if (nchunks > 0) {
-        dim3 g((unsigned)nchunks), b(kChunk);
-        if (k <= 1)
-            route_select<1><<<g, b, 0, s>>>(logits, T, E, k, topk_idx, topk_gate, token_pos, chunk_counts);
-        else if (k <= 2)
-            route_select<2><<<g, b, 0, s>>>(logits, T, E, k, topk_idx, topk_gate, token_pos, chunk_counts);
-        else if (k <= 4)
-            route_select<4><<<g, b, 0, s>>>(logits, T, E, k, topk_idx, topk_gate, token_pos, chunk_counts);
-        else
-            route_select<8><<<g, b, 0, s>>>(logits, T, E, k, topk_idx, topk_gate, token_pos, chunk_counts);
+        dim3 g((unsigned)nchunks);
+        switch (k) {
+#define MOE_RS(K) \
+    case K: route_select<K><<<g, kChunk * 8, 0, s>>>(logits, T, E, k, topk_idx, topk_gate, token_pos, chunk_counts); break;
+            MOE_RS(1) MOE_RS(2) MOE_RS(3) MOE_RS(4) MOE_RS(5) MOE_RS(6) MOE_RS(7) MOE_RS(8)
+#undef MOE_RS
+            default: return MOE_ERR_SHAPE;
+        }
     }
     route_scan<<<E, 256, 0, s>>>(chunk_counts, nchunks, E, counts);
     const int64_t nb = T > 0 ? (T + 255) / 256 : 1;
