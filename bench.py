@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-padded", action="store_true",
                     help="skip the padded-capacity comparison (bf16 fwd+bwd workloads)")
+    ap.add_argument("--no-recompute", action="store_true",
+                    help="skip the recompute variant (GEMM1 rerun in the backward)")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens in the oracle's bounded sample")
     ap.add_argument("--breakdown", action="store_true",
@@ -147,6 +149,12 @@ def main():
     if not mx and w.backward and not a.no_padded:
         padded = padded_baseline(moe, torch, inp, w, a.steps, a.warmup)
         padded["dropless_speedup"] = padded["ms_per_step"] / ms
+    recompute = None
+    if w.backward and not a.no_recompute:
+        recompute = recompute_variant(moe, torch, inp, w, a.steps, a.warmup)
+        recompute["held_bytes_saving_layer"] = layer.held_bytes()
+        recompute["held_frac"] = recompute["held_bytes"] / layer.held_bytes()
+        recompute["throughput_frac"] = ms / recompute["ms_per_step"]
     if a.breakdown and not mx:
         breakdown(moe, torch, layer, x, logits, dout, w)
     if a.copy_calib:
@@ -201,9 +209,35 @@ def main():
     }
     if padded is not None:
         res["padded_baseline"] = padded
+    if recompute is not None:
+        res["recompute"] = recompute
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, w, a.cpu_tokens)
     print(json.dumps(res), flush=True)
+
+
+def recompute_variant(moe, torch, inp, w, steps, warmup):
+    """The layer that holds only y_perm and the routing metadata between its
+    forward and backward and reruns dispatch + GEMM1 in the backward, on the
+    same inputs; timed like the main loop, after it."""
+    mx = w.dtype == "mxfp8"
+    cls = moe.MoELayerMX if mx else moe.MoELayer
+    layer = cls(inp["w1"], inp["w2"], w.k, recompute=True)
+
+    def step():
+        layer.forward(inp["x"], inp["logits"])
+        layer.backward(inp["dout"])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    return {"ms_per_step": el * 1e3 / steps, "tokens_per_s": w.T * steps / el,
+            "held_bytes": layer.held_bytes()}
 
 
 def padded_baseline(moe, torch, inp, w, steps, warmup):

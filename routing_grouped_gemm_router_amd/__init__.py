@@ -318,16 +318,43 @@ def moe_capacity_zero_rows(buf: torch.Tensor, offsets: torch.Tensor, capacity: i
 # the layer
 
 
+# Scratch tensors shared by every recomputing layer of one shape: what a
+# layer rebuilds in its backward lives here instead of being held from its
+# forward to its backward.
+_SCRATCH: dict = {}
+
+
+def _scratch(name: str, shape, dtype, device) -> torch.Tensor:
+    key = (name, tuple(shape), dtype, str(device))
+    t = _SCRATCH.get(key)
+    if t is None:
+        t = _SCRATCH[key] = torch.empty(shape, dtype=dtype, device=device)
+    return t
+
+
+def _nbytes(ts) -> int:
+    return sum(t.numel() * t.element_size() for t in ts if t is not None)
+
+
 class MoELayer:
     """Forward and backward of the MoE expert layer through the C ABI.
 
     Buffers are allocated once per (T) and reused across calls, so a step
-    issues only kernel launches (no allocation, no device->host traffic)."""
+    issues only kernel launches (no allocation, no device->host traffic).
 
-    def __init__(self, w1: torch.Tensor, w2: torch.Tensor, k: int):
+    recompute=True trades compute for activation memory (the trade-off the
+    Olmo-core 3 report measures, kongchang.com "MXFP8 and memory"): the
+    layer keeps only y_perm and the routing metadata from its forward to its
+    backward. x_perm, A||B and H' are written to scratch shared by all
+    recomputing layers of the shape, and the backward rebuilds them (permute,
+    then GEMM1 + SwiGLU) before the layer's backward kernels run. The rebuilt
+    tensors are bit-identical to the forward's, so are the gradients."""
+
+    def __init__(self, w1: torch.Tensor, w2: torch.Tensor, k: int, recompute: bool = False):
         self.w1, self.w2, self.k = w1, w2, k
         self.E, h2, self.d = w1.shape
         self.h = h2 // 2
+        self.recompute = recompute
         self._T = None
 
     def _alloc(self, T, dev, dt):
@@ -343,21 +370,27 @@ class MoELayer:
                           sorted_slot=torch.empty(R, **i32), tile_offsets=torch.empty(E + 1, **i32))
         self.route_ws = torch.empty(max(moe_route_workspace_size(T, E, k), 1), dtype=torch.uint8,
                                     device=dev)
-        self.x_perm = torch.empty((R, d), dtype=dt, device=dev)
-        self.ab = torch.empty((R, 2 * h), dtype=dt, device=dev)
-        self.hp = torch.empty((R, h), dtype=dt, device=dev)
-        self.y_perm = torch.empty((R, d), dtype=dt, device=dev)
+        own = (lambda name, shape: torch.empty(shape, dtype=dt, device=dev))
+        tmp = (lambda name, shape: _scratch(name, shape, dt, dev)) if self.recompute else own
+        self.x_perm = tmp("x_perm", (R, d))
+        self.ab = tmp("ab", (R, 2 * h))
+        self.hp = tmp("hp", (R, h))
+        self.y_perm = own("y_perm", (R, d))
         self.out = torch.empty((T, d), dtype=dt, device=dev)
         self.grads = None
         self._T = T
 
+    def _gemm1(self, offsets):
+        moe_grouped_gemm(MOE_GG_FWD, self.x_perm, self.w1, self.ab, offsets,
+                         MOE_EPI_SWIGLU_FWD, N=2 * self.h, K=self.d, aux_out=self.hp)
+
     def forward(self, x: torch.Tensor, logits: torch.Tensor) -> torch.Tensor:
         T, d = x.shape
         self._alloc(T, x.device, x.dtype)
+        self.x = x
         r = moe_route(logits, self.k, out=self.route, ws=self.route_ws)
         moe_permute(x, r["token_pos"], self.x_perm)
-        moe_grouped_gemm(MOE_GG_FWD, self.x_perm, self.w1, self.ab, r["offsets"],
-                         MOE_EPI_SWIGLU_FWD, N=2 * self.h, K=d, aux_out=self.hp)
+        self._gemm1(r["offsets"])
         moe_grouped_gemm(MOE_GG_FWD, self.hp, self.w2, self.y_perm, r["offsets"], N=d, K=self.h)
         moe_combine(self.y_perm, r["topk_gate"], r["token_pos"], self.out)
         return self.out
@@ -368,7 +401,19 @@ class MoELayer:
                     topk_gate=r["topk_gate"], topk_idx=r["topk_idx"], token_pos=r["token_pos"],
                     offsets=r["offsets"], w1=self.w1, w2=self.w2)
 
+    def held_bytes(self) -> int:
+        """Bytes of activations this layer holds from its forward to its
+        backward (the input x and the weights are the caller's)."""
+        r = self.route
+        meta = _nbytes(r.values())
+        if self.recompute:
+            return meta + _nbytes([self.y_perm])
+        return meta + _nbytes([self.x_perm, self.ab, self.hp, self.y_perm])
+
     def backward(self, dout: torch.Tensor) -> dict:
+        if self.recompute:
+            moe_permute(self.x, self.route["token_pos"], self.x_perm)
+            self._gemm1(self.route["offsets"])
         self.grads = moe_backward(self.saved(), dout, self.E, self.k, self.d, self.h,
                                   out=self.grads)
         return self.grads
@@ -443,10 +488,12 @@ class MoELayerMX:
     along h for GEMM2, and y, out stay bf16. The backward (moe_backward with
     MXFP8) quantises its own GEMM operands."""
 
-    def __init__(self, w1_master: torch.Tensor, w2_master: torch.Tensor, k: int):
+    def __init__(self, w1_master: torch.Tensor, w2_master: torch.Tensor, k: int,
+                 recompute: bool = False):
         self.E, h2, self.d = w1_master.shape
         self.h = h2 // 2
         self.k = k
+        self.recompute = recompute
         self.prepare_weights(w1_master, w2_master)
         self._T = None
 
@@ -474,31 +521,39 @@ class MoELayerMX:
                           token_pos=torch.empty((T, k), **i32), sorted_token=torch.empty(R, **i32),
                           sorted_slot=torch.empty(R, **i32), tile_offsets=torch.empty(E + 1, **i32))
         self.route_ws = torch.empty(max(moe_route_workspace_size(T, E, k), 1), **u8)
-        self.xq = torch.empty((T, d), **u8)
-        self.xs = torch.empty((T, d // 32), **u8)
-        self.xpq = torch.empty((R, d), **u8)
-        self.xps = torch.empty((R, d // 32), **u8)
-        self.ab = torch.empty((R, 2 * h), **bf)
-        self.hp = torch.empty((R, h), **bf)
-        self.hpq = torch.empty((R, h), **u8)
-        self.hps = torch.empty((R, h // 32), **u8)
+        # dispatch payload, A||B, H' and its MXFP8 copy: scratch when recomputing
+        tmp = ((lambda name, shape, dt: _scratch("mx_" + name, shape, dt, dev)) if self.recompute
+               else (lambda name, shape, dt: torch.empty(shape, dtype=dt, device=dev)))
+        self.xq = tmp("xq", (T, d), torch.uint8)
+        self.xs = tmp("xs", (T, d // 32), torch.uint8)
+        self.xpq = tmp("xpq", (R, d), torch.uint8)
+        self.xps = tmp("xps", (R, d // 32), torch.uint8)
+        self.ab = tmp("ab", (R, 2 * h), torch.bfloat16)
+        self.hp = tmp("hp", (R, h), torch.bfloat16)
+        self.hpq = tmp("hpq", (R, h), torch.uint8)
+        self.hps = tmp("hps", (R, h // 32), torch.uint8)
         self.y_perm = torch.empty((R, d), **bf)
         self.out = torch.empty((T, d), **bf)
         self.grads = None
         self.bwd_ws = None
         self._T = T
 
+    def _gemm1(self, x, offsets, token_pos):
+        """Quantised dispatch of x and GEMM1 + SwiGLU (forward, and again in
+        the backward when recomputing)."""
+        mxfp8_quantize(x, 1, q=self.xq, scale=self.xs)
+        moe_permute(self.xq, token_pos, self.xpq, x_scale=self.xs, x_perm_scale=self.xps)
+        moe_grouped_gemm(MOE_GG_FWD, self.xpq, self.w1q, self.ab, offsets, MOE_EPI_SWIGLU_FWD,
+                         N=2 * self.h, K=self.d, aux_out=self.hp, a_scale=self.xps,
+                         b_scale=self.w1s, dtype=MOE_MXFP8)
+
     def forward(self, x: torch.Tensor, logits: torch.Tensor) -> torch.Tensor:
         T, d = x.shape
         h = self.h
         self._alloc(T, x.device)
         self.x = x
-        mxfp8_quantize(x, 1, q=self.xq, scale=self.xs)
         r = moe_route(logits, self.k, out=self.route, ws=self.route_ws)
-        moe_permute(self.xq, r["token_pos"], self.xpq, x_scale=self.xs, x_perm_scale=self.xps)
-        moe_grouped_gemm(MOE_GG_FWD, self.xpq, self.w1q, self.ab, r["offsets"], MOE_EPI_SWIGLU_FWD,
-                         N=2 * h, K=d, aux_out=self.hp, a_scale=self.xps, b_scale=self.w1s,
-                         dtype=MOE_MXFP8)
+        self._gemm1(x, r["offsets"], r["token_pos"])
         mxfp8_quantize(self.hp, 1, q=self.hpq, scale=self.hps)
         moe_grouped_gemm(MOE_GG_FWD, self.hpq, self.w2q, self.y_perm, r["offsets"], N=d, K=h,
                          a_scale=self.hps, b_scale=self.w2s, dtype=MOE_MXFP8)
@@ -512,7 +567,17 @@ class MoELayerMX:
                     token_pos=r["token_pos"], offsets=r["offsets"], w1t=self.w1t,
                     w1t_scale=self.w1ts, w2t=self.w2t, w2t_scale=self.w2ts)
 
+    def held_bytes(self) -> int:
+        """Bytes of activations held from forward to backward (x and the
+        weights are the caller's)."""
+        meta = _nbytes(self.route.values())
+        if self.recompute:
+            return meta + _nbytes([self.y_perm])
+        return meta + _nbytes([self.ab, self.hp, self.y_perm])
+
     def backward(self, dout: torch.Tensor) -> dict:
+        if self.recompute:
+            self._gemm1(self.x, self.route["offsets"], self.route["token_pos"])
         self.grads = moe_backward(self.saved(), dout, self.E, self.k, self.d, self.h,
                                   out=self.grads, mxfp8=True)
         return self.grads

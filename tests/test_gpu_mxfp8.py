@@ -197,6 +197,28 @@ def test_mxfp8_layer_end_to_end(shape):
         assert rel_inf(to_np(g["dw2"][e]), m["dW2"][e]) <= tol, e
 
 
+def test_mxfp8_recompute_matches_saved():
+    """recompute=True re-quantises and re-dispatches x and reruns GEMM1 in
+    the backward: bit-identical gradients to the layer that keeps A||B and H'."""
+    T, d, E, k, h = 300, 256, 8, 2, 128
+    inp = _mx_inputs(T, d, E, k, h, seed=17)
+    base, out0, g0 = _run_mx(inp, k)
+    out0 = out0.clone()
+    g0 = {key: v.clone() for key, v in g0.items() if v is not None and not key.startswith("_")}
+    layer = moe.MoELayerMX(dev(inp["w1"], torch.float32), dev(inp["w2"], torch.float32), k,
+                           recompute=True)
+    out = layer.forward(dev(inp["x"], torch.bfloat16), dev(inp["logits"], torch.float32))
+    torch.cuda.synchronize()
+    for t in moe._SCRATCH.values():
+        t.fill_(float("nan") if t.is_floating_point() else 0x7F)
+    g = layer.backward(dev(inp["dout"], torch.bfloat16))
+    torch.cuda.synchronize()
+    assert torch.equal(out, out0)
+    for key in ("dx", "dw1", "dw2", "dlogits"):
+        assert torch.equal(g[key], g0[key]), key
+    assert layer.held_bytes() < base.held_bytes()
+
+
 def test_mxfp8_full_size_sampled():
     """The 32768-token, d=4096, E=128, h=2048 workload in the launch
     configuration the bench times; a few tokens and one expert are checked."""

@@ -207,6 +207,64 @@ def test_layer_end_to_end(shape, dt):
     assert np.all(to_np(g["dlogits"])[~sel] == 0)
 
 
+def _clobber_scratch():
+    """Overwrite the shared recompute scratch, as other layers would between
+    a layer's forward and its backward."""
+    for t in moe._SCRATCH.values():
+        if t.is_floating_point():
+            t.fill_(float("nan"))
+        else:
+            t.fill_(0x7F)
+
+
+@pytest.mark.parametrize("shape,dt", [((300, 256, 8, 2, 192), "bf16"), ((200, 64, 4, 4, 64), "f32")])
+def test_recompute_matches_saved(shape, dt):
+    """recompute=True holds only y_perm and the routing metadata and rebuilds
+    x_perm, A||B and H' in the backward: gradients bit-identical to the
+    layer that keeps them, and within tolerance of the oracle."""
+    T, d, E, k, h = shape
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    inp = _layer_inputs(T, d, E, k, h, seed=13, dt=dt)
+    base, out0, g0 = _run_layer(inp, k, tdt)
+    out0 = out0.clone()
+    g0 = {key: v.clone() for key, v in g0.items() if v is not None and not key.startswith("_")}
+    layer = moe.MoELayer(dev(inp["w1"], tdt), dev(inp["w2"], tdt), k, recompute=True)
+    out = layer.forward(dev(inp["x"], tdt), dev(inp["logits"], torch.float32))
+    torch.cuda.synchronize()
+    _clobber_scratch()
+    g = layer.backward(dev(inp["dout"], tdt))
+    torch.cuda.synchronize()
+    assert torch.equal(out, out0)
+    for key in ("dx", "dw1", "dw2", "dlogits", "dgate"):
+        assert torch.equal(g[key], g0[key]), key
+    assert layer.held_bytes() < base.held_bytes()
+    b = oracle.layer_backward(inp, oracle.layer_forward(inp, k, dt), k, dt)
+    assert rel_inf(to_np(g["dx"]), b["dx"]) <= TOL[dt]
+    assert rel_inf(to_np(g["dw1"]), b["dW1"]) <= TOL[dt]
+
+
+def test_recompute_full_size():
+    """The 16384-token E=128 workload, recomputing: bit-identical to the
+    layer that keeps its activations; holds under a third of their bytes."""
+    w = synth.WORKLOADS["e128_bf16"]
+    d_in = synth.device_inputs(w, seed=0, with_dout=True)
+    ref = moe.MoELayer(d_in["w1"], d_in["w2"], w.k)
+    ref.forward(d_in["x"], d_in["logits"])
+    g0 = {key: v.clone() for key, v in ref.backward(d_in["dout"]).items()
+          if v is not None and key in ("dx", "dw1", "dw2", "dlogits")}
+    held0 = ref.held_bytes()
+    del ref
+    layer = moe.MoELayer(d_in["w1"], d_in["w2"], w.k, recompute=True)
+    layer.forward(d_in["x"], d_in["logits"])
+    torch.cuda.synchronize()
+    _clobber_scratch()
+    g = layer.backward(d_in["dout"])
+    torch.cuda.synchronize()
+    for key, v in g0.items():
+        assert torch.equal(g[key], v), key
+    assert layer.held_bytes() * 3 < held0
+
+
 def test_tiny_fp32_workload():
     w = synth.WORKLOADS["tiny_fp32"]
     inp = synth.host_inputs(w, 0)
