@@ -149,6 +149,7 @@ def main():
     if not mx and w.backward and not a.no_padded:
         padded = padded_baseline(moe, torch, inp, w, a.steps, a.warmup)
         padded["dropless_speedup"] = padded["ms_per_step"] / ms
+    balance = load_balance_report(moe, torch, inp, layer, w)
     recompute = None
     if w.backward and not a.no_recompute:
         recompute = recompute_variant(moe, torch, inp, w, a.steps, a.warmup)
@@ -211,9 +212,34 @@ def main():
         res["padded_baseline"] = padded
     if recompute is not None:
         res["recompute"] = recompute
+    res["load_balance"] = balance
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, w, a.cpu_tokens)
     print(json.dumps(res), flush=True)
+
+
+def load_balance_report(moe, torch, inp, layer, w, reps=20, alpha=0.01):
+    """The balancing loss and load statistics of the workload's routing
+    (moe_load_balance on the layer's last routing), and the call's time with
+    and without the gradient pass; outside the timed step."""
+    logits, counts = inp["logits"], layer.route["counts"]
+    dl = torch.zeros_like(logits)
+    st = moe.moe_load_balance(logits, counts, w.k, alpha)
+    times = {}
+    for name, grad in (("us_stats", None), ("us_stats_and_grad", dl)):
+        moe.moe_load_balance(logits, counts, w.k, alpha, dlogits=grad)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            moe.moe_load_balance(logits, counts, w.k, alpha, dlogits=grad)
+        e1.record()
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) * 1e3 / reps
+    vals = st.cpu().tolist()
+    out = {"alpha": alpha, **{n: v for n, v in zip(moe.LB_STAT_NAMES, vals)}}
+    out.update(times)
+    return out
 
 
 def recompute_variant(moe, torch, inp, w, steps, warmup):

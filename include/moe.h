@@ -324,6 +324,39 @@ moe_status moe_capacity_pad(const int32_t *topk_idx, const int32_t *token_pos,
 moe_status moe_capacity_zero_rows(void *buf, moe_dtype dt, const int32_t *offsets, int32_t E,
                                   int32_t capacity, int32_t cols, void *stream);
 
+/* ------------------------------------------------------------------ */
+/* Load-balance statistics and the auxiliary balancing loss             */
+
+/* The report reads the load-balancing loss as part of the routing interface
+ * and names "token gerrymandering": the loss improves while the imbalance
+ * between experts grows (Ai2 Olmo-core 3, kongchang.com, "routing is a
+ * systems problem"; bytechap.com, "What you can do": monitor it in the
+ * routing metrics). The pages print no formula. This call computes the
+ * published Switch Transformer balancing loss (Fedus, Zoph and Shazeer 2021)
+ * for top-k routing, next to the hard-load statistics it can drift from:
+ *   f_e = counts[e] / (T k),  P_e = (1/T) sum_t softmax(logits[t, :])_e,
+ *   L = alpha * E * sum_e f_e P_e.
+ * stats (device, MOE_LB_NSTATS fp32, written):
+ *   [0] L                 [1] E sum f P (what L/alpha measures; 1 if uniform)
+ *   [2] E sum f^2 (hard balance of the counts; 1 if perfectly even)
+ *   [3] E sum P^2 (balance of the router probabilities)
+ *   [4] max_e c_e / mean   [5] min_e c_e / mean   (mean = T k / E)
+ *   [6] coefficient of variation of the counts    [7] experts with no row
+ * All zero for T = 0.
+ * dlogits (device [T, E] fp32, nullable): if given, dL/dlogits is ADDED to it
+ *   (call after moe_backward, which overwrites dlogits with the layer's
+ *   gradient); the counts are treated as constants, so
+ *   dL/dlogits[t, e] = (alpha E / T) p[t, e] (f_e - sum_j p[t, j] f_j).
+ * counts: moe_route's counts (device [E] int32). logits: the routing input
+ * (device [T, E] fp32). Limits as moe_route. Deterministic: fixed-order
+ * sums, no atomics. Workspace: moe_load_balance_workspace_size(T, E) bytes,
+ * 16-byte aligned, caller-owned. */
+#define MOE_LB_NSTATS 8
+size_t moe_load_balance_workspace_size(int64_t T, int32_t E);
+moe_status moe_load_balance(const float *logits, const int32_t *counts, int64_t T, int32_t E,
+                            int32_t k, float alpha, float *stats, float *dlogits, void *ws,
+                            size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -512,3 +512,41 @@ def layer_mx(inp: dict, k: int, tokens=None, experts=None, backward: bool = True
         dW1[e] = wgrad(mx_cols(dab[sel], lib), mx_cols(xb[src[sel]], lib), lib)
     res.update(dy=dy, dgate=dg, dlogits=dlogits, dab=dab, dx_perm=dxp, dx=dx, dW1=dW1, dW2=dW2)
     return res
+
+
+# ---------------------------------------------------------------------------
+# load balance (the report's routing section names "token gerrymandering",
+# a balancing loss that improves while the expert loads grow more uneven:
+# kongchang.com, "routing is a systems problem"; bytechap.com, "What you can
+# do"; it prints no formula). The loss is the Switch Transformer balancing
+# loss (Fedus, Zoph and Shazeer 2021), with the fraction of routed rows f_e
+# counting all k selections of a token.
+
+LB_STATS = ("loss", "soft_hard_balance", "hard_balance", "soft_balance", "max_load_over_mean",
+            "min_load_over_mean", "count_cv", "empty_experts")
+
+
+def load_balance(logits, counts, k: int, alpha: float):
+    """fp64: the balancing loss, the load statistics (named in LB_STATS) and
+    the loss gradient with respect to the logits, the counts held fixed.
+    Returns (stats[8], dlogits[T, E])."""
+    logits = np.asarray(logits, np.float64)
+    counts = np.asarray(counts, np.float64)
+    T, E = logits.shape
+    if T == 0:
+        return np.zeros(8), np.zeros((0, E))
+    # router probabilities: softmax over all E experts of each token
+    z = logits - logits.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p /= p.sum(axis=1, keepdims=True)
+    P = p.mean(axis=0)                       # mean probability per expert
+    f = counts / (T * k)                     # fraction of routed rows per expert
+    balance = E * np.dot(f, P)
+    loss = alpha * balance
+    mean = T * k / E
+    stats = np.array([loss, balance, E * np.dot(f, f), E * np.dot(P, P), counts.max() / mean,
+                      counts.min() / mean, counts.std() / mean, float((counts == 0).sum())])
+    # dL/dlogit_{t,e} = (alpha E / T) * sum_j f_j dp_{t,j}/dlogit_{t,e}
+    #                = (alpha E / T) * p_{t,e} (f_e - sum_j p_{t,j} f_j)
+    grad = (alpha * E / T) * p * (f[None, :] - (p @ f)[:, None])
+    return stats, grad

@@ -90,6 +90,10 @@ def _load():
     lib.moe_capacity_pad.restype = _I32
     lib.moe_capacity_zero_rows.argtypes = [_P, _I32, _P, _I32, _I32, _I32, _P]
     lib.moe_capacity_zero_rows.restype = _I32
+    lib.moe_load_balance_workspace_size.argtypes = [_I64, _I32]
+    lib.moe_load_balance_workspace_size.restype = _SZ
+    lib.moe_load_balance.argtypes = [_P, _P, _I64, _I32, _I32, ctypes.c_float, _P, _P, _P, _SZ, _P]
+    lib.moe_load_balance.restype = _I32
     return lib
 
 
@@ -336,6 +340,60 @@ def _nbytes(ts) -> int:
     return sum(t.numel() * t.element_size() for t in ts if t is not None)
 
 
+MOE_LB_NSTATS = 8
+LB_STAT_NAMES = ("loss", "soft_hard_balance", "hard_balance", "soft_balance", "max_load_over_mean",
+                 "min_load_over_mean", "count_cv", "empty_experts")
+
+
+def moe_load_balance_workspace_size(T: int, E: int) -> int:
+    return int(_lib.moe_load_balance_workspace_size(T, E))
+
+
+def moe_load_balance(logits: torch.Tensor, counts: torch.Tensor, k: int, alpha: float,
+                     stats: torch.Tensor | None = None, dlogits: torch.Tensor | None = None,
+                     ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Switch-style balancing loss and load statistics (see moe.h); with
+    dlogits, its gradient is added into dlogits. Returns the device stats."""
+    T, E = logits.shape
+    _need(logits, (T, E), torch.float32, "logits")
+    _need(counts, (E,), torch.int32, "counts")
+    if stats is None:
+        stats = torch.empty(MOE_LB_NSTATS, dtype=torch.float32, device=logits.device)
+    if dlogits is not None:
+        _need(dlogits, (T, E), torch.float32, "dlogits")
+    wsb = moe_load_balance_workspace_size(T, E)
+    if ws is None or ws.numel() < wsb:
+        ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device=logits.device)
+    _check("moe_load_balance", _lib.moe_load_balance(
+        _p(logits), _p(counts), T, E, k, float(alpha), _p(stats), _p(dlogits), _p(ws), ws.numel(),
+        _stream()))
+    return stats
+
+
+class _Balance:
+    """The optional balancing loss of a layer: statistics after routing in
+    the forward, its gradient added into dlogits after the backward."""
+
+    def __init__(self, alpha: float):
+        self.alpha = alpha
+        self.stats = None
+        self.ws = None
+
+    def forward(self, logits, counts, k):
+        T, E = logits.shape
+        if self.stats is None:
+            self.stats = torch.empty(MOE_LB_NSTATS, dtype=torch.float32, device=logits.device)
+        wsb = max(moe_load_balance_workspace_size(T, E), 4)
+        if self.ws is None or self.ws.numel() < wsb:
+            self.ws = torch.empty(wsb, dtype=torch.uint8, device=logits.device)
+        self.logits, self.counts, self.k = logits, counts, k
+        return moe_load_balance(logits, counts, k, self.alpha, stats=self.stats, ws=self.ws)
+
+    def backward(self, dlogits):
+        moe_load_balance(self.logits, self.counts, self.k, self.alpha, stats=self.stats,
+                         dlogits=dlogits, ws=self.ws)
+
+
 class MoELayer:
     """Forward and backward of the MoE expert layer through the C ABI.
 
@@ -348,13 +406,20 @@ class MoELayer:
     backward. x_perm, A||B and H' are written to scratch shared by all
     recomputing layers of the shape, and the backward rebuilds them (permute,
     then GEMM1 + SwiGLU) before the layer's backward kernels run. The rebuilt
-    tensors are bit-identical to the forward's, so are the gradients."""
+    tensors are bit-identical to the forward's, so are the gradients.
 
-    def __init__(self, w1: torch.Tensor, w2: torch.Tensor, k: int, recompute: bool = False):
+    aux_alpha adds the balancing loss of moe_load_balance: its statistics
+    are in `lb_stats` (device) after forward, and backward adds its
+    gradient to dlogits."""
+
+    def __init__(self, w1: torch.Tensor, w2: torch.Tensor, k: int, recompute: bool = False,
+                 aux_alpha: float | None = None):
         self.w1, self.w2, self.k = w1, w2, k
         self.E, h2, self.d = w1.shape
         self.h = h2 // 2
         self.recompute = recompute
+        self.balance = _Balance(aux_alpha) if aux_alpha is not None else None
+        self.lb_stats = None
         self._T = None
 
     def _alloc(self, T, dev, dt):
@@ -389,6 +454,8 @@ class MoELayer:
         self._alloc(T, x.device, x.dtype)
         self.x = x
         r = moe_route(logits, self.k, out=self.route, ws=self.route_ws)
+        if self.balance is not None:
+            self.lb_stats = self.balance.forward(logits, r["counts"], self.k)
         moe_permute(x, r["token_pos"], self.x_perm)
         self._gemm1(r["offsets"])
         moe_grouped_gemm(MOE_GG_FWD, self.hp, self.w2, self.y_perm, r["offsets"], N=d, K=self.h)
@@ -416,6 +483,8 @@ class MoELayer:
             self._gemm1(self.route["offsets"])
         self.grads = moe_backward(self.saved(), dout, self.E, self.k, self.d, self.h,
                                   out=self.grads)
+        if self.balance is not None:
+            self.balance.backward(self.grads["dlogits"])
         return self.grads
 
 
@@ -489,11 +558,13 @@ class MoELayerMX:
     MXFP8) quantises its own GEMM operands."""
 
     def __init__(self, w1_master: torch.Tensor, w2_master: torch.Tensor, k: int,
-                 recompute: bool = False):
+                 recompute: bool = False, aux_alpha: float | None = None):
         self.E, h2, self.d = w1_master.shape
         self.h = h2 // 2
         self.k = k
         self.recompute = recompute
+        self.balance = _Balance(aux_alpha) if aux_alpha is not None else None
+        self.lb_stats = None
         self.prepare_weights(w1_master, w2_master)
         self._T = None
 
@@ -553,6 +624,8 @@ class MoELayerMX:
         self._alloc(T, x.device)
         self.x = x
         r = moe_route(logits, self.k, out=self.route, ws=self.route_ws)
+        if self.balance is not None:
+            self.lb_stats = self.balance.forward(logits, r["counts"], self.k)
         self._gemm1(x, r["offsets"], r["token_pos"])
         mxfp8_quantize(self.hp, 1, q=self.hpq, scale=self.hps)
         moe_grouped_gemm(MOE_GG_FWD, self.hpq, self.w2q, self.y_perm, r["offsets"], N=d, K=h,
@@ -580,4 +653,6 @@ class MoELayerMX:
             self._gemm1(self.x, self.route["offsets"], self.route["token_pos"])
         self.grads = moe_backward(self.saved(), dout, self.E, self.k, self.d, self.h,
                                   out=self.grads, mxfp8=True)
+        if self.balance is not None:
+            self.balance.backward(self.grads["dlogits"])
         return self.grads

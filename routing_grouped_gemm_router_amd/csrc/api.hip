@@ -37,6 +37,9 @@ moe_status capacity_pad_launch(const int32_t *topk_idx, const int32_t *token_pos
                                int32_t *token_pos_pad, int32_t *offsets_pad, hipStream_t s);
 moe_status capacity_zero_launch(void *buf, moe_dtype dt, const int32_t *offsets, int E, int C,
                                 int cols, hipStream_t s);
+moe_status load_balance_launch(const float *logits, const int32_t *counts, int64_t T, int E, int k,
+                               float alpha, float *stats, float *dlogits, void *ws, hipStream_t s);
+size_t load_balance_ws_bytes(int64_t T, int E);
 
 int num_cus() {
     static int cache[64] = {0};
@@ -369,6 +372,24 @@ moe_status moe_capacity_zero_rows(void *buf, moe_dtype dt, const int32_t *offset
     if (!buf || !offsets) return MOE_ERR_NULL;
     if (!aligned16(buf)) return MOE_ERR_ALIGN;
     return capacity_zero_launch(buf, dt, offsets, E, capacity, cols, (hipStream_t)stream);
+}
+
+size_t moe_load_balance_workspace_size(int64_t T, int32_t E) {
+    if (T < 0 || E < 1 || E > 256) return 0;
+    return load_balance_ws_bytes(T, E);
+}
+
+moe_status moe_load_balance(const float *logits, const int32_t *counts, int64_t T, int32_t E,
+                            int32_t k, float alpha, float *stats, float *dlogits, void *ws,
+                            size_t ws_bytes, void *stream) {
+    if (!routing_shape_ok(T, E, k)) return MOE_ERR_SHAPE;
+    if (!stats) return MOE_ERR_NULL;
+    if (T > 0 && (!logits || !counts || !ws)) return MOE_ERR_NULL;
+    if (!aligned4(logits) || !aligned4(stats) || !aligned4(dlogits) || !aligned16(ws))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < load_balance_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
+    return load_balance_launch(logits, counts, T, E, k, alpha, stats, dlogits, ws,
+                               (hipStream_t)stream);
 }
 
 moe_status mxfp8_quantize(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,

@@ -167,3 +167,23 @@ def test_capacity_validation(lib):
     assert lib.moe_capacity_zero_rows(None, 1, a, 8, 8, 64, None) == 1
     assert lib.moe_capacity_zero_rows(a16 + 4, 1, a, 8, 8, 64, None) == 4       # alignment
     assert lib.moe_capacity_zero_rows(None, 1, None, 8, 0, 64, None) == 0       # nothing to do
+
+
+def test_load_balance_validation(lib):
+    """Host-side checks of moe_load_balance (nothing is launched)."""
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    lib.moe_load_balance.argtypes = [P, P, I64, I32, I32, ctypes.c_float, P, P, P, SZ, P]
+    lib.moe_load_balance_workspace_size.argtypes = [I64, I32]
+    lib.moe_load_balance_workspace_size.restype = SZ
+    assert lib.moe_load_balance_workspace_size(16384, 128) == 256 * 128 * 4 + 128 * 8
+    fake = 0x100000
+    big = 1 << 30
+    assert lib.moe_load_balance(fake, fake, 16, 300, 2, 1.0, fake, None, fake, big, None) == 2  # E
+    assert lib.moe_load_balance(fake, fake, 16, 8, 9, 1.0, fake, None, fake, big, None) == 2    # k > E
+    assert lib.moe_load_balance(fake, fake, 16, 8, 2, 1.0, None, None, fake, big, None) == 1    # stats
+    assert lib.moe_load_balance(None, fake, 16, 8, 2, 1.0, fake, None, fake, big, None) == 1    # logits
+    assert lib.moe_load_balance(fake, fake, 16, 8, 2, 1.0, fake, None, None, big, None) == 1    # ws
+    assert lib.moe_load_balance(fake, fake, 16, 8, 2, 1.0, fake + 2, None, fake, big, None) == 4
+    assert lib.moe_load_balance(fake, fake, 16, 8, 2, 1.0, fake, fake + 1, fake, big, None) == 4
+    assert lib.moe_load_balance(fake, fake, 16, 8, 2, 1.0, fake, None, fake + 4, big, None) == 4
+    assert lib.moe_load_balance(fake, fake, 100, 8, 2, 1.0, fake, None, fake, 4, None) == 5     # ws size
