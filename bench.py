@@ -150,6 +150,9 @@ def main():
         padded = padded_baseline(moe, torch, inp, w, a.steps, a.warmup)
         padded["dropless_speedup"] = padded["ms_per_step"] / ms
     balance = load_balance_report(moe, torch, inp, layer, w)
+    accum = grad_accumulation(moe, torch, layer, x, logits, dout, w, a.steps, ms) \
+        if w.backward else None
+    requant = weight_requant(moe, torch, inp, layer, w) if mx else None
     recompute = None
     if w.backward and not a.no_recompute:
         recompute = recompute_variant(moe, torch, inp, w, a.steps, a.warmup)
@@ -213,6 +216,10 @@ def main():
     if recompute is not None:
         res["recompute"] = recompute
     res["load_balance"] = balance
+    if accum is not None:
+        res["grad_accumulation"] = accum
+    if requant is not None:
+        res["weight_requant"] = requant
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, w, a.cpu_tokens)
     print(json.dumps(res), flush=True)
@@ -240,6 +247,56 @@ def load_balance_report(moe, torch, inp, layer, w, reps=20, alpha=0.01):
     out = {"alpha": alpha, **{n: v for n, v in zip(moe.LB_STAT_NAMES, vals)}}
     out.update(times)
     return out
+
+
+def grad_accumulation(moe, torch, layer, x, logits, dout, w, steps, ms_overwrite):
+    """A micro-batch step whose backward adds dW1, dW2 into the previous
+    micro-batch's (accumulate_dw), against the main step that overwrites
+    them; outside the main timed region."""
+    layer.forward(x, logits)
+    layer.backward(dout)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward(x, logits)
+        layer.backward(dout, accumulate_dw=True)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    return {"ms_per_step": el * 1e3 / steps, "tokens_per_s": w.T * steps / el,
+            "extra_ms_vs_overwrite": el * 1e3 / steps - ms_overwrite,
+            "dw_bytes": 4 * w.E * 3 * w.d * w.h}
+
+
+def weight_requant(moe, torch, inp, layer, w, reps=5):
+    """Once-per-optimizer-step re-quantisation of the fp32 master weights to
+    MXFP8 in both orientations: fused (each master read once) against four
+    separate mxfp8_quantize calls (each master read twice)."""
+    E, d, h = w.E, w.d, w.h
+    w1, w2 = inp["w1"], inp["w2"]
+    g1 = torch.arange(0, E + 1, dtype=torch.int32, device="cuda") * (2 * h)
+    g2 = torch.arange(0, E + 1, dtype=torch.int32, device="cuda") * d
+
+    def separate():
+        moe.mxfp8_quantize(w1.reshape(E * 2 * h, d), 1)
+        moe.mxfp8_quantize(w2.reshape(E * d, h), 1)
+        moe.mxfp8_quantize(w1.reshape(E * 2 * h, d), 0, g1)
+        moe.mxfp8_quantize(w2.reshape(E * d, h), 0, g2)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / reps
+
+    fused_ms = timed(lambda: layer.prepare_weights(w1, w2))
+    sep_ms = timed(separate)
+    n = E * 3 * d * h                                    # master elements
+    algo = n * 4 + 2 * (n + n // 32)                     # read once, write both orientations
+    return {"fused_ms": fused_ms, "separate_ms": sep_ms, "algorithmic_bytes": algo,
+            "fused_GBps": algo / (fused_ms * 1e-3) / 1e9}
 
 
 def recompute_variant(moe, torch, inp, w, steps, warmup):

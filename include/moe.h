@@ -145,7 +145,13 @@ enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU_FWD = 1, MOE_EPI_SWIGLU_BWD = 2 };
  * mode MOE_GG_DGRAD: C[r, n]    = sum_k A[r, k] * B[g][k, n]
  *                    A [rows, K], B [E, K, N], C [rows, N]
  * mode MOE_GG_WGRAD: C[g][m, n] = sum_{r in g} A[r, m] * B[r, n]
- *                    A [rows, M], B [rows, N], C [E, M, N] fp32, overwritten
+ *                    A [rows, M], B [rows, N], C [E, M, N] fp32, overwritten,
+ *                    or with accumulate = 1: C[g][m, n] += that sum (one
+ *                    fp32 add per element; a group of 0 rows leaves C[g]
+ *                    unchanged). For gradient accumulation over
+ *                    micro-batches between optimizer steps, the window the
+ *                    report's data-parallel setup keeps the weights for
+ *                    (kongchang.com, "capacity tax").
  *
  * epilogue MOE_EPI_SWIGLU_FWD (mode FWD, N = 2h, B = W1 [E, 2h, d]):
  *   C = AB [rows, 2h] (gate pre-activation a in columns 0..h-1, up b in
@@ -191,6 +197,7 @@ typedef struct moe_gemm_desc {
     uint8_t *aux_out_scale;  /* SWIGLU_FWD with MXFP8: H' scales */
     void *ws;                /* scratch (split-K partials); may be null if ws_bytes = 0 */
     size_t ws_bytes;
+    int32_t accumulate;      /* WGRAD only: 1 = C[g] += the product (fp32 add), 0 = overwrite */
 } moe_gemm_desc;
 
 /* Scratch bytes moe_grouped_gemm needs for this descriptor (0 when none). */
@@ -254,6 +261,7 @@ typedef struct moe_bwd_desc {
     const uint8_t *w2t_scale;      /* [E, h, d/32] */
     void *ws;                      /* scratch, moe_backward_workspace_size bytes */
     size_t ws_bytes;
+    int32_t accumulate_dw;         /* 1: dW1, dW2 += this micro-batch's gradients; 0: overwrite */
 } moe_bwd_desc;
 
 size_t moe_backward_workspace_size(const moe_bwd_desc *b);
@@ -293,6 +301,18 @@ moe_status mxfp8_quantize(const void *in, moe_dtype in_dt, int64_t rows, int64_t
 
 /* Worst-case block count of the column-block layout: rows/32 + 4*n_groups + 4. */
 size_t mxfp8_col_blocks(int64_t rows, int32_t n_groups);
+
+/* Both orientations from one read of the input: q_rows / s_rows exactly as
+ * mxfp8_quantize with axis = 1, and q_cols / s_cols exactly as axis = 0 with
+ * these groups. Its use here is the once-per-optimizer-step re-quantisation
+ * of the fp32 master weights (the report keeps FP32 masters and quantises to
+ * MXFP8 for the GEMMs, kongchang.com "caveats behind the numbers"): W [E*R, C] along C
+ * for the forward GEMMs and, per expert (group_offsets = e*R), along R for
+ * the backward ones, reading the 4-byte masters once instead of twice. Same
+ * limits, layouts and alignment as mxfp8_quantize (no row_map). */
+moe_status mxfp8_quantize_both(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
+                               const int32_t *group_offsets, int32_t n_groups, uint8_t *q_rows,
+                               uint8_t *s_rows, uint8_t *q_cols, uint8_t *s_cols, void *stream);
 
 /* ------------------------------------------------------------------ */
 /* Padded-capacity alternative (for comparison)                         */

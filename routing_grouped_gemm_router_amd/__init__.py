@@ -44,7 +44,7 @@ class GemmDesc(ctypes.Structure):
                 ("rows", _I64), ("M", _I32), ("N", _I32), ("K", _I32),
                 ("offsets", _P), ("A", _P), ("B", _P), ("C", _P), ("a_scale", _P),
                 ("b_scale", _P), ("aux", _P), ("aux_out", _P), ("aux_out_scale", _P),
-                ("ws", _P), ("ws_bytes", _SZ)]
+                ("ws", _P), ("ws_bytes", _SZ), ("accumulate", _I32)]
 
 
 class BwdDesc(ctypes.Structure):
@@ -54,7 +54,7 @@ class BwdDesc(ctypes.Structure):
                 ("dout", _P), ("dx", _P), ("dlogits", _P), ("dw1", _P), ("dw2", _P),
                 ("dgate", _P), ("dy_perm", _P), ("dab", _P), ("dx_perm", _P), ("x", _P),
                 ("sorted_token", _P), ("w1t", _P), ("w1t_scale", _P), ("w2t", _P),
-                ("w2t_scale", _P), ("ws", _P), ("ws_bytes", _SZ)]
+                ("w2t_scale", _P), ("ws", _P), ("ws_bytes", _SZ), ("accumulate_dw", _I32)]
 
 
 def _load():
@@ -86,6 +86,8 @@ def _load():
     lib.mxfp8_quantize.restype = _I32
     lib.mxfp8_col_blocks.argtypes = [_I64, _I32]
     lib.mxfp8_col_blocks.restype = _SZ
+    lib.mxfp8_quantize_both.argtypes = [_P, _I32, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P]
+    lib.mxfp8_quantize_both.restype = _I32
     lib.moe_capacity_pad.argtypes = [_P, _P, _P, _I64, _I32, _I32, _I32, _P, _P, _P]
     lib.moe_capacity_pad.restype = _I32
     lib.moe_capacity_zero_rows.argtypes = [_P, _I32, _P, _I32, _I32, _I32, _P]
@@ -200,9 +202,10 @@ def moe_grouped_gemm(mode: int, A: torch.Tensor, B: torch.Tensor, C: torch.Tenso
                      offsets: torch.Tensor, epilogue: int = MOE_EPI_NONE, M: int = 0, N: int = 0,
                      K: int = 0, aux: torch.Tensor | None = None,
                      aux_out: torch.Tensor | None = None, a_scale=None, b_scale=None,
-                     aux_out_scale=None, dtype: int | None = None):
+                     aux_out_scale=None, dtype: int | None = None, accumulate: bool = False):
     """One grouped GEMM (see moe.h for the modes and epilogues)."""
     desc = GemmDesc()
+    desc.accumulate = 1 if accumulate else 0
     desc.mode = mode
     desc.dtype = _dt(A) if dtype is None else dtype
     desc.epilogue = epilogue
@@ -225,7 +228,8 @@ def moe_grouped_gemm(mode: int, A: torch.Tensor, B: torch.Tensor, C: torch.Tenso
 
 
 def moe_backward(saved: dict, dout: torch.Tensor, E: int, k: int, d: int, h: int,
-                 out: dict | None = None, want_dgate: bool = True, mxfp8: bool = False) -> dict:
+                 out: dict | None = None, want_dgate: bool = True, mxfp8: bool = False,
+                 accumulate_dw: bool = False) -> dict:
     """Backward of the whole layer. `saved` holds the forward tensors
     (x_perm, ab, hp, y_perm, topk_gate, topk_idx, token_pos, offsets, w1, w2;
     with mxfp8: x, sorted_token, w1t, w1t_scale, w2t, w2t_scale instead of
@@ -243,6 +247,7 @@ def moe_backward(saved: dict, dout: torch.Tensor, E: int, k: int, d: int, h: int
                    dab=torch.empty((R, 2 * h), dtype=dt, device=dev),
                    dx_perm=torch.empty((R, d), dtype=dt, device=dev))
     b = BwdDesc()
+    b.accumulate_dw = 1 if accumulate_dw else 0
     b.dtype = MOE_MXFP8 if mxfp8 else _dt(dout)
     b.d, b.h, b.E, b.k, b.T = d, h, E, k, T
     names = ("ab", "hp", "y_perm", "topk_gate", "topk_idx", "token_pos", "offsets")
@@ -292,6 +297,23 @@ def mxfp8_quantize(x: torch.Tensor, axis: int = 1, group_offsets: torch.Tensor |
                                                  _p(group_offsets), ng, _p(row_map), _p(q),
                                                  _p(scale), _stream()))
     return q, scale
+
+
+def mxfp8_quantize_both(x: torch.Tensor, group_offsets: torch.Tensor | None = None):
+    """Both orientations from one read (see moe.h): returns (q_rows, s_rows)
+    as mxfp8_quantize axis=1 and (q_cols, s_cols) as axis=0 with these groups."""
+    rows, cols = x.shape
+    dev = x.device
+    ng = 0 if group_offsets is None else group_offsets.numel() - 1
+    q1 = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    s1 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    nb = mxfp8_col_blocks(rows, max(ng, 1))
+    q0 = torch.empty(nb * 32 * cols, dtype=torch.uint8, device=dev)
+    s0 = torch.empty(nb * cols, dtype=torch.uint8, device=dev)
+    _check("mxfp8_quantize_both", _lib.mxfp8_quantize_both(
+        _p(x), _dt(x), rows, cols, _p(group_offsets), ng, _p(q1), _p(s1), _p(q0), _p(s0),
+        _stream()))
+    return (q1, s1), (q0, s0)
 
 
 def moe_capacity_pad(route: dict, capacity: int, out: dict | None = None) -> dict:
@@ -401,7 +423,7 @@ class MoELayer:
     issues only kernel launches (no allocation, no device->host traffic).
 
     recompute=True trades compute for activation memory (the trade-off the
-    Olmo-core 3 report measures, kongchang.com "MXFP8 and memory"): the
+    Olmo-core 3 report measures, kongchang.com "where the costs are"): the
     layer keeps only y_perm and the routing metadata from its forward to its
     backward. x_perm, A||B and H' are written to scratch shared by all
     recomputing layers of the shape, and the backward rebuilds them (permute,
@@ -477,12 +499,16 @@ class MoELayer:
             return meta + _nbytes([self.y_perm])
         return meta + _nbytes([self.x_perm, self.ab, self.hp, self.y_perm])
 
-    def backward(self, dout: torch.Tensor) -> dict:
+    def backward(self, dout: torch.Tensor, accumulate_dw: bool = False) -> dict:
+        """accumulate_dw: add this micro-batch's dW1, dW2 to the ones already
+        in self.grads (gradient accumulation between optimizer steps)."""
         if self.recompute:
             moe_permute(self.x, self.route["token_pos"], self.x_perm)
             self._gemm1(self.route["offsets"])
+        if accumulate_dw and self.grads is None:
+            raise ValueError("accumulate_dw needs the gradients of an earlier backward")
         self.grads = moe_backward(self.saved(), dout, self.E, self.k, self.d, self.h,
-                                  out=self.grads)
+                                  out=self.grads, accumulate_dw=accumulate_dw)
         if self.balance is not None:
             self.balance.backward(self.grads["dlogits"])
         return self.grads
@@ -541,9 +567,9 @@ class MoELayerPadded(MoELayer):
         sv["offsets"] = self.pad["offsets"]
         return sv
 
-    def backward(self, dout: torch.Tensor) -> dict:
+    def backward(self, dout: torch.Tensor, accumulate_dw: bool = False) -> dict:
         moe_capacity_zero_rows(self.grads["dy_perm"], self.route["offsets"], self.capacity)
-        return super().backward(dout)
+        return super().backward(dout, accumulate_dw)
 
 
 class MoELayerMX:
@@ -569,14 +595,16 @@ class MoELayerMX:
         self._T = None
 
     def prepare_weights(self, w1: torch.Tensor, w2: torch.Tensor):
+        """Re-quantise the fp32 masters, once per optimizer step: each master
+        is read once and written in both orientations (mxfp8_quantize_both)."""
         E, d, h = self.E, self.d, self.h
         dev = w1.device
-        self.w1q, self.w1s = mxfp8_quantize(w1.reshape(E * 2 * h, d), 1)
-        self.w2q, self.w2s = mxfp8_quantize(w2.reshape(E * d, h), 1)
         g1 = torch.arange(0, E + 1, dtype=torch.int32, device=dev) * (2 * h)
         g2 = torch.arange(0, E + 1, dtype=torch.int32, device=dev) * d
-        self.w1t, self.w1ts = mxfp8_quantize(w1.reshape(E * 2 * h, d), 0, g1)
-        self.w2t, self.w2ts = mxfp8_quantize(w2.reshape(E * d, h), 0, g2)
+        (self.w1q, self.w1s), (self.w1t, self.w1ts) = mxfp8_quantize_both(
+            w1.reshape(E * 2 * h, d), g1)
+        (self.w2q, self.w2s), (self.w2t, self.w2ts) = mxfp8_quantize_both(
+            w2.reshape(E * d, h), g2)
 
     def _alloc(self, T, dev):
         if self._T == T:
@@ -648,11 +676,15 @@ class MoELayerMX:
             return meta + _nbytes([self.y_perm])
         return meta + _nbytes([self.ab, self.hp, self.y_perm])
 
-    def backward(self, dout: torch.Tensor) -> dict:
+    def backward(self, dout: torch.Tensor, accumulate_dw: bool = False) -> dict:
+        """accumulate_dw: add this micro-batch's dW1, dW2 to the ones already
+        in self.grads."""
         if self.recompute:
             self._gemm1(self.x, self.route["offsets"], self.route["token_pos"])
+        if accumulate_dw and self.grads is None:
+            raise ValueError("accumulate_dw needs the gradients of an earlier backward")
         self.grads = moe_backward(self.saved(), dout, self.E, self.k, self.d, self.h,
-                                  out=self.grads, mxfp8=True)
+                                  out=self.grads, mxfp8=True, accumulate_dw=accumulate_dw)
         if self.balance is not None:
             self.balance.backward(self.grads["dlogits"])
         return self.grads

@@ -28,7 +28,7 @@ moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, 
                                  int axis, const int32_t *group_offsets, int n_groups,
                                  const int32_t *row_map, uint8_t *q, uint8_t *scale,
                                  hipStream_t s);
-moe_status mxfp8_quantize_both_launch(const void *in, int64_t rows, int64_t cols,
+moe_status mxfp8_quantize_both_launch(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
                                       const int32_t *group_offsets, int n_groups, uint8_t *q1,
                                       uint8_t *s1, uint8_t *q0, uint8_t *s0, hipStream_t s);
 size_t mxfp8_col_blocks(int64_t rows, int n_groups);
@@ -171,6 +171,7 @@ static moe_status check_gemm(const moe_gemm_desc *g) {
     if (g->epilogue == MOE_EPI_SWIGLU_FWD && g->mode != MOE_GG_FWD) return MOE_ERR_DTYPE;
     if (g->epilogue == MOE_EPI_SWIGLU_BWD && g->mode != MOE_GG_DGRAD) return MOE_ERR_DTYPE;
     if (g->epilogue < MOE_EPI_NONE || g->epilogue > MOE_EPI_SWIGLU_BWD) return MOE_ERR_DTYPE;
+    if (g->accumulate != 0 && (g->accumulate != 1 || g->mode != MOE_GG_WGRAD)) return MOE_ERR_DTYPE;
     if (g->n_groups < 1 || g->n_groups > 256) return MOE_ERR_SHAPE;
     if (g->rows < 0 || g->rows >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
     if (g->mode == MOE_GG_WGRAD) {
@@ -219,6 +220,7 @@ moe_status moe_backward(const moe_bwd_desc *b, void *stream) {
     if (!b) return MOE_ERR_NULL;
     if (b->dtype == MOE_MXFP8) return backward_mxfp8(b, (hipStream_t)stream);
     if (b->dtype != MOE_F32 && b->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (b->accumulate_dw != 0 && b->accumulate_dw != 1) return MOE_ERR_DTYPE;
     if (!routing_shape_ok(b->T, b->E, b->k) || !width_ok(b->d) || !width_ok(b->h))
         return MOE_ERR_SHAPE;
     if (!b->dw1 || !b->dw2 || !b->offsets || !b->w1 || !b->w2) return MOE_ERR_NULL;
@@ -250,15 +252,16 @@ moe_status moe_backward(const moe_bwd_desc *b, void *stream) {
     if (R > 0 && (st = gemm_launch(&g, s)) != MOE_OK) return st;
     // GEMM2 wgrad: dW2[e] = dy^T H'
     g.mode = MOE_GG_WGRAD; g.epilogue = MOE_EPI_NONE; g.aux = nullptr;
+    g.accumulate = b->accumulate_dw;
     g.M = b->d; g.N = b->h; g.K = 0;
     g.A = b->dy_perm; g.B = b->hp; g.C = b->dw2;
     if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
     // GEMM1 dgrad: dx_perm = dAB . W1[e]
-    g.mode = MOE_GG_DGRAD; g.M = 0; g.N = b->d; g.K = 2 * b->h;
+    g.mode = MOE_GG_DGRAD; g.accumulate = 0; g.M = 0; g.N = b->d; g.K = 2 * b->h;
     g.A = b->dab; g.B = b->w1; g.C = b->dx_perm;
     if (R > 0 && (st = gemm_launch(&g, s)) != MOE_OK) return st;
     // GEMM1 wgrad: dW1[e] = dAB^T x
-    g.mode = MOE_GG_WGRAD; g.M = 2 * b->h; g.N = b->d; g.K = 0;
+    g.mode = MOE_GG_WGRAD; g.accumulate = b->accumulate_dw; g.M = 2 * b->h; g.N = b->d; g.K = 0;
     g.A = b->dab; g.B = b->x_perm; g.C = b->dw1;
     if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
     // unpermute backward: dX[t] = sum_j dx_perm[token_pos[t, j]]
@@ -267,6 +270,7 @@ moe_status moe_backward(const moe_bwd_desc *b, void *stream) {
 }
 
 static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
+    if (b->accumulate_dw != 0 && b->accumulate_dw != 1) return MOE_ERR_DTYPE;
     if (!routing_shape_ok(b->T, b->E, b->k) || !width_ok(b->d) || !width_ok(b->h) ||
         b->d % 128 || b->h % 128)
         return MOE_ERR_SHAPE;
@@ -304,7 +308,7 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
     g.rows = R;
     g.offsets = b->offsets;
     // dy along d (GEMM2 dgrad) and along rows per expert (GEMM2 wgrad), one read
-    if ((st = R > 0 ? mxfp8_quantize_both_launch(b->dy_perm, R, d, b->offsets, E, aq, as, b0q,
+    if ((st = R > 0 ? mxfp8_quantize_both_launch(b->dy_perm, MOE_BF16, R, d, b->offsets, E, aq, as, b0q,
                                                   b0s, s)
                     : mxfp8_quantize_launch(b->dy_perm, MOE_BF16, R, d, 0, b->offsets, E,
                                             nullptr, b0q, b0s, s)) != MOE_OK)
@@ -321,17 +325,18 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
                                     s)) != MOE_OK)
         return st;
     g.mode = MOE_GG_WGRAD; g.epilogue = MOE_EPI_NONE; g.aux = nullptr; g.M = d; g.N = h; g.K = 0;
+    g.accumulate = b->accumulate_dw;
     g.A = b0q; g.a_scale = b0s; g.B = b1q; g.b_scale = b1s; g.C = b->dw2;
     if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
     // dAB along 2h (GEMM1 dgrad) and along rows per expert (GEMM1 wgrad), one read
-    if ((st = R > 0 ? mxfp8_quantize_both_launch(b->dab, R, 2 * h, b->offsets, E, aq, as, b0q,
+    if ((st = R > 0 ? mxfp8_quantize_both_launch(b->dab, MOE_BF16, R, 2 * h, b->offsets, E, aq, as, b0q,
                                                   b0s, s)
                     : mxfp8_quantize_launch(b->dab, MOE_BF16, R, 2 * h, 0, b->offsets, E,
                                             nullptr, b0q, b0s, s)) != MOE_OK)
         return st;
     if (R > 0) {
         // GEMM1 dgrad: dAB . W1t
-        g.mode = MOE_GG_DGRAD; g.M = 0; g.N = d; g.K = 2 * h;
+        g.mode = MOE_GG_DGRAD; g.accumulate = 0; g.M = 0; g.N = d; g.K = 2 * h;
         g.A = aq; g.a_scale = as; g.B = b->w1t; g.b_scale = b->w1t_scale; g.C = b->dx_perm;
         if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
     }
@@ -339,7 +344,7 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
     if ((st = mxfp8_quantize_launch(b->x, MOE_BF16, R, d, 0, b->offsets, E, b->sorted_token, b1q,
                                     b1s, s)) != MOE_OK)
         return st;
-    g.mode = MOE_GG_WGRAD; g.M = 2 * h; g.N = d; g.K = 0;
+    g.mode = MOE_GG_WGRAD; g.accumulate = b->accumulate_dw; g.M = 2 * h; g.N = d; g.K = 0;
     g.A = b0q; g.a_scale = b0s; g.B = b1q; g.b_scale = b1s; g.C = b->dw1;
     if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
     // unpermute backward
@@ -348,6 +353,22 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
 }
 
 size_t mxfp8_col_blocks(int64_t rows, int32_t n_groups) { return moe::mxfp8_col_blocks(rows, n_groups); }
+
+moe_status mxfp8_quantize_both(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
+                               const int32_t *group_offsets, int32_t n_groups, uint8_t *q_rows,
+                               uint8_t *s_rows, uint8_t *q_cols, uint8_t *s_cols, void *stream) {
+    if (in_dt != MOE_F32 && in_dt != MOE_BF16) return MOE_ERR_DTYPE;
+    if (rows < 0 || cols < 32 || cols % 32 || rows >= ((int64_t)1 << 31) ||
+        cols >= ((int64_t)1 << 20))
+        return MOE_ERR_SHAPE;
+    if (group_offsets && (n_groups < 1 || n_groups > 1024)) return MOE_ERR_SHAPE;
+    if (rows == 0) return MOE_OK;
+    if (!in || !q_rows || !s_rows || !q_cols || !s_cols) return MOE_ERR_NULL;
+    if (!aligned16(in) || !aligned16(q_rows) || !aligned16(q_cols)) return MOE_ERR_ALIGN;
+    return mxfp8_quantize_both_launch(in, in_dt, rows, cols, group_offsets,
+                                      group_offsets ? n_groups : 1, q_rows, s_rows, q_cols, s_cols,
+                                      (hipStream_t)stream);
+}
 
 moe_status moe_capacity_pad(const int32_t *topk_idx, const int32_t *token_pos,
                             const int32_t *offsets, int64_t T, int32_t E, int32_t k,

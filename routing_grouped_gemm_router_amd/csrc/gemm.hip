@@ -46,6 +46,7 @@ struct GemmArgs {
     int M, N, K;
     int E;
     int h;          // hidden width (SwiGLU epilogues)
+    int accumulate; // WGRAD: add to C instead of overwriting it
 };
 
 // ---------------------------------------------------------------------------
@@ -862,7 +863,11 @@ void gg_mfma(GemmArgs g) {
         const bool has_next = npos < total;
         TileC nxt = cur;
         if constexpr (DIRECT_EPI) {
-            if (has_next) {
+            // An accumulating weight gradient reads C in its epilogue; those
+            // reads go out before the next tile's copies, which they would
+            // otherwise wait behind (vector-memory loads return in issue order).
+            const bool epi_first = MODE == MOE_GG_WGRAD && g.accumulate;
+            if (has_next && !epi_first) {
                 nxt = decode(npos);
                 setup(nxt);
                 lds_sync();                       // every wave is done with this tile's stages
@@ -878,10 +883,25 @@ void gg_mfma(GemmArgs g) {
 #pragma unroll
                     for (int j = 0; j < TN; j++) {
                         const int n = cur.n0 + wn * WTN + j * 32 + col_l;
+                        if (epi_first) {
+                            // C += the tile, one fp32 add per element
+                            float old[16];
 #pragma unroll
-                        for (int v = 0; v < 16; v++) {
-                            const int m = cur.m0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-                            if (m < g.M && n < g.N) store_f32(C + (int64_t)m * g.N + n, acc[i][j][v]);
+                            for (int v = 0; v < 16; v++) {
+                                const int m = cur.m0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                                old[v] = (m < g.M && n < g.N) ? C[(int64_t)m * g.N + n] : 0.f;
+                            }
+#pragma unroll
+                            for (int v = 0; v < 16; v++) {
+                                const int m = cur.m0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                                if (m < g.M && n < g.N) store_f32(C + (int64_t)m * g.N + n, old[v] + acc[i][j][v]);
+                            }
+                        } else {
+#pragma unroll
+                            for (int v = 0; v < 16; v++) {
+                                const int m = cur.m0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                                if (m < g.M && n < g.N) store_f32(C + (int64_t)m * g.N + n, acc[i][j][v]);
+                            }
                         }
                     }
             } else if constexpr (EPI == MOE_EPI_SWIGLU_FWD) {
@@ -919,6 +939,12 @@ void gg_mfma(GemmArgs g) {
                                 C[(int64_t)grow * g.N + n] = f32_to_bf16(acc[i][j][v]);
                         }
                     }
+            }
+            if (has_next && epi_first) {
+                nxt = decode(npos);
+                setup(nxt);
+                lds_sync();
+                prologue(nxt);
             }
         } else {
             // ---- epilogue. acc[i][j][v] holds row (v/4)*8 + (lane/32)*4 + v%4 and
@@ -1159,7 +1185,7 @@ __global__ __launch_bounds__(256) void gg_f32(GemmArgs g) {
 #pragma unroll
                 for (int j = 0; j < 4; j++) {
                     const int bc = bcol(cols[j]);
-                    if (bc >= 0) C[bc] = acc[i][j];
+                    if (bc >= 0) C[bc] = g.accumulate ? C[bc] + acc[i][j] : acc[i][j];
                 }
             } else {
                 const int r = row0 + ml;
@@ -1276,6 +1302,7 @@ moe_status gemm_launch(const moe_gemm_desc *d, hipStream_t s) {
     a.a_scale = d->a_scale; a.b_scale = d->b_scale;
     a.E = d->n_groups;
     a.h = d->epilogue == MOE_EPI_SWIGLU_FWD ? d->N / 2 : d->N;
+    a.accumulate = d->accumulate;
 #define GO(MODE, EPI)                                                          \
     (d->dtype == MOE_BF16    ? launch_mfma<MODE, EPI, false>(a, s)             \
      : d->dtype == MOE_MXFP8 ? launch_mfma<MODE, EPI, true>(a, s)              \

@@ -194,17 +194,26 @@ MOE_DEV uint32_t encode_block32(const float *f, uint8_t *dst) {
     return sb;
 }
 
-// axis 0, fp32 input (weights; once per weight update): one workgroup per
-// (unit, 64 columns). The 128 x 64 tile is read with 16-B row loads,
-// transposed through LDS, and each thread encodes one 32-row block of one
-// column; 4 neighbouring threads write the column's 128 contiguous bytes.
+// axis 0, fp32 input (weights; once per weight update). Persistent over
+// units like the bf16 kernel below: a workgroup owns 64 columns and walks
+// units blockIdx.y, blockIdx.y + gridDim.y, ...; the next unit's 32 KiB tile
+// is loaded into registers while the current one is encoded. The 128 x 64
+// tile is read with 16-B row loads, transposed through LDS, and each thread
+// encodes one 32-row block of one column; 4 neighbouring threads write the
+// column's 128 contiguous bytes.
+// BOTH: the loaded rows are also quantised along the columns into the
+// row-major axis-1 layout (q1, s1): a 32-column block is 8 neighbouring
+// lanes of one row, so the fp32 masters are read once for both orientations.
+template <bool BOTH>
 __global__ __launch_bounds__(256) void mx_quant_cols_f32(const float *__restrict__ in, int64_t rows,
                                                          int64_t cols,
                                                          const int32_t *__restrict__ group_offsets,
                                                          int n_groups,
                                                          const int32_t *__restrict__ row_map,
                                                          uint8_t *__restrict__ q,
-                                                         uint8_t *__restrict__ scale) {
+                                                         uint8_t *__restrict__ scale,
+                                                         uint8_t *__restrict__ q1,
+                                                         uint8_t *__restrict__ s1) {
     constexpr int TP = 129;               // LDS pitch (floats) of one column: conflict-free writes
     __shared__ float s_t[64 * TP];
     __shared__ ColUnits cu;
@@ -212,33 +221,68 @@ __global__ __launch_bounds__(256) void mx_quant_cols_f32(const float *__restrict
     const int ng = group_offsets ? n_groups : 1;
     const int n_units = col_units_init(cu, group_offsets, ng, rows);
     const int64_t c0 = (int64_t)blockIdx.x * 64;
-    for (int unit = blockIdx.y; unit < n_units; unit += gridDim.y) {   // uniform over the workgroup
-        const UnitGeom u = unit_geom(cu, ng, unit);
-        const int ch = tid & 15, rr = tid >> 4;   // 4 columns per load, 16 loads per row
-        const bool cok = c0 + 4 * ch < cols;
+    const int ch = tid & 15, rr = tid >> 4;   // 4 columns per load, 16 loads per row
+    const bool cok = c0 + 4 * ch < cols;
+
+    float4 v[8];                          // rows rr + 16 p
+    auto load = [&](const UnitGeom &u) {
 #pragma unroll
         for (int p = 0; p < 8; p++) {
             const int r = rr + 16 * p;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            v[p] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (r < u.n && cok) {
                 const int64_t src = row_map ? (int64_t)row_map[u.r0 + r] : u.r0 + r;
-                v = *reinterpret_cast<const float4 *>(in + src * cols + c0 + 4 * ch);
+                v[p] = *reinterpret_cast<const float4 *>(in + src * cols + c0 + 4 * ch);
             }
-            s_t[(4 * ch) * TP + r] = v.x;
-            s_t[(4 * ch + 1) * TP + r] = v.y;
-            s_t[(4 * ch + 2) * TP + r] = v.z;
-            s_t[(4 * ch + 3) * TP + r] = v.w;
+        }
+    };
+    int unit = blockIdx.y;
+    if (unit >= n_units) return;          // uniform over the workgroup
+    UnitGeom u = unit_geom(cu, ng, unit);
+    load(u);
+    while (true) {
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            const int r = rr + 16 * p;
+            s_t[(4 * ch) * TP + r] = v[p].x;
+            s_t[(4 * ch + 1) * TP + r] = v[p].y;
+            s_t[(4 * ch + 2) * TP + r] = v[p].z;
+            s_t[(4 * ch + 3) * TP + r] = v[p].w;
+            if constexpr (BOTH) {
+                float am = fmaxf(fmaxf(fabsf(v[p].x), fabsf(v[p].y)), fmaxf(fabsf(v[p].z), fabsf(v[p].w)));
+                am = fmaxf(am, __shfl_xor(am, 1, 64));
+                am = fmaxf(am, __shfl_xor(am, 2, 64));
+                am = fmaxf(am, __shfl_xor(am, 4, 64));
+                if (r < u.n && cok) {
+                    const uint32_t sb = mx_scale_byte(am);
+                    const int sh = 127 - (int)sb;
+                    const uint32_t w = e4m3_rne_sat(ldexpf(v[p].x, sh)) |
+                                       (e4m3_rne_sat(ldexpf(v[p].y, sh)) << 8) |
+                                       (e4m3_rne_sat(ldexpf(v[p].z, sh)) << 16) |
+                                       (e4m3_rne_sat(ldexpf(v[p].w, sh)) << 24);
+                    *reinterpret_cast<uint32_t *>(q1 + (u.r0 + r) * cols + c0 + 4 * ch) = w;
+                    if ((ch & 7) == 0) s1[(u.r0 + r) * (cols / 32) + (c0 + 4 * ch) / 32] = (uint8_t)sb;
+                }
+            }
         }
         __syncthreads();
+        const UnitGeom cur = u;
+        const int next = unit + gridDim.y;
+        if (next < n_units) {             // prefetch the next tile while this one is encoded
+            u = unit_geom(cu, ng, next);
+            load(u);
+        }
         const int cc = tid >> 2, b = tid & 3;
         const int64_t c = c0 + cc;
         if (c < cols) {
             float f[32];
 #pragma unroll
             for (int i = 0; i < 32; i++) f[i] = s_t[cc * TP + 32 * b + i];
-            const uint32_t sb = encode_block32(f, q + u.bb * 32 * cols + c * u.nb * 32 + 128 * (int64_t)u.j + 32 * b);
-            scale[u.bb * cols + c * u.nb + 4 * u.j + b] = (uint8_t)sb;
+            const uint32_t sb = encode_block32(f, q + cur.bb * 32 * cols + c * cur.nb * 32 + 128 * (int64_t)cur.j + 32 * b);
+            scale[cur.bb * cols + c * cur.nb + 4 * cur.j + b] = (uint8_t)sb;
         }
+        if (next >= n_units) break;
+        unit = next;
         __syncthreads();                  // s_t is rewritten by the next unit
     }
 }
@@ -361,6 +405,7 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
 #define MOE_COLS_PER_CU 8
 #endif
 constexpr int kColsPerCU = MOE_COLS_PER_CU;
+constexpr int kColsPerCUF32 = 4;          // the fp32 tile's 33 KiB of LDS: four workgroups per CU
 
 // column tiles along x; units (upper bound sum_g ceil(len_g/128) <= rows/128 + groups) along
 // y, `per_cu` workgroups per CU in all when the kernel walks several units
@@ -392,19 +437,26 @@ moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, 
                 (const uint16_t *)in, rows, cols, group_offsets, n_groups, row_map, q, scale,
                 nullptr, nullptr);
         else
-            mx_quant_cols_f32<<<cols_grid(rows, cols, ng, 0), 256, 0, s>>>(
-                (const float *)in, rows, cols, group_offsets, n_groups, row_map, q, scale);
+            mx_quant_cols_f32<false><<<cols_grid(rows, cols, ng, kColsPerCUF32), 256, 0, s>>>(
+                (const float *)in, rows, cols, group_offsets, n_groups, row_map, q, scale, nullptr,
+                nullptr);
     }
     return launch_status();
 }
 
-// bf16 [rows, cols] in grouped row order -> both the row-major axis-1 layout
-// (q1, s1) and the grouped column-block layout (q0, s0), from one read.
-moe_status mxfp8_quantize_both_launch(const void *in, int64_t rows, int64_t cols,
+// bf16 or fp32 [rows, cols] in grouped row order -> both the row-major
+// axis-1 layout (q1, s1) and the grouped column-block layout (q0, s0), from
+// one read.
+moe_status mxfp8_quantize_both_launch(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
                                       const int32_t *group_offsets, int n_groups, uint8_t *q1,
                                       uint8_t *s1, uint8_t *q0, uint8_t *s0, hipStream_t s) {
-    mx_quant_cols_bf16<true><<<cols_grid(rows, cols, n_groups, kColsPerCU), 256, 0, s>>>(
-        (const uint16_t *)in, rows, cols, group_offsets, n_groups, nullptr, q0, s0, q1, s1);
+    const int ng = group_offsets ? n_groups : 1;
+    if (in_dt == MOE_BF16)
+        mx_quant_cols_bf16<true><<<cols_grid(rows, cols, ng, kColsPerCU), 256, 0, s>>>(
+            (const uint16_t *)in, rows, cols, group_offsets, n_groups, nullptr, q0, s0, q1, s1);
+    else
+        mx_quant_cols_f32<true><<<cols_grid(rows, cols, ng, kColsPerCUF32), 256, 0, s>>>(
+            (const float *)in, rows, cols, group_offsets, n_groups, nullptr, q0, s0, q1, s1);
     return launch_status();
 }
 

@@ -187,3 +187,31 @@ def test_load_balance_validation(lib):
     assert lib.moe_load_balance(fake, fake, 16, 8, 2, 1.0, fake, fake + 1, fake, big, None) == 4
     assert lib.moe_load_balance(fake, fake, 16, 8, 2, 1.0, fake, None, fake + 4, big, None) == 4
     assert lib.moe_load_balance(fake, fake, 100, 8, 2, 1.0, fake, None, fake, 4, None) == 5     # ws size
+
+
+def test_accumulate_and_quantize_both_validation(lib):
+    import sys
+    sys.path.insert(0, ROOT)
+    from routing_grouped_gemm_router_amd import GemmDesc, BwdDesc
+    lib.moe_grouped_gemm.argtypes = [ctypes.POINTER(GemmDesc), ctypes.c_void_p]
+    g = GemmDesc()
+    g.mode, g.dtype, g.epilogue, g.n_groups, g.rows = 0, 1, 0, 8, 64
+    g.N, g.K = 64, 64
+    g.offsets = g.A = g.B = g.C = 0x100000
+    g.accumulate = 1                               # accumulate is for WGRAD only
+    assert lib.moe_grouped_gemm(ctypes.byref(g), None) == 3
+    g.mode, g.M, g.N, g.accumulate = 2, 64, 64, 2  # and takes 0 or 1
+    assert lib.moe_grouped_gemm(ctypes.byref(g), None) == 3
+    lib.moe_backward.argtypes = [ctypes.POINTER(BwdDesc), ctypes.c_void_p]
+    b = BwdDesc()
+    b.dtype, b.d, b.h, b.E, b.k, b.T, b.accumulate_dw = 1, 64, 64, 8, 2, 16, 3
+    assert lib.moe_backward(ctypes.byref(b), None) == 3
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.mxfp8_quantize_both.argtypes = [P, I32, I64, I64, P, I32, P, P, P, P, P]
+    f = 0x100000
+    assert lib.mxfp8_quantize_both(f, 2, 64, 64, None, 0, f, f, f, f, None) == 3     # dtype
+    assert lib.mxfp8_quantize_both(f, 0, 64, 48, None, 0, f, f, f, f, None) == 2     # cols % 32
+    assert lib.mxfp8_quantize_both(f, 0, 64, 64, f, 0, f, f, f, f, None) == 2        # n_groups
+    assert lib.mxfp8_quantize_both(f, 0, 64, 64, None, 0, f, None, f, f, None) == 1
+    assert lib.mxfp8_quantize_both(f + 4, 0, 64, 64, None, 0, f, f, f, f, None) == 4
+    assert lib.mxfp8_quantize_both(None, 0, 0, 64, None, 0, None, None, None, None, None) == 0
