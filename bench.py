@@ -49,6 +49,9 @@ def parse():
                     help="skip the padded-capacity comparison (bf16 fwd+bwd workloads)")
     ap.add_argument("--no-recompute", action="store_true",
                     help="skip the recompute variant (GEMM1 rerun in the backward)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed step: skip the padded, recompute, load-balance, "
+                         "accumulation and re-quantisation sections (for profiling runs)")
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens in the oracle's bounded sample")
     ap.add_argument("--breakdown", action="store_true",
@@ -145,14 +148,17 @@ def main():
     flops = w.fwd_bwd_flops() if w.backward else w.fwd_flops()
     peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
 
+    if a.no_extras:
+        a.no_padded = a.no_recompute = True
     padded = None
     if not mx and w.backward and not a.no_padded:
         padded = padded_baseline(moe, torch, inp, w, a.steps, a.warmup)
         padded["dropless_speedup"] = padded["ms_per_step"] / ms
-    balance = load_balance_report(moe, torch, inp, layer, w)
+    extras = not a.no_extras
+    balance = load_balance_report(moe, torch, inp, layer, w) if extras else None
     accum = grad_accumulation(moe, torch, layer, x, logits, dout, w, a.steps, ms) \
-        if w.backward else None
-    requant = weight_requant(moe, torch, inp, layer, w) if mx else None
+        if w.backward and extras else None
+    requant = weight_requant(moe, torch, inp, layer, w) if mx and extras else None
     recompute = None
     if w.backward and not a.no_recompute:
         recompute = recompute_variant(moe, torch, inp, w, a.steps, a.warmup)
@@ -215,7 +221,8 @@ def main():
         res["padded_baseline"] = padded
     if recompute is not None:
         res["recompute"] = recompute
-    res["load_balance"] = balance
+    if balance is not None:
+        res["load_balance"] = balance
     if accum is not None:
         res["grad_accumulation"] = accum
     if requant is not None:

@@ -8,13 +8,17 @@
 // [-127, 127]; elements x * 2^-shared rounded to nearest even E4M3 (bias 7,
 // no infinities) and saturated to +-448.
 //
-// Both the scale and the element encodings are done with integer operations
-// on the fp32 bit pattern:
+// The scale is taken from the fp32 bit pattern:
 //   scale byte = max(biased fp32 exponent of amax - 8, 0)   (zero and fp32
 //                subnormal amax give byte 0, i.e. 2^-127)
-//   element    = fp32 mantissa rounded from 23 to 3 bits (ties to even) and
-//                exponent rebased from bias 127 to 7 in the normal range;
-//                rint(|v| * 2^9) in the subnormal range (|v| < 2^-6).
+// The elements x * 2^-shared are encoded by the CDNA4 conversion instruction
+// (v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even) on inputs clamped to
+// +-448, which is the saturation; its only departure from the format is a
+// NaN, which it writes as 0xff whatever the sign, so a positive NaN is
+// patched to 0x7f. Checked on the GPU against an integer encoding of the
+// format (mantissa rounded from 23 to 3 bits ties to even, exponent rebased
+// from 127 to 7; rint(|v| * 2^9) below 2^-6) on all 2^32 fp32 patterns:
+// identical except NaN's sign, which the patch restores.
 // The kernels are HBM-bound: one read of the input, one write of the bytes.
 #include "common.h"
 
@@ -25,20 +29,19 @@ MOE_DEV uint32_t mx_scale_byte(float amax) {
     return (uint32_t)max(ef - 8, 0);
 }
 
-// v already multiplied by 2^-shared
-MOE_DEV uint32_t e4m3_rne_sat(float v) {
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    if (a > 0x7f800000u) return sign | 0x7fu;          // NaN
-    if (a >= 0x43e00000u) return sign | 0x7eu;         // >= 448 (and inf): saturate
-    if (a >= 0x3c800000u) {                            // >= 2^-6: normal E4M3
-        uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);  // round 20 bits off, ties to even
-        r >>= 20;                                      // [fp32 exponent | 3-bit mantissa]
-        return sign | (r - (120u << 3));               // rebias 127 -> 7
+// four elements, scaled by 2^sh, to four E4M3 bytes (first element lowest)
+MOE_DEV uint32_t e4m3x4(float a, float b, float c, float d, int sh) {
+    const float v[4] = {ldexpf(a, sh), ldexpf(b, sh), ldexpf(c, sh), ldexpf(d, sh)};
+    float cl[4];
+    uint32_t pnan = 0;                                  // positive NaNs: 0xff -> 0x7f
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        cl[i] = fabsf(v[i]) > 448.0f ? copysignf(448.0f, v[i]) : v[i];
+        pnan |= ((int32_t)__float_as_uint(v[i]) > 0x7f800000) ? 0x80u << (8 * i) : 0u;
     }
-    const float m = rintf(__uint_as_float(a) * 512.0f);   // subnormal: m * 2^-9, m in 0..8
-    return sign | (uint32_t)m;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl[0], cl[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(cl[2], cl[3], w, true);
+    return (uint32_t)w ^ pnan;
 }
 
 template <bool BF16>
@@ -92,11 +95,7 @@ __global__ __launch_bounds__(256) void mx_quant_rows(const void *__restrict__ in
     const int sh = 127 - (int)sb;
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        w[i] = 0;
-#pragma unroll
-        for (int j = 0; j < 4; j++) w[i] |= e4m3_rne_sat(ldexpf(f[4 * i + j], sh)) << (8 * j);
-    }
+    for (int i = 0; i < 4; i++) w[i] = e4m3x4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], sh);
     reinterpret_cast<uint4 *>(q)[gid] = make_uint4(w[0], w[1], w[2], w[3]);
     if ((threadIdx.x & 1) == 0) scale[blk] = (uint8_t)sb;
 }
@@ -183,11 +182,7 @@ MOE_DEV uint32_t encode_block32(const float *f, uint8_t *dst) {
     const int sh = 127 - (int)sb;
     uint32_t w[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        w[i] = 0;
-#pragma unroll
-        for (int e = 0; e < 4; e++) w[i] |= e4m3_rne_sat(ldexpf(f[4 * i + e], sh)) << (8 * e);
-    }
+    for (int i = 0; i < 8; i++) w[i] = e4m3x4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], sh);
     uint4 *d = reinterpret_cast<uint4 *>(dst);
     d[0] = make_uint4(w[0], w[1], w[2], w[3]);
     d[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -256,10 +251,7 @@ __global__ __launch_bounds__(256) void mx_quant_cols_f32(const float *__restrict
                 if (r < u.n && cok) {
                     const uint32_t sb = mx_scale_byte(am);
                     const int sh = 127 - (int)sb;
-                    const uint32_t w = e4m3_rne_sat(ldexpf(v[p].x, sh)) |
-                                       (e4m3_rne_sat(ldexpf(v[p].y, sh)) << 8) |
-                                       (e4m3_rne_sat(ldexpf(v[p].z, sh)) << 16) |
-                                       (e4m3_rne_sat(ldexpf(v[p].w, sh)) << 24);
+                    const uint32_t w = e4m3x4(v[p].x, v[p].y, v[p].z, v[p].w, sh);
                     *reinterpret_cast<uint32_t *>(q1 + (u.r0 + r) * cols + c0 + 4 * ch) = w;
                     if ((ch & 7) == 0) s1[(u.r0 + r) * (cols / 32) + (c0 + 4 * ch) / 32] = (uint8_t)sb;
                 }
@@ -364,12 +356,8 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
                 if (r < u.n && cok) {
                     const uint32_t sb = mx_scale_byte(am);
                     const int sh = 127 - (int)sb;
-                    uint32_t lo4 = 0, hi4 = 0;
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        lo4 |= e4m3_rne_sat(ldexpf(f[e], sh)) << (8 * e);
-                        hi4 |= e4m3_rne_sat(ldexpf(f[e + 4], sh)) << (8 * e);
-                    }
+                    const uint32_t lo4 = e4m3x4(f[0], f[1], f[2], f[3], sh);
+                    const uint32_t hi4 = e4m3x4(f[4], f[5], f[6], f[7], sh);
                     *reinterpret_cast<uint2 *>(q1 + (u.r0 + r) * cols + c0 + 8 * ch) = make_uint2(lo4, hi4);
                     if ((ch & 3) == 0) s1[(u.r0 + r) * (cols / 32) + (c0 + 8 * ch) / 32] = (uint8_t)sb;
                 }
