@@ -17,6 +17,18 @@ namespace moe {
 constexpr int kRowWaves = 4;
 constexpr int kUnroll = 4;   // combine kernels: 16-byte column chunks per lane in flight together
 
+// Non-temporal 16-byte loads of rows read exactly once (the combine kernels'
+// gathered rows, the combine backward's dOut): measured in the layer step at
+// T=16384, d=2048, k=4 bf16, combine 64 -> 58 us and the unpermute backward
+// 72 -> 67 us. Stores stay ordinary: the next kernel reads x_perm and dy_perm
+// while they are still in the last-level cache (non-temporal stores made the
+// dispatch 53 -> 65 us and the GEMMs reading its output ~4 % slower).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+MOE_DEV uint4 ld16_nt(const uint4 *p) {
+    const u32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(w.x, w.y, w.z, w.w);
+}
+
 // ---------------------------------------------------------------------------
 // dispatch: x_perm[token_pos[t, j]] = x[t]
 
@@ -120,7 +132,7 @@ __global__ __launch_bounds__(256) void combine_rows(const uint4 *__restrict__ y,
             const int c = c0 + 64 * u;
 #pragma unroll
             for (int j = 0; j < KMAX; j++)
-                if (c < n16 && pos[j] >= 0) v[u][j] = y[(int64_t)pos[j] * n16 + c];
+                if (c < n16 && pos[j] >= 0) v[u][j] = ld16_nt(y + (int64_t)pos[j] * n16 + c);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
@@ -171,10 +183,10 @@ __global__ __launch_bounds__(256) void combine_bwd_rows(
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
             const int c = c0 + 64 * u;
-            if (c < n16) vo[u] = dout[t * n16 + c];
+            if (c < n16) vo[u] = ld16_nt(dout + t * n16 + c);
 #pragma unroll
             for (int j = 0; j < KMAX; j++)
-                if (c < n16 && pos[j] >= 0) v[u][j] = y[(int64_t)pos[j] * n16 + c];
+                if (c < n16 && pos[j] >= 0) v[u][j] = ld16_nt(y + (int64_t)pos[j] * n16 + c);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
