@@ -432,7 +432,10 @@ struct DmaTile {
 // FP8: operands are MXFP8 (E4M3 bytes, K-contiguous in every mode) and each
 // stage also holds the E8M0 scale words (4 blocks = one 128-byte step) of its
 // A rows and B rows, copied with one 4-byte LDS-DMA per wave.
-template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int WPE>
+// ACC (WGRAD only): C += the product instead of C = (a separate
+// instantiation, so the overwriting kernel carries none of its code)
+template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int STAGES, int WPE,
+          bool ACC = false>
 __global__ __launch_bounds__(WM *WN * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void gg_mfma(GemmArgs g) {
     constexpr int NW = WM * WN;
@@ -866,8 +869,8 @@ void gg_mfma(GemmArgs g) {
             // An accumulating weight gradient reads C in its epilogue; those
             // reads go out before the next tile's copies, which they would
             // otherwise wait behind (vector-memory loads return in issue order).
-            const bool epi_first = MODE == MOE_GG_WGRAD && g.accumulate;
-            if (has_next && !epi_first) {
+            constexpr bool epi_first = MODE == MOE_GG_WGRAD && ACC;
+            if (!epi_first && has_next) {
                 nxt = decode(npos);
                 setup(nxt);
                 lds_sync();                       // every wave is done with this tile's stages
@@ -883,7 +886,7 @@ void gg_mfma(GemmArgs g) {
 #pragma unroll
                     for (int j = 0; j < TN; j++) {
                         const int n = cur.n0 + wn * WTN + j * 32 + col_l;
-                        if (epi_first) {
+                        if constexpr (epi_first) {
                             // C += the tile, one fp32 add per element
                             float old[16];
 #pragma unroll
@@ -940,7 +943,7 @@ void gg_mfma(GemmArgs g) {
                         }
                     }
             }
-            if (has_next && epi_first) {
+            if (epi_first && has_next) {
                 nxt = decode(npos);
                 setup(nxt);
                 lds_sync();
@@ -1280,8 +1283,12 @@ template <int MODE, int EPI, bool FP8>
 static void launch_mfma(const GemmArgs &a, hipStream_t s) {
     if constexpr (MODE == MOE_GG_WGRAD) {
         const int grid = (num_cus() * MOE_WG_OCC + 7) / 8 * 8;
-        gg_mfma<MODE, EPI, FP8, MOE_WG_BM, MOE_WG_BN, MOE_WG_WM, MOE_WG_WN, MOE_WG_STAGES,
-                MOE_WG_WPE><<<grid, MOE_WG_WM * MOE_WG_WN * 64, 0, s>>>(a);
+        if (a.accumulate)
+            gg_mfma<MODE, EPI, FP8, MOE_WG_BM, MOE_WG_BN, MOE_WG_WM, MOE_WG_WN, MOE_WG_STAGES,
+                    MOE_WG_WPE, true><<<grid, MOE_WG_WM * MOE_WG_WN * 64, 0, s>>>(a);
+        else
+            gg_mfma<MODE, EPI, FP8, MOE_WG_BM, MOE_WG_BN, MOE_WG_WM, MOE_WG_WN, MOE_WG_STAGES,
+                    MOE_WG_WPE><<<grid, MOE_WG_WM * MOE_WG_WN * 64, 0, s>>>(a);
     } else {
         const int grid = (num_cus() * MOE_ROW_OCC + 7) / 8 * 8;
         gg_mfma<MODE, EPI, FP8, MOE_ROW_BM, MOE_ROW_BN, MOE_ROW_WM, MOE_ROW_WN, MOE_ROW_STAGES,
