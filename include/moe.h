@@ -176,7 +176,9 @@ enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU_FWD = 1, MOE_EPI_SWIGLU_BWD = 2 };
  *     groups = offsets): A holds the [rows, M] operand, B the [rows, N]
  *     operand; C [E, M, N] fp32. Their scale arrays must be sized by
  *     mxfp8_col_blocks (the kernel may read up to 12 bytes past the last
- *     used scale byte, into the spare blocks).
+ *     used scale byte, into the spare blocks). rows <= 2^25 (MOE_ERR_SHAPE
+ *     otherwise): the kernel addresses 128 rows of one group's column block
+ *     with 32-bit offsets.
  * (aux_out_scale is reserved and must be null.)
  */
 typedef struct moe_gemm_desc {

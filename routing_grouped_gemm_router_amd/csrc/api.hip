@@ -165,6 +165,9 @@ static moe_status check_gemm(const moe_gemm_desc *g) {
     if (g->dtype == MOE_MXFP8) {
         if (g->aux_out_scale) return MOE_ERR_DTYPE;
         if (g->mode != MOE_GG_WGRAD && g->K % 128) return MOE_ERR_SHAPE;
+        // WGRAD: 128 rows of a group's column block (pitch <= rows + 127
+        // bytes) are addressed with 32-bit offsets
+        if (g->mode == MOE_GG_WGRAD && g->rows > ((int64_t)1 << 25)) return MOE_ERR_SHAPE;
         if (!g->a_scale || !g->b_scale) return MOE_ERR_NULL;
         if (!aligned4(g->a_scale) || !aligned4(g->b_scale)) return MOE_ERR_ALIGN;
     }

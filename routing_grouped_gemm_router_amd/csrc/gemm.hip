@@ -335,6 +335,28 @@ MOE_DEV void dma4(const void *src, const void *lds_wave_base) {
                  : "memory", "m0");
 }
 
+// The same copy with the address split into a wave-uniform base in SGPRs
+// and a 32-bit per-lane offset: advancing a whole tile by one K step is then
+// a scalar add, with no per-lane address arithmetic.
+MOE_DEV void dma16s(uint32_t voff, const char *sbase, const void *lds_wave_base) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const MOE_LDS void *)lds_wave_base);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(m0v)
+                 : "memory", "m0");
+}
+
+// a pointer that is equal in every lane, moved into scalar registers (the
+// builtin returns a signed int: each half is widened from uint32_t, or a low
+// word with bit 31 set would be sign-extended over the high word)
+MOE_DEV const char *uniform_ptr(const char *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const char *>((uintptr_t)((hi << 32) | lo));
+}
+
 // One operand tile per stage, copied HBM -> LDS by global_load_lds_dwordx4:
 // every instruction writes 64 lanes x 16 bytes to a contiguous 1 KiB of LDS,
 // so each lane picks the global chunk that belongs at its LDS position.
@@ -342,52 +364,72 @@ MOE_DEV void dma4(const void *src, const void *lds_wave_base) {
 //
 // KL = true : K-layout tile [R rows][128 bytes]; src rows are K-contiguous.
 // KL = false: MN-layout tile [64 k][R cols] bf16; src is [k][ld], cols contiguous.
+//
+// Rows past the operand's end (KL) and columns past it (MN) are read from the
+// last valid row / column instead: they meet only output rows or columns
+// that the epilogue does not store. K past the reduction's end is different
+// (it would add to valid outputs): a step that reaches past klim takes zeros
+// for those chunks.
 template <int R, bool KL, int NW>
 struct DmaTile {
     static constexpr int CHUNKS = R * 8;
     static constexpr int IPW = CHUNKS / 64 / NW;
+    static constexpr int STEP = KL ? kStepBytes : 64;   // K per step: bytes (KL) or rows (MN)
     static_assert(IPW >= 1 && CHUNKS % (64 * NW) == 0, "tile/wave mismatch");
     static_assert(KL || R >= 128, "MN-layout swizzle needs >= 16 chunks per row");
-    // per lane and instruction: source of step 0 (nullptr = always zero) and
-    // the chunk's K position (KL: byte offset in the step; MN: k row)
-    const char *src[IPW];
-    int kofs[IPW];
-    int64_t kstride;        // bytes to advance per step
+    const char *base;          // tile origin at step 0 (wave-uniform)
+    int64_t kstride;           // bytes to advance per step
+    uint32_t voff[IPW];        // per lane and instruction: byte offset of its chunk
 
-    // KL: row_ptr(r) -> address of byte 0 of tile row r's K run, or nullptr
+    // chunk position of lane `lane`'s instruction i: (row, 16-byte column)
+    MOE_DEV static int pos(int i, int wave, int lane) { return (wave * IPW + i) * 64 + lane; }
+    // the chunk's K position: byte offset in the step (KL) or k row (MN)
+    MOE_DEV static int kpos(int i, int wave, int lane) {
+        const int p = pos(i, wave, lane);
+        if constexpr (KL) return ((p & 7) ^ kl_swz(p >> 3)) * 16;
+        else return p / (R / 8);
+    }
+
+    // KL: row_off(r) -> byte offset from b of tile row r's K run (< 2^32)
     template <typename RowFn>
-    MOE_DEV void setup_kl(RowFn row_ptr, int wave, int lane) {
+    MOE_DEV void setup_kl(const char *b, RowFn row_off, int wave, int lane) {
+        base = uniform_ptr(b);
 #pragma unroll
         for (int i = 0; i < IPW; i++) {
-            const int p = (wave * IPW + i) * 64 + lane;
+            const int p = pos(i, wave, lane);
             const int row = p >> 3, kc = (p & 7) ^ kl_swz(row);
-            const char *rp = row_ptr(row);
-            src[i] = rp ? rp + kc * 16 : nullptr;
-            kofs[i] = kc * 16;
+            voff[i] = row_off(row) + (uint32_t)(kc * 16);
         }
         kstride = kStepBytes;
     }
-    // MN: base = element (k = 0, col 0) of the tile, ld = row pitch in bytes,
-    // cvalid = valid columns
-    MOE_DEV void setup_mn(const char *base, int64_t ld, int cvalid, int wave, int lane) {
+    // MN: b = element (k = 0, col 0) of the tile, ld = row pitch in bytes,
+    // cvalid = valid columns (>= 1)
+    MOE_DEV void setup_mn(const char *b, int64_t ld, int cvalid, int wave, int lane) {
+        base = uniform_ptr(b);
 #pragma unroll
         for (int i = 0; i < IPW; i++) {
-            const int p = (wave * IPW + i) * 64 + lane;
+            const int p = pos(i, wave, lane);
             const int k = p / (R / 8), c = (p % (R / 8)) ^ ((k & 3) << 2);
-            src[i] = c * 8 < cvalid ? base + (int64_t)k * ld + c * 16 : nullptr;
-            kofs[i] = k;
+            const int cs = c * 8 < cvalid ? c : (cvalid - 1) >> 3;
+            voff[i] = (uint32_t)(k * ld + cs * 16);
         }
         kstride = 64 * ld;
     }
     // enqueue the copy of step kt; klim = K bytes (KL) or K rows (MN)
     MOE_DEV void issue(uint4 *lds, int kt, int klim, int wave) const {
-        const int k0 = kt * (KL ? kStepBytes : 64);
+        const int k0 = kt * STEP;
+        const char *b = base + (int64_t)kt * kstride;
+        if (k0 + STEP <= klim) {
 #pragma unroll
-        for (int i = 0; i < IPW; i++) {
-            const bool ok = src[i] != nullptr && k0 + kofs[i] < klim;
-            const void *s = ok ? (const void *)(src[i] + kt * kstride)
-                               : (const void *)&g_zero_chunk[threadIdx.x & 63];
-            dma16(s, lds + (wave * IPW + i) * 64);
+            for (int i = 0; i < IPW; i++) dma16s(voff[i], b, lds + (wave * IPW + i) * 64);
+        } else {
+            const int lane = threadIdx.x & 63;
+#pragma unroll
+            for (int i = 0; i < IPW; i++) {
+                const bool ok = k0 + kpos(i, wave, lane) < klim;
+                const void *s = ok ? (const void *)(b + voff[i]) : (const void *)&g_zero_chunk[lane];
+                dma16(s, lds + (wave * IPW + i) * 64);
+            }
         }
     }
     // bf16 MFMA operand for rows/cols r0..r0+31, k slice kk (16 wide):
@@ -594,6 +636,16 @@ void gg_mfma(GemmArgs g) {
             return r < g.N ? r : -1;
         }
     };
+    // the same with columns past the end mapped to the last valid B row
+    auto b_row_clamped = [&](const TileC &t, int n) -> int {
+        if constexpr (MODE == MOE_GG_FWD && EPI == MOE_EPI_SWIGLU_FWD) {
+            const int wc = n / WTN, off = n % WTN, half = WTN / 2;
+            const int j = min(t.nt * (BN / 2) + wc * half + (off % half), g.h - 1);
+            return off < half ? j : g.h + j;
+        } else {
+            return min(t.n0 + n, g.N - 1);
+        }
+    };
 
     // per-lane copy sources of a tile (operand chunks and FP8 scale words)
     AT ta;
@@ -602,31 +654,26 @@ void gg_mfma(GemmArgs g) {
     auto setup = [&](const TileC &t) {
         if constexpr (MODE == MOE_GG_WGRAD) {
             if constexpr (FP8) {
-                // column-block layout: expert e's A is [M][kpad] at byte sb0*128*M
-                const char *abase = A + (int64_t)t.sb0 * 128 * g.M;
-                const char *bbase = B + (int64_t)t.sb0 * 128 * g.N;
-                ta.setup_kl([&](int r) -> const char * {
-                    const int m = t.m0 + r;
-                    return m < g.M ? abase + (int64_t)m * t.kpad : nullptr;
-                }, wave, lane);
-                tb.setup_kl([&](int n) -> const char * {
-                    const int c = t.n0 + n;
-                    return c < g.N ? bbase + (int64_t)c * t.kpad : nullptr;
-                }, wave, lane);
+                // column-block layout: expert e's A is [M][kpad] at byte
+                // sb0*128*M (B likewise); offsets from the tile's first row
+                // stay below 128 * kpad < 2^32 (the host bounds the rows)
+                const uint32_t kp = (uint32_t)t.kpad;
+                ta.setup_kl(A + (int64_t)t.sb0 * 128 * g.M + (int64_t)t.m0 * t.kpad,
+                            [&](int r) { return (uint32_t)min(r, g.M - 1 - t.m0) * kp; }, wave, lane);
+                tb.setup_kl(B + (int64_t)t.sb0 * 128 * g.N + (int64_t)t.n0 * t.kpad,
+                            [&](int n) { return (uint32_t)min(n, g.N - 1 - t.n0) * kp; }, wave, lane);
             } else {
                 ta.setup_mn(A + ((int64_t)t.row0 * g.M + t.m0) * 2, (int64_t)g.M * 2, g.M - t.m0, wave, lane);
                 tb.setup_mn(B + ((int64_t)t.row0 * g.N + t.n0) * 2, (int64_t)g.N * 2, g.N - t.n0, wave, lane);
             }
         } else {
-            ta.setup_kl([&](int r) -> const char * {
-                const int gr = t.row0 + r;
-                return gr < t.row_end ? A + (int64_t)gr * g.K * ESZ : nullptr;
-            }, wave, lane);
+            const int last = t.row_end - t.row0 - 1;      // a tile has at least one row
+            const uint32_t pitch = (uint32_t)(g.K * ESZ);
+            ta.setup_kl(A + (int64_t)t.row0 * g.K * ESZ,
+                        [&](int r) { return (uint32_t)min(r, last) * pitch; }, wave, lane);
             if constexpr (B_KL) {
-                tb.setup_kl([&](int n) -> const char * {
-                    const int br = b_row_index(t, n);
-                    return br >= 0 ? B + ((int64_t)t.e * g.N + br) * g.K * ESZ : nullptr;
-                }, wave, lane);
+                tb.setup_kl(B + (int64_t)t.e * g.N * g.K * ESZ,
+                            [&](int n) { return (uint32_t)b_row_clamped(t, n) * pitch; }, wave, lane);
             } else {
                 tb.setup_mn(B + ((int64_t)t.e * g.K * g.N + t.n0) * 2, (int64_t)g.N * 2, g.N - t.n0, wave,
                             lane);

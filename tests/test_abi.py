@@ -143,6 +143,9 @@ def test_mxfp8_gemm_validation(lib):
     bad = GemmDesc.from_buffer_copy(g)
     bad.aux_out_scale = 0x100000                                     # reserved
     assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 3
+    bad = GemmDesc.from_buffer_copy(g)
+    bad.mode, bad.M, bad.N, bad.rows = 2, 64, 64, (1 << 25) + 1      # WGRAD column blocks:
+    assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 2        # 32-bit row offsets
     lib.mxfp8_col_blocks.argtypes = [ctypes.c_int64, ctypes.c_int32]
     lib.mxfp8_col_blocks.restype = ctypes.c_size_t
     assert lib.mxfp8_col_blocks(65536, 128) == 65536 // 32 + 4 * 128 + 4
