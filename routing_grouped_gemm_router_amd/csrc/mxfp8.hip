@@ -280,17 +280,19 @@ __global__ __launch_bounds__(256) void mx_quant_cols_f32(const float *__restrict
 }
 
 // axis 0, bf16 input (activations and gradients, every step). Persistent over
-// units: a workgroup owns 64 columns and walks units blockIdx.y,
-// blockIdx.y + gridDim.y, ...; the next unit's 16 KiB tile is loaded into
-// registers while the current one is encoded. Thread (ch = tid % 8,
-// rp = tid / 8) loads 8 columns of rows 2rp, 2rp+1 and 2rp+64, 2rp+65; LDS
-// holds the tile transposed as packed row pairs (dword = rows 2i, 2i+1 of one
-// column, pitch 65 dwords), conflict-free for both the writes and the
-// column-block reads. Column tiles vary fastest over the grid, so
+// units: a workgroup owns 128 columns and walks units blockIdx.y,
+// blockIdx.y + gridDim.y, ...; the next unit's 32 KiB tile is loaded into
+// registers while the current one is encoded. Sixteen lanes read a row's 256
+// bytes: thread (ch = tid % 16, q = tid / 16) loads 8 columns of rows
+// 2q + {0, 1} + 32k. LDS holds the tile transposed as packed row pairs (dword
+// = rows 2i, 2i+1 of one column, pitch 65 dwords); the column-block reads
+// are conflict-free. Column tiles vary fastest over the grid, so
 // neighbouring workgroups stream the same input rows.
 // BOTH: the tile is also quantised along its rows into the row-major axis-1
 // layout (q1, s1), row index = position in the grouped order, which saves a
-// second read of tensors needed in both orientations.
+// second read of tensors needed in both orientations. Each lane pair writes
+// 16 bytes, so a row's 128 bytes go out as one full line, and its four scale
+// bytes as one word.
 template <bool BOTH>
 __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__restrict__ in,
                                                           int64_t rows, int64_t cols,
@@ -302,20 +304,24 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
                                                           uint8_t *__restrict__ q1,
                                                           uint8_t *__restrict__ s1) {
     constexpr int TP = 65;
-    __shared__ uint32_t s_t[64 * TP];
+    __shared__ uint32_t s_t[128 * TP];
     __shared__ ColUnits cu;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int ng = group_offsets ? n_groups : 1;
     const int n_units = col_units_init(cu, group_offsets, ng, rows);
-    const int64_t c0 = (int64_t)blockIdx.x * 64;
-    const int ch = tid & 7, rp = tid >> 3;
+    const int64_t c0 = (int64_t)blockIdx.x * 128;
+    const int ch = tid & 15, qr = tid >> 4;
+    // cols % 32 == 0: the four 8-column chunks of a 32-column block are all
+    // in range or all out
     const bool cok = c0 + 8 * ch < cols;
+    // a row's four scale bytes as one word: whole tile, word-aligned rows
+    const bool full_row = c0 + 128 <= cols && cols % 128 == 0 && ((uintptr_t)s1 & 3) == 0;
 
-    uint4 v[4];                           // rows 2rp, 2rp+1, 2rp+64, 2rp+65
+    uint4 v[8];                           // v[p]: row 2qr + (p & 1) + 32 (p >> 1)
     auto load = [&](const UnitGeom &u) {
 #pragma unroll
-        for (int p = 0; p < 4; p++) {
-            const int r = 2 * rp + (p & 1) + 64 * (p >> 1);
+        for (int p = 0; p < 8; p++) {
+            const int r = 2 * qr + (p & 1) + 32 * (p >> 1);
             v[p] = make_uint4(0, 0, 0, 0);
             if (r < u.n && cok) {
                 const int64_t src = row_map ? (int64_t)row_map[u.r0 + r] : u.r0 + r;
@@ -328,12 +334,12 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
     UnitGeom u = unit_geom(cu, ng, unit);
     load(u);
     while (true) {
-        // registers -> LDS (packed row pairs), and the row-wise blocks
+        // registers -> LDS (packed row pairs)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; h2++) {
-            const uint4 a = v[2 * h2], b = v[2 * h2 + 1];   // rows r, r+1
+        for (int k = 0; k < 4; k++) {
+            const uint4 a = v[2 * k], b = v[2 * k + 1];     // rows r, r+1
             const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
-            const int pr = rp + 32 * h2;                     // row pair index
+            const int pr = qr + 16 * k;                      // row pair index
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 s_t[(8 * ch + 2 * e) * TP + pr] = (wa[e] & 0xffffu) | (wb[e] << 16);
@@ -341,9 +347,10 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
             }
         }
         if constexpr (BOTH) {             // 32-column block = 4 neighbouring lanes of one row
+            const int rl = lane & ~15;    // the row's first lane in the wave
 #pragma unroll
-            for (int p = 0; p < 4; p++) {
-                const int r = 2 * rp + (p & 1) + 64 * (p >> 1);
+            for (int p = 0; p < 8; p++) {
+                const int r = 2 * qr + (p & 1) + 32 * (p >> 1);
                 const uint32_t w[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
                 float f[8];
 #pragma unroll
@@ -353,13 +360,24 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
                 for (int e = 0; e < 8; e++) am = fmaxf(am, fabsf(f[e]));
                 am = fmaxf(am, __shfl_xor(am, 1, 64));
                 am = fmaxf(am, __shfl_xor(am, 2, 64));
+                const uint32_t sb = mx_scale_byte(am);
+                const int sh = 127 - (int)sb;
+                const uint32_t lo4 = e4m3x4(f[0], f[1], f[2], f[3], sh);
+                const uint32_t hi4 = e4m3x4(f[4], f[5], f[6], f[7], sh);
+                // the odd lane's 8 bytes go out with the even lane's store
+                const uint32_t plo = __shfl_xor(lo4, 1, 64), phi = __shfl_xor(hi4, 1, 64);
+                const uint32_t s4 = __shfl(sb, rl, 64) | (__shfl(sb, rl + 4, 64) << 8) |
+                                    (__shfl(sb, rl + 8, 64) << 16) | (__shfl(sb, rl + 12, 64) << 24);
                 if (r < u.n && cok) {
-                    const uint32_t sb = mx_scale_byte(am);
-                    const int sh = 127 - (int)sb;
-                    const uint32_t lo4 = e4m3x4(f[0], f[1], f[2], f[3], sh);
-                    const uint32_t hi4 = e4m3x4(f[4], f[5], f[6], f[7], sh);
-                    *reinterpret_cast<uint2 *>(q1 + (u.r0 + r) * cols + c0 + 8 * ch) = make_uint2(lo4, hi4);
-                    if ((ch & 3) == 0) s1[(u.r0 + r) * (cols / 32) + (c0 + 8 * ch) / 32] = (uint8_t)sb;
+                    uint8_t *qrow = q1 + (u.r0 + r) * cols + c0;
+                    if ((ch & 1) == 0)
+                        *reinterpret_cast<uint4 *>(qrow + 8 * ch) = make_uint4(lo4, hi4, plo, phi);
+                    uint8_t *srow = s1 + (u.r0 + r) * (cols / 32) + c0 / 32;
+                    if (full_row) {
+                        if (ch == 0) *reinterpret_cast<uint32_t *>(srow) = s4;
+                    } else if ((ch & 3) == 0) {
+                        srow[ch / 4] = (uint8_t)sb;
+                    }
                 }
             }
         }
@@ -370,18 +388,21 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
             u = unit_geom(cu, ng, next);
             load(u);
         }
-        const int cc = tid >> 2, b = tid & 3;
-        const int64_t c = c0 + cc;
-        if (c < cols) {
-            float f[32];
 #pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const uint32_t w = s_t[cc * TP + 16 * b + i];
-                f[2 * i] = lo_bf16(w);
-                f[2 * i + 1] = hi_bf16(w);
+        for (int pass = 0; pass < 2; pass++) {
+            const int cc = (tid >> 2) + 64 * pass, b = tid & 3;
+            const int64_t c = c0 + cc;
+            if (c < cols) {
+                float f[32];
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const uint32_t w = s_t[cc * TP + 16 * b + i];
+                    f[2 * i] = lo_bf16(w);
+                    f[2 * i + 1] = hi_bf16(w);
+                }
+                const uint32_t sb = encode_block32(f, q + cur.bb * 32 * cols + c * cur.nb * 32 + 128 * (int64_t)cur.j + 32 * b);
+                scale[cur.bb * cols + c * cur.nb + 4 * cur.j + b] = (uint8_t)sb;
             }
-            const uint32_t sb = encode_block32(f, q + cur.bb * 32 * cols + c * cur.nb * 32 + 128 * (int64_t)cur.j + 32 * b);
-            scale[cur.bb * cols + c * cur.nb + 4 * cur.j + b] = (uint8_t)sb;
         }
         if (next >= n_units) break;
         unit = next;
@@ -390,15 +411,15 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
 }
 
 #ifndef MOE_COLS_PER_CU
-#define MOE_COLS_PER_CU 8
+#define MOE_COLS_PER_CU 3
 #endif
-constexpr int kColsPerCU = MOE_COLS_PER_CU;
+constexpr int kColsPerCU = MOE_COLS_PER_CU;   // the bf16 tile's 41 KiB of LDS: three workgroups per CU
 constexpr int kColsPerCUF32 = 4;          // the fp32 tile's 33 KiB of LDS: four workgroups per CU
 
 // column tiles along x; units (upper bound sum_g ceil(len_g/128) <= rows/128 + groups) along
 // y, `per_cu` workgroups per CU in all when the kernel walks several units
-static dim3 cols_grid(int64_t rows, int64_t cols, int ng, int per_cu) {
-    const int64_t xt = (cols + 63) / 64;
+static dim3 cols_grid(int64_t rows, int64_t cols, int ng, int per_cu, int tile_cols) {
+    const int64_t xt = (cols + tile_cols - 1) / tile_cols;
     int64_t y = rows / 128 + ng + 1;
     if (per_cu > 0) {
         const int64_t want = ((int64_t)num_cus() * per_cu + xt - 1) / xt;
@@ -421,11 +442,11 @@ moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, 
     } else {
         const int ng = group_offsets ? n_groups : 1;
         if (bf)
-            mx_quant_cols_bf16<false><<<cols_grid(rows, cols, ng, kColsPerCU), 256, 0, s>>>(
+            mx_quant_cols_bf16<false><<<cols_grid(rows, cols, ng, kColsPerCU, 128), 256, 0, s>>>(
                 (const uint16_t *)in, rows, cols, group_offsets, n_groups, row_map, q, scale,
                 nullptr, nullptr);
         else
-            mx_quant_cols_f32<false><<<cols_grid(rows, cols, ng, kColsPerCUF32), 256, 0, s>>>(
+            mx_quant_cols_f32<false><<<cols_grid(rows, cols, ng, kColsPerCUF32, 64), 256, 0, s>>>(
                 (const float *)in, rows, cols, group_offsets, n_groups, row_map, q, scale, nullptr,
                 nullptr);
     }
@@ -440,10 +461,10 @@ moe_status mxfp8_quantize_both_launch(const void *in, moe_dtype in_dt, int64_t r
                                       uint8_t *s1, uint8_t *q0, uint8_t *s0, hipStream_t s) {
     const int ng = group_offsets ? n_groups : 1;
     if (in_dt == MOE_BF16)
-        mx_quant_cols_bf16<true><<<cols_grid(rows, cols, ng, kColsPerCU), 256, 0, s>>>(
+        mx_quant_cols_bf16<true><<<cols_grid(rows, cols, ng, kColsPerCU, 128), 256, 0, s>>>(
             (const uint16_t *)in, rows, cols, group_offsets, n_groups, nullptr, q0, s0, q1, s1);
     else
-        mx_quant_cols_f32<true><<<cols_grid(rows, cols, ng, kColsPerCUF32), 256, 0, s>>>(
+        mx_quant_cols_f32<true><<<cols_grid(rows, cols, ng, kColsPerCUF32, 64), 256, 0, s>>>(
             (const float *)in, rows, cols, group_offsets, n_groups, nullptr, q0, s0, q1, s1);
     return launch_status();
 }
