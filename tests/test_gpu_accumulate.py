@@ -111,8 +111,9 @@ def test_layer_accumulates_over_micro_batches(mx):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_quantize_both_matches_separate(dt):
-    rows, cols = 8 * 192, 320
+@pytest.mark.parametrize("cols", [320, 256])   # a partial last column tile / whole tiles only
+def test_quantize_both_matches_separate(dt, cols):
+    rows = 8 * 192
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     x = torch.from_numpy(synth.normal((rows, cols), 4, 0, 0.02)).to(tdt).cuda()
     x[5, :40] = 0.0                                        # an all-zero block
@@ -127,3 +128,27 @@ def test_quantize_both_matches_separate(dt):
     # and against the oracle along rows
     oq, os_ = oracle.mxfp8_quantize(to_np(x), 1)
     assert np.array_equal(to_np(q1), oq) and np.array_equal(to_np(s1), os_)
+
+
+def test_quantize_both_unaligned_row_scales():
+    """Row-layout scales at an odd address: the kernel's per-row word stores
+    of four scale bytes must give way to byte stores."""
+    import ctypes
+    rows, cols = 8 * 192, 256
+    x = torch.from_numpy(synth.normal((rows, cols), 5, 0, 0.02)).to(torch.bfloat16).cuda()
+    groups = torch.arange(0, 9, dtype=torch.int32, device="cuda") * 192
+    (r1, rs1), (r0, rs0) = moe.mxfp8_quantize_both(x, groups)
+    q1 = torch.empty_like(r1)
+    s1_buf = torch.full((rs1.numel() + 1,), 0xA5, dtype=torch.uint8, device="cuda")
+    q0 = torch.empty_like(r0)
+    s0 = torch.empty_like(rs0)
+    P = lambda t, off=0: ctypes.c_void_p(t.data_ptr() + off)
+    st = moe.lib().mxfp8_quantize_both(P(x), 1, rows, cols, P(groups), 8, P(q1), P(s1_buf, 1), P(q0), P(s0),
+                                       ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(q1, r1)
+    assert torch.equal(s1_buf[1:].view(rs1.shape), rs1)
+    assert s1_buf[0].item() == 0xA5                    # nothing written before the array
+    n = 8 * 2 * 4 * 32 * cols
+    assert torch.equal(q0[:n], r0[:n]) and torch.equal(s0[:n // 32], rs0[:n // 32])
