@@ -213,8 +213,8 @@ moe_status moe_grouped_gemm(const moe_gemm_desc *g, void *stream);
 /* Backward of route -> permute -> GEMM1 + SwiGLU -> GEMM2 -> combine.
  * Enqueues, in order: combine-bwd with the router backward fused in
  * (dy_perm, dgate, dlogits), GEMM2-dgrad with the SwiGLU backward (dAB),
- * GEMM2-wgrad (dW2), GEMM1-dgrad (dx_perm), GEMM1-wgrad (dW1),
- * unpermute-bwd (dX). Saved forward tensors and the three intermediates are
+ * GEMM2-wgrad (dW2), GEMM1-dgrad (dx_perm), unpermute-bwd (dX),
+ * GEMM1-wgrad (dW1). Saved forward tensors and the three intermediates are
  * caller-owned buffers.
  *   dlogits[t, e] = g_i (dg_i - sum_j g_j dg_j) for e = topk_idx[t, i], and
  *   exactly 0 for unselected experts, with dg_j = <dOut[t], y_perm[row]>.

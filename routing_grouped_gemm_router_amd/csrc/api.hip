@@ -263,13 +263,16 @@ moe_status moe_backward(const moe_bwd_desc *b, void *stream) {
     g.mode = MOE_GG_DGRAD; g.accumulate = 0; g.M = 0; g.N = b->d; g.K = 2 * b->h;
     g.A = b->dab; g.B = b->w1; g.C = b->dx_perm;
     if (R > 0 && (st = gemm_launch(&g, s)) != MOE_OK) return st;
+    // unpermute backward: dX[t] = sum_j dx_perm[token_pos[t, j]], straight
+    // after dx_perm is written (read back while it is still cached, and ahead
+    // of the weight gradient's 2 GiB of fp32 stores)
+    if ((st = combine_launch(b->dx_perm, b->dtype, nullptr, b->token_pos, b->T, b->d, b->k, b->dx,
+                             true, s)) != MOE_OK)
+        return st;
     // GEMM1 wgrad: dW1[e] = dAB^T x
     g.mode = MOE_GG_WGRAD; g.accumulate = b->accumulate_dw; g.M = 2 * b->h; g.N = b->d; g.K = 0;
     g.A = b->dab; g.B = b->x_perm; g.C = b->dw1;
-    if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
-    // unpermute backward: dX[t] = sum_j dx_perm[token_pos[t, j]]
-    return combine_launch(b->dx_perm, b->dtype, nullptr, b->token_pos, b->T, b->d, b->k, b->dx,
-                          true, s);
+    return gemm_launch(&g, s);
 }
 
 static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
@@ -343,16 +346,17 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
         g.A = aq; g.a_scale = as; g.B = b->w1t; g.b_scale = b->w1t_scale; g.C = b->dx_perm;
         if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
     }
+    // unpermute backward, straight after dx_perm is written
+    if ((st = combine_launch(b->dx_perm, MOE_BF16, nullptr, b->token_pos, b->T, d, b->k, b->dx,
+                             true, s)) != MOE_OK)
+        return st;
     // GEMM1 wgrad: dAB and x[sorted_token] along rows, per expert
     if ((st = mxfp8_quantize_launch(b->x, MOE_BF16, R, d, 0, b->offsets, E, b->sorted_token, b1q,
                                     b1s, s)) != MOE_OK)
         return st;
     g.mode = MOE_GG_WGRAD; g.accumulate = b->accumulate_dw; g.M = 2 * h; g.N = d; g.K = 0;
     g.A = b0q; g.a_scale = b0s; g.B = b1q; g.b_scale = b1s; g.C = b->dw1;
-    if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
-    // unpermute backward
-    return combine_launch(b->dx_perm, MOE_BF16, nullptr, b->token_pos, b->T, d, b->k, b->dx, true,
-                          s);
+    return gemm_launch(&g, s);
 }
 
 size_t mxfp8_col_blocks(int64_t rows, int32_t n_groups) { return moe::mxfp8_col_blocks(rows, n_groups); }
