@@ -14,14 +14,13 @@
 //    across the expert's m-tiles.
 //  * bf16 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulators; each wave owns a
 //    (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.
-//  * both operands are staged into LDS K-contiguous ([rows][64] bf16, 16-byte
-//    chunks XOR-swizzled by row) so every MFMA operand fetch is one
-//    ds_read_b128. Operands that are K-contiguous in HBM (activations in
-//    FWD/DGRAD, weights in FWD) are copied chunk by chunk; operands that are
-//    M/N-contiguous (weights in DGRAD, both operands of WGRAD) are loaded as
-//    8x8 bf16 blocks with coalesced 16-byte loads and transposed in registers.
-//  * double-buffered LDS with a register prefetch of the next K block: one
-//    barrier per K step.
+//  * operands reach LDS by direct global -> LDS copies (global_load_lds_dwordx4)
+//    through a 3-stage pipeline of 128-byte K steps, one workgroup barrier
+//    per step. K-contiguous operands (activations in FWD/DGRAD, weights in
+//    FWD, every MXFP8 operand) are staged [rows][128 bytes] with XOR-swizzled
+//    16-byte chunks, so an MFMA operand is one ds_read_b128; M/N-contiguous
+//    bf16 operands (weights in DGRAD, both operands of WGRAD) are staged as
+//    they lie and read with the transposing ds_read_b64_tr_b16.
 //  * epilogues: plain store; SwiGLU forward (the weight panel is laid out so
 //    each wave holds the gate and up columns of the same hidden unit in the
 //    same registers, so H' = silu(a) * b is formed from the fp32
@@ -253,8 +252,8 @@ constexpr int kStepBytes = 128;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define MOE_LDS __attribute__((address_space(3)))
 
-// Source of the LDS copies of masked chunks (rows past a group's end, the K
-// tail, columns past N): zero-initialised device memory.
+// Source of the LDS copies of chunks past the K extent (and of the MXFP8
+// scale words of rows that have none): zero-initialised device memory.
 __device__ uint4 g_zero_chunk[64] = {};
 
 // K-layout LDS tile: [R rows][128 bytes]. LDS has 64 4-byte banks, i.e. two
