@@ -227,7 +227,8 @@ moe_status moe_grouped_gemm(const moe_gemm_desc *g, void *stream);
  * x[sorted_token] along rows. The weights come pre-quantised in their second
  * orientation (w1t/w1t_scale = W1[e] along 2h as [E, d, 2h];
  * w2t/w2t_scale = W2[e] along d as [E, h, d]; see mxfp8_quantize axis 0),
- * i.e. once per weight update. Needs d % 128 == 0 and h % 128 == 0. */
+ * i.e. once per weight update. Needs d % 128 == 0, h % 128 == 0 and
+ * T*k <= 2^25 (the bound of MXFP8 WGRAD in moe_grouped_gemm). */
 typedef struct moe_bwd_desc {
     int32_t dtype;
     int32_t d, h, E, k;

@@ -280,6 +280,9 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
     if (!routing_shape_ok(b->T, b->E, b->k) || !width_ok(b->d) || !width_ok(b->h) ||
         b->d % 128 || b->h % 128)
         return MOE_ERR_SHAPE;
+    // the weight gradients address 128 rows of a group's column block with
+    // 32-bit offsets (as moe_grouped_gemm's MXFP8 WGRAD)
+    if (b->T * b->k > ((int64_t)1 << 25)) return MOE_ERR_SHAPE;
     if (!b->dw1 || !b->dw2 || !b->offsets || !b->w1t || !b->w1t_scale || !b->w2t ||
         !b->w2t_scale)
         return MOE_ERR_NULL;

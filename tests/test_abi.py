@@ -209,6 +209,9 @@ def test_accumulate_and_quantize_both_validation(lib):
     b = BwdDesc()
     b.dtype, b.d, b.h, b.E, b.k, b.T, b.accumulate_dw = 1, 64, 64, 8, 2, 16, 3
     assert lib.moe_backward(ctypes.byref(b), None) == 3
+    b.dtype, b.d, b.h, b.accumulate_dw = 2, 128, 128, 0          # MXFP8: T*k <= 2^25
+    b.T = (1 << 24) + 1
+    assert lib.moe_backward(ctypes.byref(b), None) == 2
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.mxfp8_quantize_both.argtypes = [P, I32, I64, I64, P, I32, P, P, P, P, P]
     f = 0x100000
