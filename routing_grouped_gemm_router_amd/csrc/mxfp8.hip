@@ -318,13 +318,23 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
     const bool full_row = c0 + 128 <= cols && cols % 128 == 0 && ((uintptr_t)s1 & 3) == 0;
 
     uint4 v[8];                           // v[p]: row 2qr + (p & 1) + 32 (p >> 1)
+    // row_map: this thread's source rows of the next unit to load, read one
+    // unit ahead so that the tile loads do not wait on the index loads
+    int32_t ri[8];
+    auto rows_of = [&](const UnitGeom &u) {
+#pragma unroll
+        for (int p = 0; p < 8; p++) {
+            const int r = 2 * qr + (p & 1) + 32 * (p >> 1);
+            ri[p] = (r < u.n && cok) ? row_map[u.r0 + r] : 0;
+        }
+    };
     auto load = [&](const UnitGeom &u) {
 #pragma unroll
         for (int p = 0; p < 8; p++) {
             const int r = 2 * qr + (p & 1) + 32 * (p >> 1);
             v[p] = make_uint4(0, 0, 0, 0);
             if (r < u.n && cok) {
-                const int64_t src = row_map ? (int64_t)row_map[u.r0 + r] : u.r0 + r;
+                const int64_t src = row_map ? (int64_t)ri[p] : u.r0 + r;
                 v[p] = *reinterpret_cast<const uint4 *>(in + src * cols + c0 + 8 * ch);
             }
         }
@@ -332,7 +342,9 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
     int unit = blockIdx.y;
     if (unit >= n_units) return;          // uniform over the workgroup
     UnitGeom u = unit_geom(cu, ng, unit);
+    if (row_map) rows_of(u);
     load(u);
+    if (row_map && unit + (int)gridDim.y < n_units) rows_of(unit_geom(cu, ng, unit + gridDim.y));
     while (true) {
         // registers -> LDS (packed row pairs)
 #pragma unroll
@@ -387,6 +399,7 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
         if (next < n_units) {             // prefetch the next tile while this one is encoded
             u = unit_geom(cu, ng, next);
             load(u);
+            if (row_map && next + (int)gridDim.y < n_units) rows_of(unit_geom(cu, ng, next + gridDim.y));
         }
 #pragma unroll
         for (int pass = 0; pass < 2; pass++) {
