@@ -246,7 +246,9 @@ __global__ __launch_bounds__(256) void mx_quant_cols_f32(const float *__restrict
             s_t[(4 * ch + 2) * TP + r] = v[p].z;
             s_t[(4 * ch + 3) * TP + r] = v[p].w;
             if constexpr (BOTH) {
-                float am = fmaxf(fmaxf(fabsf(v[p].x), fabsf(v[p].y)), fmaxf(fabsf(v[p].z), fabsf(v[p].w)));
+                // from 0, so that NaN elements never enter the block maximum
+                float am = fmaxf(fmaxf(fmaxf(0.f, fabsf(v[p].x)), fabsf(v[p].y)),
+                                 fmaxf(fabsf(v[p].z), fabsf(v[p].w)));
                 am = fmaxf(am, __shfl_xor(am, 1, 64));
                 am = fmaxf(am, __shfl_xor(am, 2, 64));
                 am = fmaxf(am, __shfl_xor(am, 4, 64));

@@ -66,6 +66,37 @@ def test_quantise_with_row_map():
     assert np.array_equal(q1.cpu().numpy(), q1o) and np.array_equal(s1.cpu().numpy(), s1o)
 
 
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_quantise_nan_elements(dt):
+    """NaN elements (both signs) among finite ones: the block scale ignores
+    them and each encodes as its sign | 0x7f, as the oracle does; a wave
+    that holds a NaN takes the encoder's exact select path, the others the
+    fast one, so blocks with and without NaN sit side by side."""
+    x = dev(_wide((257, 160), 6), dt)
+    # quiet NaNs of both signs, planted as bit patterns
+    bits = x.view(torch.int32) if dt == torch.float32 else x.view(torch.int16)
+    pos, neg = (0x7FC00000, -0x400000) if dt == torch.float32 else (0x7FC0, -0x40)
+    bits[3, 7] = pos
+    bits[3, 40] = neg
+    bits[100, :32] = neg                  # a block of NaNs only
+    bits[200, 150] = pos
+    xn = to_np(x)
+    assert np.isnan(xn[3, 7]) and not np.signbit(xn[3, 7])
+    assert np.isnan(xn[3, 40]) and np.signbit(xn[3, 40])
+    q, s = moe.mxfp8_quantize(x, 1)
+    qo, so = oracle.mxfp8_quantize(xn, 1)
+    assert np.array_equal(q.cpu().numpy(), qo) and np.array_equal(s.cpu().numpy(), so)
+    go = np.array([0, 5, 130, 257], np.int32)
+    q0, s0 = moe.mxfp8_quantize(x, 0, torch.from_numpy(go).cuda())
+    qo0, so0 = oracle.mxfp8_quantize(xn, 0, go)
+    assert np.array_equal(q0.cpu().numpy()[:len(qo0)], qo0)
+    assert np.array_equal(s0.cpu().numpy()[:len(so0)], so0)
+    (qb1, sb1), (qb0, sb0) = moe.mxfp8_quantize_both(x, torch.from_numpy(go).cuda())
+    assert np.array_equal(qb1.cpu().numpy(), qo) and np.array_equal(sb1.cpu().numpy(), so)
+    assert np.array_equal(qb0.cpu().numpy()[:len(qo0)], qo0)
+    assert np.array_equal(sb0.cpu().numpy()[:len(so0)], so0)
+
+
 def test_permute_mxfp8_payload():
     T, d, E, k = 200, 256, 8, 3
     logits = synth.normal((T, E), 5, 0, 1.0)
