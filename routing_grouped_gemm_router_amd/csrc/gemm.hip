@@ -927,32 +927,54 @@ void gg_mfma(GemmArgs g) {
             const int col_l = lane & 31;
             if constexpr (MODE == MOE_GG_WGRAD) {
                 float *C = reinterpret_cast<float *>(g.C) + (int64_t)cur.e * g.M * g.N;
+                auto row_of = [&](int i, int v) {
+                    return cur.m0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                };
+                if constexpr (epi_first) {
+                    // C += the tile, one fp32 add per element. Every old value
+                    // of the wave's tile is loaded before the first store: with
+                    // loads and stores both in flight the compiler would wait
+                    // for all memory operations before each use of a loaded
+                    // value
+                    float old[TM][TN][16];
 #pragma unroll
-                for (int i = 0; i < TM; i++)
+                    for (int i = 0; i < TM; i++)
 #pragma unroll
-                    for (int j = 0; j < TN; j++) {
-                        const int n = cur.n0 + wn * WTN + j * 32 + col_l;
-                        if constexpr (epi_first) {
-                            // C += the tile, one fp32 add per element
-                            float old[16];
+                        for (int j = 0; j < TN; j++) {
+                            const int n = cur.n0 + wn * WTN + j * 32 + col_l;
 #pragma unroll
                             for (int v = 0; v < 16; v++) {
-                                const int m = cur.m0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-                                old[v] = (m < g.M && n < g.N) ? C[(int64_t)m * g.N + n] : 0.f;
+                                const int m = row_of(i, v);
+                                old[i][j][v] = (m < g.M && n < g.N) ? C[(int64_t)m * g.N + n] : 0.f;
                             }
+                        }
+                    // one wait for all of them, on the path every lane takes
+                    // (the stores below sit in masked branches)
+                    wait_vmem<0>();
+#pragma unroll
+                    for (int i = 0; i < TM; i++)
+#pragma unroll
+                        for (int j = 0; j < TN; j++) {
+                            const int n = cur.n0 + wn * WTN + j * 32 + col_l;
 #pragma unroll
                             for (int v = 0; v < 16; v++) {
-                                const int m = cur.m0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-                                if (m < g.M && n < g.N) store_f32(C + (int64_t)m * g.N + n, old[v] + acc[i][j][v]);
+                                const int m = row_of(i, v);
+                                if (m < g.M && n < g.N) store_f32(C + (int64_t)m * g.N + n, old[i][j][v] + acc[i][j][v]);
                             }
-                        } else {
+                        }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < TM; i++)
+#pragma unroll
+                        for (int j = 0; j < TN; j++) {
+                            const int n = cur.n0 + wn * WTN + j * 32 + col_l;
 #pragma unroll
                             for (int v = 0; v < 16; v++) {
-                                const int m = cur.m0 + wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+                                const int m = row_of(i, v);
                                 if (m < g.M && n < g.N) store_f32(C + (int64_t)m * g.N + n, acc[i][j][v]);
                             }
                         }
-                    }
+                }
             } else if constexpr (EPI == MOE_EPI_SWIGLU_FWD) {
                 uint16_t *AB = reinterpret_cast<uint16_t *>(g.C);
                 uint16_t *HP = reinterpret_cast<uint16_t *>(g.aux_out);
@@ -1048,37 +1070,59 @@ void gg_mfma(GemmArgs g) {
                     const uint16_t *AB = reinterpret_cast<const uint16_t *>(g.aux);
                     uint16_t *dAB = reinterpret_cast<uint16_t *>(g.C);
                     const int h = g.h;
+                    // each thread's (row, 8-column) chunks of the pass, GRP at a
+                    // time: their a and b loads are issued together and waited
+                    // for once, on the path every lane takes (with loads and
+                    // stores both in flight the compiler would otherwise wait
+                    // for everything before each chunk)
                     constexpr int CPR = BN / 8;
-                    for (int it = tid; it < EP_ROWS * CPR; it += NT) {
-                        const int r = it / CPR, c = it % CPR;
-                        const int grow = cur.row0 + pr0 + r, jj = cur.n0 + c * 8;
-                        if (grow >= cur.row_end || jj >= h) continue;
-                        const uint16_t *abr = AB + (int64_t)grow * 2 * h;
-                        const uint4 ua = *reinterpret_cast<const uint4 *>(abr + jj);
-                        const uint4 ub = *reinterpret_cast<const uint4 *>(abr + h + jj);
-                        const float4 d0 = *reinterpret_cast<const float4 *>(stg + r * PF + c * 32);
-                        const float4 d1 = *reinterpret_cast<const float4 *>(stg + r * PF + c * 32 + 16);
-                        const float dh[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-                        const uint32_t wa[4] = {ua.x, ua.y, ua.z, ua.w}, wb[4] = {ub.x, ub.y, ub.z, ub.w};
-                        uint32_t oa[4], ob[4];
-    #pragma unroll
-                        for (int q = 0; q < 4; q++) {
-                            float da2[2], db2[2];
-    #pragma unroll
-                            for (int hh = 0; hh < 2; hh++) {
-                                const float a = hh ? hi_bf16(wa[q]) : lo_bf16(wa[q]);
-                                const float b = hh ? hi_bf16(wb[q]) : lo_bf16(wb[q]);
-                                const float sg = 1.f / (1.f + __expf(-a));
-                                const float d = dh[2 * q + hh];
-                                da2[hh] = d * b * sg * (1.f + a * (1.f - sg));
-                                db2[hh] = d * a * sg;
+                    constexpr int ITERS = (EP_ROWS * CPR + NT - 1) / NT;
+                    constexpr int GRP = ITERS < 2 ? ITERS : 2;
+                    for (int q0 = 0; q0 < ITERS; q0 += GRP) {
+                        uint4 la[GRP], lb[GRP];
+#pragma unroll
+                        for (int u = 0; u < GRP; u++) {
+                            const int it = tid + (q0 + u) * NT;
+                            const int r = it / CPR, c = it % CPR;
+                            const int grow = cur.row0 + pr0 + r, jj = cur.n0 + c * 8;
+                            if (q0 + u < ITERS && it < EP_ROWS * CPR && grow < cur.row_end && jj < h) {
+                                const uint16_t *abr = AB + (int64_t)grow * 2 * h;
+                                la[u] = *reinterpret_cast<const uint4 *>(abr + jj);
+                                lb[u] = *reinterpret_cast<const uint4 *>(abr + h + jj);
                             }
-                            oa[q] = pack_bf16x2(da2[0], da2[1]);
-                            ob[q] = pack_bf16x2(db2[0], db2[1]);
                         }
-                        uint16_t *dr = dAB + (int64_t)grow * 2 * h;
-                        store16(dr + jj, make_uint4(oa[0], oa[1], oa[2], oa[3]));
-                        store16(dr + h + jj, make_uint4(ob[0], ob[1], ob[2], ob[3]));
+                        wait_vmem<0>();
+#pragma unroll
+                        for (int u = 0; u < GRP; u++) {
+                            const int it = tid + (q0 + u) * NT;
+                            const int r = it / CPR, c = it % CPR;
+                            const int grow = cur.row0 + pr0 + r, jj = cur.n0 + c * 8;
+                            if (q0 + u >= ITERS || it >= EP_ROWS * CPR || grow >= cur.row_end || jj >= h) continue;
+                            const uint4 ua = la[u], ub = lb[u];
+                            const float4 d0 = *reinterpret_cast<const float4 *>(stg + r * PF + c * 32);
+                            const float4 d1 = *reinterpret_cast<const float4 *>(stg + r * PF + c * 32 + 16);
+                            const float dh[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                            const uint32_t wa[4] = {ua.x, ua.y, ua.z, ua.w}, wb[4] = {ub.x, ub.y, ub.z, ub.w};
+                            uint32_t oa[4], ob[4];
+#pragma unroll
+                            for (int w = 0; w < 4; w++) {
+                                float da2[2], db2[2];
+#pragma unroll
+                                for (int hh = 0; hh < 2; hh++) {
+                                    const float a = hh ? hi_bf16(wa[w]) : lo_bf16(wa[w]);
+                                    const float b = hh ? hi_bf16(wb[w]) : lo_bf16(wb[w]);
+                                    const float sg = 1.f / (1.f + __expf(-a));
+                                    const float d = dh[2 * w + hh];
+                                    da2[hh] = d * b * sg * (1.f + a * (1.f - sg));
+                                    db2[hh] = d * a * sg;
+                                }
+                                oa[w] = pack_bf16x2(da2[0], da2[1]);
+                                ob[w] = pack_bf16x2(db2[0], db2[1]);
+                            }
+                            uint16_t *dr = dAB + (int64_t)grow * 2 * h;
+                            store16(dr + jj, make_uint4(oa[0], oa[1], oa[2], oa[3]));
+                            store16(dr + h + jj, make_uint4(ob[0], ob[1], ob[2], ob[3]));
+                        }
                     }
                 } else if constexpr (EPI == MOE_EPI_SWIGLU_FWD) {
                     uint16_t *AB = reinterpret_cast<uint16_t *>(g.C);
