@@ -69,6 +69,10 @@ __global__ __launch_bounds__(256) void lb_partial(const float *__restrict__ logi
     // before the first softmax
     constexpr int NTW = kLbChunk / 4;
     float l[NTW][EPL];
+    // with a gradient, the current dlogits rows too: loaded with the logits,
+    // before the first store (a load used while stores are in flight would
+    // wait for all of them)
+    float dl[NTW][EPL];
 #pragma unroll
     for (int i = 0; i < NTW; i++) {
         const int64_t t = t0 + wave + 4 * i;
@@ -76,6 +80,7 @@ __global__ __launch_bounds__(256) void lb_partial(const float *__restrict__ logi
         for (int j = 0; j < EPL; j++) {
             const int e = lane + 64 * j;
             l[i][j] = (t < t1 && e < E) ? logits[t * E + e] : -INFINITY;
+            dl[i][j] = (dlogits && t < t1 && e < E) ? dlogits[t * E + e] : 0.f;
         }
     }
 #pragma unroll
@@ -106,7 +111,7 @@ __global__ __launch_bounds__(256) void lb_partial(const float *__restrict__ logi
 #pragma unroll
             for (int j = 0; j < EPL; j++) {
                 const int e = lane + 64 * j;
-                if (e < E) drow[e] += coef * p[j] * (f[j] - sf);
+                if (e < E) drow[e] = dl[i][j] + coef * p[j] * (f[j] - sf);
             }
         }
     }
