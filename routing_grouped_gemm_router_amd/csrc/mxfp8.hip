@@ -15,13 +15,14 @@
 // (v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even) on inputs clamped to
 // +-448, which is the saturation; its only departure from the format is a
 // NaN, which it writes as 0xff whatever the sign, so a positive NaN is
-// patched to 0x7f. Waves without a NaN clamp with v_med3_f32 (e4m3x4). Checked on the GPU against an integer encoding of the
-// format (mantissa rounded from 23 to 3 bits ties to even, exponent rebased
-// from 127 to 7; rint(|v| * 2^9) below 2^-6) on all 2^32 fp32 patterns:
-// identical except NaN's sign, which the patch restores.
+// patched to 0x7f. Waves without a NaN clamp with v_med3_f32 (e4m3x4).
+// Checked on the GPU against an integer encoding of the format (mantissa
+// rounded from 23 to 3 bits ties to even, exponent rebased from 127 to 7;
+// rint(|v| * 2^9) below 2^-6) on all 2^32 fp32 patterns: identical except
+// NaN's sign, which the patch restores.
 // Each kernel reads its input once and writes each output once; the encoding
-// arithmetic (~10 VALU instructions per element and orientation) is about half
-// of the time of the both-layouts kernels, memory traffic the rest.
+// arithmetic is about half of the time of the both-layouts kernels, memory
+// traffic the rest.
 #include "common.h"
 
 namespace moe {
