@@ -33,7 +33,8 @@
  *     validation error nothing is enqueued. After enqueueing, a launch error
  *     is reported as MOE_ERR_LAUNCH.
  *   - Limits: 1 <= E <= 256; 1 <= k <= min(E, 8); 0 <= T; T*k < 2^31;
- *     d and h multiples of 32; d, h <= 16384.
+ *     d and h multiples of 32; d <= 16384, h <= 8192 (GEMM1 is 2h wide;
+ *     every GEMM width N, K, M <= 16384).
  *   - Non-finite logits are outside the contract: outputs are then
  *     unspecified, but no kernel indexes out of bounds.
  *   - Stateless and re-entrant: concurrent calls on different streams are
@@ -176,9 +177,9 @@ enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU_FWD = 1, MOE_EPI_SWIGLU_BWD = 2 };
  *     groups = offsets): A holds the [rows, M] operand, B the [rows, N]
  *     operand; C [E, M, N] fp32. Their scale arrays must be sized by
  *     mxfp8_col_blocks (the kernel may read up to 12 bytes past the last
- *     used scale byte, into the spare blocks). rows <= 2^25 (MOE_ERR_SHAPE
- *     otherwise): the kernel addresses 128 rows of one group's column block
- *     with 32-bit offsets.
+ *     used scale byte, into the spare blocks). rows <= 2^24 (MOE_ERR_SHAPE
+ *     otherwise): the kernel addresses the 256 rows of a B tile in one
+ *     group's column block with 32-bit offsets from one base.
  * (aux_out_scale is reserved and must be null.)
  */
 typedef struct moe_gemm_desc {
@@ -228,7 +229,7 @@ moe_status moe_grouped_gemm(const moe_gemm_desc *g, void *stream);
  * orientation (w1t/w1t_scale = W1[e] along 2h as [E, d, 2h];
  * w2t/w2t_scale = W2[e] along d as [E, h, d]; see mxfp8_quantize axis 0),
  * i.e. once per weight update. Needs d % 128 == 0, h % 128 == 0 and
- * T*k <= 2^25 (the bound of MXFP8 WGRAD in moe_grouped_gemm). */
+ * T*k <= 2^24 (the bound of MXFP8 WGRAD in moe_grouped_gemm). */
 typedef struct moe_bwd_desc {
     int32_t dtype;
     int32_t d, h, E, k;

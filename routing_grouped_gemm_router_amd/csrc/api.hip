@@ -61,6 +61,8 @@ static bool routing_shape_ok(int64_t T, int32_t E, int32_t k) {
 }
 
 static bool width_ok(int32_t w) { return w >= 32 && w <= 16384 && w % 32 == 0; }
+// the expert hidden width h: GEMM1 is 2h wide, so 2h is held to the GEMM limit
+static bool hidden_ok(int32_t h) { return width_ok(h) && 2 * h <= 16384; }
 
 static size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -79,8 +81,10 @@ static MxBwdLayout mx_bwd_layout(int64_t R, int d, int h, int E) {
     L.a_q = 0;
     L.a_s = round256((size_t)R * wmax);
     const size_t regA = L.a_s + round256((size_t)R * wmax / 32);
-    // B: (dy rows along d, H' rows along h) then (dAB rows along 2h, x rows along d)
-    const size_t c0 = nbc * 32 * wmax, c1 = nbc * 32 * (size_t)d;
+    // B: (dy rows along d, H' rows along h) then (dAB rows along 2h, x rows along d);
+    // slot 0 holds d or 2h columns, slot 1 h or d
+    const size_t w1 = (size_t)(h > d ? h : d);
+    const size_t c0 = nbc * 32 * wmax, c1 = nbc * 32 * w1;
     L.b0_q = regA;
     L.b0_s = L.b0_q + round256(c0);
     L.b1_q = L.b0_s + round256(c0 / 32);
@@ -165,9 +169,10 @@ static moe_status check_gemm(const moe_gemm_desc *g) {
     if (g->dtype == MOE_MXFP8) {
         if (g->aux_out_scale) return MOE_ERR_DTYPE;
         if (g->mode != MOE_GG_WGRAD && g->K % 128) return MOE_ERR_SHAPE;
-        // WGRAD: 128 rows of a group's column block (pitch <= rows + 127
-        // bytes) are addressed with 32-bit offsets
-        if (g->mode == MOE_GG_WGRAD && g->rows > ((int64_t)1 << 25)) return MOE_ERR_SHAPE;
+        // WGRAD: the 256 rows of a B tile in a group's column block (pitch:
+        // the group's rows rounded up to 128 bytes) are addressed with 32-bit
+        // offsets from one base
+        if (g->mode == MOE_GG_WGRAD && g->rows > ((int64_t)1 << 24)) return MOE_ERR_SHAPE;
         if (!g->a_scale || !g->b_scale) return MOE_ERR_NULL;
         if (!aligned4(g->a_scale) || !aligned4(g->b_scale)) return MOE_ERR_ALIGN;
     }
@@ -224,7 +229,7 @@ moe_status moe_backward(const moe_bwd_desc *b, void *stream) {
     if (b->dtype == MOE_MXFP8) return backward_mxfp8(b, (hipStream_t)stream);
     if (b->dtype != MOE_F32 && b->dtype != MOE_BF16) return MOE_ERR_DTYPE;
     if (b->accumulate_dw != 0 && b->accumulate_dw != 1) return MOE_ERR_DTYPE;
-    if (!routing_shape_ok(b->T, b->E, b->k) || !width_ok(b->d) || !width_ok(b->h))
+    if (!routing_shape_ok(b->T, b->E, b->k) || !width_ok(b->d) || !hidden_ok(b->h))
         return MOE_ERR_SHAPE;
     if (!b->dw1 || !b->dw2 || !b->offsets || !b->w1 || !b->w2) return MOE_ERR_NULL;
     const bool any = b->T > 0;
@@ -277,12 +282,12 @@ moe_status moe_backward(const moe_bwd_desc *b, void *stream) {
 
 static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
     if (b->accumulate_dw != 0 && b->accumulate_dw != 1) return MOE_ERR_DTYPE;
-    if (!routing_shape_ok(b->T, b->E, b->k) || !width_ok(b->d) || !width_ok(b->h) ||
+    if (!routing_shape_ok(b->T, b->E, b->k) || !width_ok(b->d) || !hidden_ok(b->h) ||
         b->d % 128 || b->h % 128)
         return MOE_ERR_SHAPE;
-    // the weight gradients address 128 rows of a group's column block with
+    // the weight gradients address 256 rows of a group's column block with
     // 32-bit offsets (as moe_grouped_gemm's MXFP8 WGRAD)
-    if (b->T * b->k > ((int64_t)1 << 25)) return MOE_ERR_SHAPE;
+    if (b->T * b->k > ((int64_t)1 << 24)) return MOE_ERR_SHAPE;
     if (!b->dw1 || !b->dw2 || !b->offsets || !b->w1t || !b->w1t_scale || !b->w2t ||
         !b->w2t_scale)
         return MOE_ERR_NULL;

@@ -655,7 +655,7 @@ void gg_mfma(GemmArgs g) {
             if constexpr (FP8) {
                 // column-block layout: expert e's A is [M][kpad] at byte
                 // sb0*128*M (B likewise); offsets from the tile's first row
-                // stay below 128 * kpad < 2^32 (the host bounds the rows)
+                // stay below BN * kpad <= 2^32 (the host bounds the rows to 2^24)
                 const uint32_t kp = (uint32_t)t.kpad;
                 ta.setup_kl(A + (int64_t)t.sb0 * 128 * g.M + (int64_t)t.m0 * t.kpad,
                             [&](int r) { return (uint32_t)min(r, g.M - 1 - t.m0) * kp; }, wave, lane);

@@ -13,6 +13,16 @@ def rel_inf(x, ref) -> float:
     return float(np.abs(x - ref).max() / den)
 
 
+def rel_fro(x, ref) -> float:
+    """||x - ref||_2 / ||ref||_2 over all elements (Frobenius-norm relative error)."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = float(np.linalg.norm(ref))
+    if den == 0:
+        return float(np.linalg.norm(x))
+    return float(np.linalg.norm(x - ref) / den)
+
+
 def to_np(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         t = t.float()

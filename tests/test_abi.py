@@ -144,7 +144,7 @@ def test_mxfp8_gemm_validation(lib):
     bad.aux_out_scale = 0x100000                                     # reserved
     assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 3
     bad = GemmDesc.from_buffer_copy(g)
-    bad.mode, bad.M, bad.N, bad.rows = 2, 64, 64, (1 << 25) + 1      # WGRAD column blocks:
+    bad.mode, bad.M, bad.N, bad.rows = 2, 64, 64, (1 << 24) + 1      # WGRAD column blocks:
     assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 2        # 32-bit row offsets
     lib.mxfp8_col_blocks.argtypes = [ctypes.c_int64, ctypes.c_int32]
     lib.mxfp8_col_blocks.restype = ctypes.c_size_t
@@ -209,9 +209,13 @@ def test_accumulate_and_quantize_both_validation(lib):
     b = BwdDesc()
     b.dtype, b.d, b.h, b.E, b.k, b.T, b.accumulate_dw = 1, 64, 64, 8, 2, 16, 3
     assert lib.moe_backward(ctypes.byref(b), None) == 3
-    b.dtype, b.d, b.h, b.accumulate_dw = 2, 128, 128, 0          # MXFP8: T*k <= 2^25
-    b.T = (1 << 24) + 1
+    b.dtype, b.d, b.h, b.accumulate_dw = 2, 128, 128, 0          # MXFP8: T*k <= 2^24
+    b.T = (1 << 23) + 1
     assert lib.moe_backward(ctypes.byref(b), None) == 2
+    b.T = 16
+    for dt in (0, 1, 2):                                         # h <= 8192: GEMM1 is 2h wide
+        b.dtype, b.h = dt, 8192 + 128
+        assert lib.moe_backward(ctypes.byref(b), None) == 2
     P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.mxfp8_quantize_both.argtypes = [P, I32, I64, I64, P, I32, P, P, P, P, P]
     f = 0x100000

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from helpers import TOL, dev, rel_inf, to_np
+from helpers import TOL, dev, rel_fro, rel_inf, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -213,7 +213,10 @@ def _run_mx(inp, k):
     return layer, out, g
 
 
-@pytest.mark.parametrize("shape", [(300, 256, 8, 2, 128), (130, 128, 16, 4, 128)])
+@pytest.mark.parametrize("shape", [(300, 256, 8, 2, 128), (130, 128, 16, 4, 128),
+                                   # widest d, widest h; largest E with the largest k
+                                   (64, 16384, 4, 2, 128), (64, 128, 4, 2, 8192),
+                                   (2048, 128, 256, 8, 128)])
 def test_mxfp8_layer_end_to_end(shape):
     T, d, E, k, h = shape
     inp = _mx_inputs(T, d, E, k, h, seed=11)
@@ -223,9 +226,26 @@ def test_mxfp8_layer_end_to_end(shape):
     assert rel_inf(to_np(out), m["out"]) <= tol
     assert rel_inf(to_np(g["dx"]), m["dx"]) <= tol
     assert rel_inf(to_np(g["dlogits"]), m["dlogits"]) <= tol
+    dw1, dw2 = to_np(g["dw1"]), to_np(g["dw2"])
+    ref1 = np.stack([m["dW1"][e] for e in range(E)])
+    ref2 = np.stack([m["dW2"][e] for e in range(E)])
+    # each weight gradient as one tensor (the error metric of every other check)
+    assert rel_inf(dw1, ref1) <= tol
+    assert rel_inf(dw2, ref2) <= tol
+    # and each expert's slice: the two sides quantise their own bf16 dAB and
+    # dy, which differ by rounding in a few percent of the elements; where
+    # that moves a value across an E4M3 rounding step (an eighth of it) or
+    # changes a block's scale, one term of an expert's sum moves by up to
+    # that much. The slice's largest such error against its largest value
+    # grows with the number of slices checked (4 % at E = 256), so per
+    # expert the relative Frobenius error is checked, and the infinity norm
+    # with up to 16 experts
     for e in range(E):
-        assert rel_inf(to_np(g["dw1"][e]), m["dW1"][e]) <= tol, e
-        assert rel_inf(to_np(g["dw2"][e]), m["dW2"][e]) <= tol, e
+        assert rel_fro(dw1[e], ref1[e]) <= tol, e
+        assert rel_fro(dw2[e], ref2[e]) <= tol, e
+        if E <= 16:
+            assert rel_inf(dw1[e], ref1[e]) <= tol, e
+            assert rel_inf(dw2[e], ref2[e]) <= tol, e
 
 
 def test_mxfp8_recompute_matches_saved():

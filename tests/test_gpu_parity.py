@@ -187,7 +187,12 @@ def _run_layer(inp, k, tdt):
 
 
 @pytest.mark.parametrize("shape,dt", [((256, 128, 8, 2, 256), "f32"), ((300, 256, 8, 2, 192), "bf16"),
-                                      ((513, 128, 16, 4, 96), "bf16"), ((200, 64, 4, 4, 64), "f32")])
+                                      ((513, 128, 16, 4, 96), "bf16"), ((200, 64, 4, 4, 64), "f32"),
+                                      # the widest d and h the library accepts (d = 16384: GEMM1's
+                                      # K and GEMM2's N; h = 8192: GEMM1's N = 2h = 16384 and
+                                      # GEMM2's K), and the largest E with the largest k
+                                      ((64, 16384, 4, 2, 128), "bf16"), ((64, 128, 4, 2, 8192), "bf16"),
+                                      ((300, 128, 256, 8, 64), "bf16")])
 def test_layer_end_to_end(shape, dt):
     T, d, E, k, h = shape
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
