@@ -731,7 +731,8 @@ void gg_mfma(GemmArgs g) {
             }
         }
         ta.issue(st, kt, klim, wave);
-        tb.issue(st + BM * 8, kt, klim, wave);
+        // bf16 DGRAD: klim is A's K extent in bytes; B (MN layout) counts K rows
+        tb.issue(st + BM * 8, kt, (A_KL && !B_KL) ? klim / ESZ : klim, wave);
         if constexpr (FP8) {
             if (!sbatch) {
                 uint4 *sarea = lds_pool + STAGES * STAGE_U4 + si * SCALE_U4;

@@ -115,6 +115,10 @@ SHAPES = [  # T, d, E, k, h: several tiles plus ragged tails, an empty expert
     (300, 256, 8, 2, 192),
     (513, 128, 5, 3, 320),
     (64, 96, 3, 1, 32),
+    # d % 64 == 32: GEMM2 dgrad's last K step is half a step, the weight rows
+    # past K must not be read (the last expert's W2 ends there)
+    (97, 32, 3, 3, 1024),
+    (333, 96, 7, 3, 160),
 ]
 
 
@@ -192,7 +196,9 @@ def _run_layer(inp, k, tdt):
                                       # K and GEMM2's N; h = 8192: GEMM1's N = 2h = 16384 and
                                       # GEMM2's K), and the largest E with the largest k
                                       ((64, 16384, 4, 2, 128), "bf16"), ((64, 128, 4, 2, 8192), "bf16"),
-                                      ((300, 128, 256, 8, 64), "bf16")])
+                                      ((300, 128, 256, 8, 64), "bf16"),
+                                      # h > d and d % 64 == 32
+                                      ((333, 96, 7, 3, 160), "bf16"), ((200, 64, 8, 2, 512), "bf16")])
 def test_layer_end_to_end(shape, dt):
     T, d, E, k, h = shape
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
