@@ -248,6 +248,27 @@ def test_mxfp8_layer_end_to_end(shape):
             assert rel_inf(dw2[e], ref2[e]) <= tol, e
 
 
+@pytest.mark.parametrize("shape,empty", [((1, 128, 1, 1, 128), None),    # one token, one expert
+                                         ((3, 128, 8, 8, 128), None),    # k = E
+                                         ((200, 256, 6, 2, 128), -1),    # last expert empty
+                                         ((200, 128, 6, 2, 256), 0)])    # first expert empty
+def test_mxfp8_layer_edge_cases(shape, empty):
+    T, d, E, k, h = shape
+    inp = _mx_inputs(T, d, E, k, h, seed=5)
+    if empty is not None:
+        inp["logits"][:, empty] -= 100.0
+    m = oracle.layer_mx(inp, k)
+    layer, out, g = _run_mx(inp, k)
+    tol = TOL["mxfp8"]
+    assert rel_inf(to_np(out), m["out"]) <= tol
+    assert rel_inf(to_np(g["dx"]), m["dx"]) <= tol
+    assert rel_inf(to_np(g["dlogits"]), m["dlogits"]) <= tol
+    assert rel_inf(to_np(g["dw1"]), np.stack([m["dW1"][e] for e in range(E)])) <= tol
+    assert rel_inf(to_np(g["dw2"]), np.stack([m["dW2"][e] for e in range(E)])) <= tol
+    if empty is not None:
+        assert torch.all(g["dw1"][empty] == 0) and torch.all(g["dw2"][empty] == 0)
+
+
 def test_mxfp8_recompute_matches_saved():
     """recompute=True re-quantises and re-dispatches x and reruns GEMM1 in
     the backward: bit-identical gradients to the layer that keeps A||B and H'."""

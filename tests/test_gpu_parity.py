@@ -218,6 +218,37 @@ def test_layer_end_to_end(shape, dt):
     assert np.all(to_np(g["dlogits"])[~sel] == 0)
 
 
+def _bias(col, by):
+    def f(inp):
+        inp["logits"][:, col] += by
+    return f
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("shape,mod", [
+    ((1, 32, 1, 1, 32), None),                  # one token, one expert
+    ((1, 64, 8, 8, 32), None),                  # one token on every expert (k = E)
+    ((200, 96, 6, 2, 64), _bias(-1, -100.0)),   # the last expert gets no rows
+    ((200, 64, 6, 2, 96), _bias(0, -100.0)),    # the first expert gets no rows
+    ((300, 128, 8, 2, 128), _bias(1, 100.0)),   # every token's first choice is expert 1
+])
+def test_layer_edge_cases(shape, mod, dt):
+    T, d, E, k, h = shape
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    inp = _layer_inputs(T, d, E, k, h, seed=3, dt=dt)
+    if mod:
+        mod(inp)
+    f = oracle.layer_forward(inp, k, dt)
+    b = oracle.layer_backward(inp, f, k, dt)
+    layer, out, g = _run_layer(inp, k, tdt)
+    _route_eq(layer.route, f["route"])
+    tol = TOL[dt]
+    assert rel_inf(to_np(out), f["out"]) <= tol
+    for key, ref in (("dx", b["dx"]), ("dw1", b["dW1"]), ("dw2", b["dW2"]),
+                     ("dlogits", b["dlogits"]), ("dgate", b["dgate"])):
+        assert rel_inf(to_np(g[key]), ref) <= tol, key
+
+
 def _clobber_scratch():
     """Overwrite the shared recompute scratch, as other layers would between
     a layer's forward and its backward."""
