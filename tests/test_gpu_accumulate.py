@@ -82,11 +82,12 @@ def _layer_in(T, d, E, k, h, seed):
     return inp
 
 
+@pytest.mark.parametrize("shape", [(256, 128, 8, 2, 128), (200, 128, 8, 2, 512)])   # h = d, h > d
 @pytest.mark.parametrize("mx", [False, True])
-def test_layer_accumulates_over_micro_batches(mx):
+def test_layer_accumulates_over_micro_batches(mx, shape):
     """Two micro-batches: the second backward with accumulate_dw adds its
     weight gradients to the first's, exactly (one fp32 add per element)."""
-    T, d, E, k, h = 256, 128, 8, 2, 128
+    T, d, E, k, h = shape
     a = _layer_in(T, d, E, k, h, 21)
     b = _layer_in(T, d, E, k, h, 22)
     w1 = dev(a["w1"], torch.float32 if mx else torch.bfloat16)
@@ -111,7 +112,7 @@ def test_layer_accumulates_over_micro_batches(mx):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("cols", [320, 256])   # a partial last column tile / whole tiles only
+@pytest.mark.parametrize("cols", [320, 256, 96])   # a partial last column tile / whole tiles only / one partial tile
 def test_quantize_both_matches_separate(dt, cols):
     rows = 8 * 192
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
