@@ -52,6 +52,37 @@ def test_quantise_cols_grouped_bit_exact(groups):
     assert np.array_equal(s.cpu().numpy()[:len(so)], so)
 
 
+@pytest.mark.parametrize("dt,mapped", [(torch.bfloat16, False), (torch.bfloat16, True),
+                                        (torch.float32, False)])
+def test_quantise_cols_many_units(dt, mapped):
+    """4096 x 4096 in 8 groups (an empty one, a one-row one): each workgroup of
+    the column quantisers walks several 128-row units, with the next unit's
+    tile (and, with a row map, its row indices) read ahead of the current
+    one's encoding. Column layout bit-exact; the both-layout path too."""
+    rows, cols = 4096, 4096
+    a = synth.normal((rows, cols), 9, 0, 1.0)
+    a[7, :32] = 0.0
+    x = dev(a, dt)
+    go = np.array([0, 300, 300, 1100, 2048, 2049, 3000, 3500, 4096], np.int32)
+    g = torch.from_numpy(go).cuda()
+    if mapped:
+        perm = np.random.default_rng(4).integers(0, rows, rows).astype(np.int32)
+        q, s = moe.mxfp8_quantize(x, 0, g, row_map=torch.from_numpy(perm).cuda())
+        src = to_np(x)[perm]
+    else:
+        q, s = moe.mxfp8_quantize(x, 0, g)
+        src = to_np(x)
+    qo, so = oracle.mxfp8_quantize(src, 0, go)
+    assert np.array_equal(q.cpu().numpy()[:len(qo)], qo)
+    assert np.array_equal(s.cpu().numpy()[:len(so)], so)
+    if not mapped:
+        (q1, s1), (q0, s0) = moe.mxfp8_quantize_both(x, g)
+        q1o, s1o = oracle.mxfp8_quantize(src, 1)
+        assert np.array_equal(q0.cpu().numpy()[:len(qo)], qo)
+        assert np.array_equal(s0.cpu().numpy()[:len(so)], so)
+        assert np.array_equal(q1.cpu().numpy(), q1o) and np.array_equal(s1.cpu().numpy(), s1o)
+
+
 def test_quantise_with_row_map():
     a = _wide((100, 128), 3)
     x = dev(a, torch.bfloat16)
