@@ -217,7 +217,9 @@ moe_status moe_grouped_gemm(const moe_gemm_desc *g, void *stream);
  * GEMM2-wgrad (dW2), GEMM1-dgrad (dx_perm), unpermute-bwd (dX),
  * GEMM1-wgrad (dW1). Saved forward tensors and the three intermediates are
  * caller-owned buffers.
- *   dlogits[t, e] = g_i (dg_i - sum_j g_j dg_j) for e = topk_idx[t, i], and
+ *   dlogits[t, e] = g_i (dg_i - sum_j g_j dg_j) for e = topk_idx[t, i]
+ *   (evaluated as g_i sum_j g_j (dg_i - dg_j), equal since the gates sum to
+ *   one, so a confident router's small gradients lose no precision), and
  *   exactly 0 for unselected experts, with dg_j = <dOut[t], y_perm[row]>.
  * dtype MOE_F32 or MOE_BF16: activations, weights, dOut, dX and the
  * intermediates in that dtype. dW1, dW2, dlogits and dgate are fp32.
@@ -266,7 +268,23 @@ typedef struct moe_bwd_desc {
     void *ws;                      /* scratch, moe_backward_workspace_size bytes */
     size_t ws_bytes;
     int32_t accumulate_dw;         /* 1: dW1, dW2 += this micro-batch's gradients; 0: overwrite */
+    /* Optional (null = none): MOE_BWD_MAX_STAGES hipEvent_t handles (null
+     * entries skipped), created by the caller. Event i is recorded on the
+     * stream right after the call's i-th kernel is enqueued, so a caller can
+     * time each stage on the stream it runs on. Stages, bf16 / f32:
+     *   0 combine-bwd + router-bwd, 1 GEMM2 dgrad + SwiGLU-bwd, 2 GEMM2 wgrad,
+     *   3 GEMM1 dgrad, 4 unpermute-bwd, 5 GEMM1 wgrad;
+     * MXFP8:
+     *   0 combine-bwd + router-bwd, 1 quantise dy (both layouts),
+     *   2 GEMM2 dgrad + SwiGLU-bwd, 3 quantise H' (columns), 4 GEMM2 wgrad,
+     *   5 quantise dAB (both layouts), 6 GEMM1 dgrad, 7 unpermute-bwd,
+     *   8 quantise x[sorted_token] (columns), 9 GEMM1 wgrad.
+     * A stage with no work (T = 0) still records its event. A failed record
+     * returns MOE_ERR_LAUNCH. */
+    void *const *stage_events;
 } moe_bwd_desc;
+
+#define MOE_BWD_MAX_STAGES 10
 
 size_t moe_backward_workspace_size(const moe_bwd_desc *b);
 

@@ -54,7 +54,16 @@ class BwdDesc(ctypes.Structure):
                 ("dout", _P), ("dx", _P), ("dlogits", _P), ("dw1", _P), ("dw2", _P),
                 ("dgate", _P), ("dy_perm", _P), ("dab", _P), ("dx_perm", _P), ("x", _P),
                 ("sorted_token", _P), ("w1t", _P), ("w1t_scale", _P), ("w2t", _P),
-                ("w2t_scale", _P), ("ws", _P), ("ws_bytes", _SZ), ("accumulate_dw", _I32)]
+                ("w2t_scale", _P), ("ws", _P), ("ws_bytes", _SZ), ("accumulate_dw", _I32),
+                ("stage_events", ctypes.POINTER(_P))]
+
+MOE_BWD_MAX_STAGES = 10
+BWD_STAGES = {
+    "bf16": ("combine_bwd", "gemm2_dgrad_swiglu", "gemm2_wgrad", "gemm1_dgrad", "unpermute_bwd",
+             "gemm1_wgrad"),
+    "mxfp8": ("combine_bwd", "quant_dy_both", "gemm2_dgrad_swiglu", "quant_hp_cols", "gemm2_wgrad",
+              "quant_dab_both", "gemm1_dgrad", "unpermute_bwd", "quant_x_cols", "gemm1_wgrad"),
+}
 
 
 def _load():
@@ -198,19 +207,83 @@ def moe_combine(y_perm: torch.Tensor, topk_gate: torch.Tensor, token_pos: torch.
     return out
 
 
+def _need_elems(t, n, dtype, name):
+    """t is a contiguous GPU tensor of `dtype` with at least n elements."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected a contiguous {dtype} GPU tensor, got {t.dtype} "
+                         f"(contiguous={t.is_contiguous()}, device={t.device})")
+    if t.numel() < n:
+        raise ValueError(f"{name}: needs at least {n} elements, has {t.numel()}")
+
+
+_TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_MXFP8: torch.uint8}
+
+
+def _check_gemm_operands(mode, dt, epilogue, A, B, C, offsets, rows, M, N, K, aux, aux_out,
+                         a_scale, b_scale):
+    """Host-side sizes of every operand against what the mode reads and
+    writes (the C ABI sees only pointers, so an undersized tensor would be
+    read or written past its end on the device)."""
+    E = offsets.numel() - 1
+    _need_elems(offsets, E + 1, torch.int32, "offsets")
+    if offsets.device != A.device:
+        raise ValueError("offsets must be on A's device")
+    et = _TORCH_DT[dt]
+    act = torch.bfloat16 if dt == MOE_MXFP8 else et      # stored activations
+    if mode == MOE_GG_WGRAD:
+        if dt == MOE_MXFP8:
+            nb = mxfp8_col_blocks(rows, E)
+            _need_elems(A, nb * 32 * M, et, "A")
+            _need_elems(B, nb * 32 * N, et, "B")
+            _need_elems(a_scale, nb * M, torch.uint8, "a_scale")
+            _need_elems(b_scale, nb * N, torch.uint8, "b_scale")
+        else:
+            _need_elems(A, rows * M, et, "A")
+            _need_elems(B, rows * N, et, "B")
+        _need_elems(C, E * M * N, torch.float32, "C")
+        return
+    _need_elems(A, rows * K, et, "A")
+    _need_elems(B, E * N * K, et, "B")
+    if dt == MOE_MXFP8:
+        _need_elems(a_scale, rows * (K // 32), torch.uint8, "a_scale")
+        _need_elems(b_scale, E * N * (K // 32), torch.uint8, "b_scale")
+    if epilogue == MOE_EPI_SWIGLU_BWD:
+        _need_elems(C, rows * 2 * N, act, "C")
+        _need_elems(aux, rows * 2 * N, act, "aux")
+    else:
+        _need_elems(C, rows * N, act, "C")
+    if epilogue == MOE_EPI_SWIGLU_FWD:
+        _need_elems(aux_out, rows * (N // 2), act, "aux_out")
+
+
 def moe_grouped_gemm(mode: int, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
                      offsets: torch.Tensor, epilogue: int = MOE_EPI_NONE, M: int = 0, N: int = 0,
                      K: int = 0, aux: torch.Tensor | None = None,
                      aux_out: torch.Tensor | None = None, a_scale=None, b_scale=None,
-                     aux_out_scale=None, dtype: int | None = None, accumulate: bool = False):
-    """One grouped GEMM (see moe.h for the modes and epilogues)."""
+                     aux_out_scale=None, dtype: int | None = None, accumulate: bool = False,
+                     rows: int | None = None):
+    """One grouped GEMM (see moe.h for the modes and epilogues). Every
+    operand's dtype and size is checked against the mode before the call.
+    rows = total routed rows (offsets[-1]); it defaults to A.shape[0] and must
+    be given for MXFP8 WGRAD, whose operands are flat column-block arrays."""
+    dt = _dt(A) if dtype is None else dtype
+    if dt not in _TORCH_DT:
+        raise ValueError(f"unsupported GEMM dtype {dt}")
+    if rows is None:
+        if mode == MOE_GG_WGRAD and dt == MOE_MXFP8:
+            raise ValueError("MXFP8 WGRAD: pass rows (the column-block operands are flat)")
+        rows = A.shape[0]
+    _check_gemm_operands(mode, dt, epilogue, A, B, C, offsets, rows, M, N, K, aux, aux_out,
+                         a_scale, b_scale)
     desc = GemmDesc()
     desc.accumulate = 1 if accumulate else 0
     desc.mode = mode
-    desc.dtype = _dt(A) if dtype is None else dtype
+    desc.dtype = dt
     desc.epilogue = epilogue
     desc.n_groups = offsets.numel() - 1
-    desc.rows = A.shape[0]
+    desc.rows = rows
     desc.M, desc.N, desc.K = M, N, K
     desc.offsets = offsets.data_ptr()
     desc.A, desc.B, desc.C = A.data_ptr(), B.data_ptr(), C.data_ptr()
@@ -229,7 +302,7 @@ def moe_grouped_gemm(mode: int, A: torch.Tensor, B: torch.Tensor, C: torch.Tenso
 
 def moe_backward(saved: dict, dout: torch.Tensor, E: int, k: int, d: int, h: int,
                  out: dict | None = None, want_dgate: bool = True, mxfp8: bool = False,
-                 accumulate_dw: bool = False) -> dict:
+                 accumulate_dw: bool = False, stage_events=None) -> dict:
     """Backward of the whole layer. `saved` holds the forward tensors
     (x_perm, ab, hp, y_perm, topk_gate, topk_idx, token_pos, offsets, w1, w2;
     with mxfp8: x, sorted_token, w1t, w1t_scale, w2t, w2t_scale instead of
@@ -266,6 +339,12 @@ def moe_backward(saved: dict, dout: torch.Tensor, E: int, k: int, d: int, h: int
         out["_ws"] = ws
     b.ws = ws.data_ptr() if wsb else None
     b.ws_bytes = wsb
+    if stage_events is not None:
+        # hipEvent_t handles of recorded torch.cuda.Event objects, one per stage
+        arr = (_P * MOE_BWD_MAX_STAGES)(*[ctypes.c_void_p(e.cuda_event) if e is not None else None
+                                          for e in list(stage_events) +
+                                          [None] * (MOE_BWD_MAX_STAGES - len(stage_events))])
+        b.stage_events = ctypes.cast(arr, ctypes.POINTER(_P))
     _check("moe_backward", _lib.moe_backward(ctypes.byref(b), _stream()))
     return out
 
@@ -419,7 +498,7 @@ class _Balance:
 class MoELayer:
     """Forward and backward of the MoE expert layer through the C ABI.
 
-    Buffers are allocated once per (T) and reused across calls, so a step
+    Buffers are allocated once per (T, dtype, device) and reused across calls, so a step
     issues only kernel launches (no allocation, no device->host traffic).
 
     recompute=True trades compute for activation memory (the trade-off the
@@ -444,8 +523,20 @@ class MoELayer:
         self.lb_stats = None
         self._T = None
 
+    def _check_input(self, x, logits):
+        if x.dim() != 2 or x.shape[1] != self.d:
+            raise ValueError(f"x: expected [T, {self.d}], got {tuple(x.shape)}")
+        if x.dtype != self.w1.dtype or self.w2.dtype != self.w1.dtype:
+            raise ValueError(f"x ({x.dtype}) and the weights ({self.w1.dtype}, {self.w2.dtype}) "
+                             "must share one dtype")
+        if x.device != self.w1.device or x.device != self.w2.device or not x.is_cuda:
+            raise ValueError("x and the weights must be on the same GPU")
+        _need(x, (x.shape[0], self.d), x.dtype, "x")
+        _need(logits, (x.shape[0], self.E), torch.float32, "logits")
+
     def _alloc(self, T, dev, dt):
-        if self._T == T:
+        key = (T, dt, str(dev))
+        if self._T == key:
             return
         E, k, d, h = self.E, self.k, self.d, self.h
         R = T * k
@@ -465,13 +556,14 @@ class MoELayer:
         self.y_perm = own("y_perm", (R, d))
         self.out = torch.empty((T, d), dtype=dt, device=dev)
         self.grads = None
-        self._T = T
+        self._T = key
 
     def _gemm1(self, offsets):
         moe_grouped_gemm(MOE_GG_FWD, self.x_perm, self.w1, self.ab, offsets,
                          MOE_EPI_SWIGLU_FWD, N=2 * self.h, K=self.d, aux_out=self.hp)
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor) -> torch.Tensor:
+        self._check_input(x, logits)
         T, d = x.shape
         self._alloc(T, x.device, x.dtype)
         self.x = x
@@ -499,16 +591,21 @@ class MoELayer:
             return meta + _nbytes([self.y_perm])
         return meta + _nbytes([self.x_perm, self.ab, self.hp, self.y_perm])
 
-    def backward(self, dout: torch.Tensor, accumulate_dw: bool = False) -> dict:
+    def backward(self, dout: torch.Tensor, accumulate_dw: bool = False,
+                 stage_events=None) -> dict:
         """accumulate_dw: add this micro-batch's dW1, dW2 to the ones already
-        in self.grads (gradient accumulation between optimizer steps)."""
+        in self.grads (gradient accumulation between optimizer steps).
+        stage_events: optional recorded torch.cuda.Event per backward stage
+        (moe_bwd_desc.stage_events)."""
+        _need(dout, tuple(self.x.shape), self.x.dtype, "dout")
         if self.recompute:
             moe_permute(self.x, self.route["token_pos"], self.x_perm)
             self._gemm1(self.route["offsets"])
         if accumulate_dw and self.grads is None:
             raise ValueError("accumulate_dw needs the gradients of an earlier backward")
         self.grads = moe_backward(self.saved(), dout, self.E, self.k, self.d, self.h,
-                                  out=self.grads, accumulate_dw=accumulate_dw)
+                                  out=self.grads, accumulate_dw=accumulate_dw,
+                                  stage_events=stage_events)
         if self.balance is not None:
             self.balance.backward(self.grads["dlogits"])
         return self.grads
@@ -527,7 +624,7 @@ class MoELayerPadded(MoELayer):
         self.capacity = capacity
 
     def _alloc(self, T, dev, dt):
-        if self._T == T:
+        if self._T == (T, dt, str(dev)):
             return
         super()._alloc(T, dev, dt)
         E, k, d, h, C = self.E, self.k, self.d, self.h, self.capacity
@@ -548,9 +645,11 @@ class MoELayerPadded(MoELayer):
                           dx_perm=torch.empty((P, d), dtype=dt, device=dev))
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor) -> torch.Tensor:
+        self._check_input(x, logits)
         T, d = x.shape
         C = self.capacity
         self._alloc(T, x.device, x.dtype)
+        self.x = x
         r = moe_route(logits, self.k, out=self.route, ws=self.route_ws)
         p = moe_capacity_pad(r, C, out=self.pad)
         moe_permute(x, p["token_pos"], self.x_perm)
@@ -567,9 +666,10 @@ class MoELayerPadded(MoELayer):
         sv["offsets"] = self.pad["offsets"]
         return sv
 
-    def backward(self, dout: torch.Tensor, accumulate_dw: bool = False) -> dict:
+    def backward(self, dout: torch.Tensor, accumulate_dw: bool = False,
+                 stage_events=None) -> dict:
         moe_capacity_zero_rows(self.grads["dy_perm"], self.route["offsets"], self.capacity)
-        return super().backward(dout, accumulate_dw)
+        return super().backward(dout, accumulate_dw, stage_events)
 
 
 class MoELayerMX:
@@ -607,7 +707,8 @@ class MoELayerMX:
             w2.reshape(E * d, h), g2)
 
     def _alloc(self, T, dev):
-        if self._T == T:
+        key = (T, str(dev))
+        if self._T == key:
             return
         E, k, d, h = self.E, self.k, self.d, self.h
         R = T * k
@@ -635,7 +736,7 @@ class MoELayerMX:
         self.out = torch.empty((T, d), **bf)
         self.grads = None
         self.bwd_ws = None
-        self._T = T
+        self._T = key
 
     def _gemm1(self, x, offsets, token_pos):
         """Quantised dispatch of x and GEMM1 + SwiGLU (forward, and again in
@@ -647,6 +748,12 @@ class MoELayerMX:
                          b_scale=self.w1s, dtype=MOE_MXFP8)
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor) -> torch.Tensor:
+        if x.dim() != 2 or x.shape[1] != self.d or x.dtype != torch.bfloat16:
+            raise ValueError(f"x: expected bf16 [T, {self.d}], got {x.dtype} {tuple(x.shape)}")
+        if x.device != self.w1q.device:
+            raise ValueError("x and the weights must be on the same GPU")
+        _need(x, tuple(x.shape), torch.bfloat16, "x")
+        _need(logits, (x.shape[0], self.E), torch.float32, "logits")
         T, d = x.shape
         h = self.h
         self._alloc(T, x.device)
@@ -676,15 +783,18 @@ class MoELayerMX:
             return meta + _nbytes([self.y_perm])
         return meta + _nbytes([self.ab, self.hp, self.y_perm])
 
-    def backward(self, dout: torch.Tensor, accumulate_dw: bool = False) -> dict:
+    def backward(self, dout: torch.Tensor, accumulate_dw: bool = False,
+                 stage_events=None) -> dict:
         """accumulate_dw: add this micro-batch's dW1, dW2 to the ones already
-        in self.grads."""
+        in self.grads. stage_events: as MoELayer.backward."""
+        _need(dout, tuple(self.x.shape), torch.bfloat16, "dout")
         if self.recompute:
             self._gemm1(self.x, self.route["offsets"], self.route["token_pos"])
         if accumulate_dw and self.grads is None:
             raise ValueError("accumulate_dw needs the gradients of an earlier backward")
         self.grads = moe_backward(self.saved(), dout, self.E, self.k, self.d, self.h,
-                                  out=self.grads, mxfp8=True, accumulate_dw=accumulate_dw)
+                                  out=self.grads, mxfp8=True, accumulate_dw=accumulate_dw,
+                                  stage_events=stage_events)
         if self.balance is not None:
             self.balance.backward(self.grads["dlogits"])
         return self.grads

@@ -41,18 +41,15 @@ moe_status load_balance_launch(const float *logits, const int32_t *counts, int64
                                float alpha, float *stats, float *dlogits, void *ws, hipStream_t s);
 size_t load_balance_ws_bytes(int64_t T, int E);
 
+// Queried at every launch (a host-side lookup in the runtime, no device
+// work), so the library holds no mutable state for it.
 int num_cus() {
-    static int cache[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cache[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cache[dev] = n;
-    }
-    return cache[dev];
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        n = 256;
+    return n;
 }
 
 static bool routing_shape_ok(int64_t T, int32_t E, int32_t k) {
@@ -91,6 +88,13 @@ static MxBwdLayout mx_bwd_layout(int64_t R, int d, int h, int E) {
     L.b1_s = L.b1_q + round256(c1);
     L.total = L.b1_s + round256(c1 / 32);
     return L;
+}
+
+// records the caller's stage event i (if any) on s
+static moe_status stage_mark(const moe_bwd_desc *b, int i, hipStream_t s) {
+    if (!b->stage_events || !b->stage_events[i]) return MOE_OK;
+    return hipEventRecord((hipEvent_t)b->stage_events[i], s) == hipSuccess ? MOE_OK
+                                                                             : MOE_ERR_LAUNCH;
 }
 
 }  // namespace moe
@@ -246,7 +250,7 @@ moe_status moe_backward(const moe_bwd_desc *b, void *stream) {
     moe_status st = combine_bwd_launch(b->dout, b->y_perm, b->dtype, b->topk_gate, b->topk_idx,
                                        b->token_pos, b->T, b->d, b->k, b->E, b->dy_perm,
                                        b->dlogits, b->dgate, s);
-    if (st != MOE_OK) return st;
+    if (st != MOE_OK || (st = stage_mark(b, 0, s)) != MOE_OK) return st;
     moe_gemm_desc g;
     memset(&g, 0, sizeof(g));
     g.dtype = b->dtype;
@@ -258,26 +262,30 @@ moe_status moe_backward(const moe_bwd_desc *b, void *stream) {
     g.N = b->h; g.K = b->d;
     g.A = b->dy_perm; g.B = b->w2; g.C = b->dab; g.aux = b->ab;
     if (R > 0 && (st = gemm_launch(&g, s)) != MOE_OK) return st;
+    if ((st = stage_mark(b, 1, s)) != MOE_OK) return st;
     // GEMM2 wgrad: dW2[e] = dy^T H'
     g.mode = MOE_GG_WGRAD; g.epilogue = MOE_EPI_NONE; g.aux = nullptr;
     g.accumulate = b->accumulate_dw;
     g.M = b->d; g.N = b->h; g.K = 0;
     g.A = b->dy_perm; g.B = b->hp; g.C = b->dw2;
-    if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
+    if ((st = gemm_launch(&g, s)) != MOE_OK || (st = stage_mark(b, 2, s)) != MOE_OK) return st;
     // GEMM1 dgrad: dx_perm = dAB . W1[e]
     g.mode = MOE_GG_DGRAD; g.accumulate = 0; g.M = 0; g.N = b->d; g.K = 2 * b->h;
     g.A = b->dab; g.B = b->w1; g.C = b->dx_perm;
     if (R > 0 && (st = gemm_launch(&g, s)) != MOE_OK) return st;
+    if ((st = stage_mark(b, 3, s)) != MOE_OK) return st;
     // unpermute backward: dX[t] = sum_j dx_perm[token_pos[t, j]], straight
     // after dx_perm is written (read back while it is still cached, and ahead
     // of the weight gradient's 2 GiB of fp32 stores)
     if ((st = combine_launch(b->dx_perm, b->dtype, nullptr, b->token_pos, b->T, b->d, b->k, b->dx,
-                             true, s)) != MOE_OK)
+                             true, s)) != MOE_OK ||
+        (st = stage_mark(b, 4, s)) != MOE_OK)
         return st;
     // GEMM1 wgrad: dW1[e] = dAB^T x
     g.mode = MOE_GG_WGRAD; g.accumulate = b->accumulate_dw; g.M = 2 * b->h; g.N = b->d; g.K = 0;
     g.A = b->dab; g.B = b->x_perm; g.C = b->dw1;
-    return gemm_launch(&g, s);
+    if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
+    return stage_mark(b, 5, s);
 }
 
 static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
@@ -313,7 +321,8 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
     // combine backward + router backward (bf16)
     if ((st = combine_bwd_launch(b->dout, b->y_perm, MOE_BF16, b->topk_gate, b->topk_idx,
                                  b->token_pos, b->T, d, b->k, E, b->dy_perm, b->dlogits,
-                                 b->dgate, s)) != MOE_OK)
+                                 b->dgate, s)) != MOE_OK ||
+        (st = stage_mark(b, 0, s)) != MOE_OK)
         return st;
     moe_gemm_desc g;
     memset(&g, 0, sizeof(g));
@@ -325,7 +334,8 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
     if ((st = R > 0 ? mxfp8_quantize_both_launch(b->dy_perm, MOE_BF16, R, d, b->offsets, E, aq, as, b0q,
                                                   b0s, s)
                     : mxfp8_quantize_launch(b->dy_perm, MOE_BF16, R, d, 0, b->offsets, E,
-                                            nullptr, b0q, b0s, s)) != MOE_OK)
+                                            nullptr, b0q, b0s, s)) != MOE_OK ||
+        (st = stage_mark(b, 1, s)) != MOE_OK)
         return st;
     if (R > 0) {
         // GEMM2 dgrad + SwiGLU backward: dy . W2t
@@ -334,19 +344,22 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
         g.C = b->dab; g.aux = b->ab;
         if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
     }
+    if ((st = stage_mark(b, 2, s)) != MOE_OK) return st;
     // GEMM2 wgrad: dy and H' along rows, per expert
     if ((st = mxfp8_quantize_launch(b->hp, MOE_BF16, R, h, 0, b->offsets, E, nullptr, b1q, b1s,
-                                    s)) != MOE_OK)
+                                    s)) != MOE_OK ||
+        (st = stage_mark(b, 3, s)) != MOE_OK)
         return st;
     g.mode = MOE_GG_WGRAD; g.epilogue = MOE_EPI_NONE; g.aux = nullptr; g.M = d; g.N = h; g.K = 0;
     g.accumulate = b->accumulate_dw;
     g.A = b0q; g.a_scale = b0s; g.B = b1q; g.b_scale = b1s; g.C = b->dw2;
-    if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
+    if ((st = gemm_launch(&g, s)) != MOE_OK || (st = stage_mark(b, 4, s)) != MOE_OK) return st;
     // dAB along 2h (GEMM1 dgrad) and along rows per expert (GEMM1 wgrad), one read
     if ((st = R > 0 ? mxfp8_quantize_both_launch(b->dab, MOE_BF16, R, 2 * h, b->offsets, E, aq, as, b0q,
                                                   b0s, s)
                     : mxfp8_quantize_launch(b->dab, MOE_BF16, R, 2 * h, 0, b->offsets, E,
-                                            nullptr, b0q, b0s, s)) != MOE_OK)
+                                            nullptr, b0q, b0s, s)) != MOE_OK ||
+        (st = stage_mark(b, 5, s)) != MOE_OK)
         return st;
     if (R > 0) {
         // GEMM1 dgrad: dAB . W1t
@@ -354,17 +367,21 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
         g.A = aq; g.a_scale = as; g.B = b->w1t; g.b_scale = b->w1t_scale; g.C = b->dx_perm;
         if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
     }
+    if ((st = stage_mark(b, 6, s)) != MOE_OK) return st;
     // unpermute backward, straight after dx_perm is written
     if ((st = combine_launch(b->dx_perm, MOE_BF16, nullptr, b->token_pos, b->T, d, b->k, b->dx,
-                             true, s)) != MOE_OK)
+                             true, s)) != MOE_OK ||
+        (st = stage_mark(b, 7, s)) != MOE_OK)
         return st;
     // GEMM1 wgrad: dAB and x[sorted_token] along rows, per expert
     if ((st = mxfp8_quantize_launch(b->x, MOE_BF16, R, d, 0, b->offsets, E, b->sorted_token, b1q,
-                                    b1s, s)) != MOE_OK)
+                                    b1s, s)) != MOE_OK ||
+        (st = stage_mark(b, 8, s)) != MOE_OK)
         return st;
     g.mode = MOE_GG_WGRAD; g.accumulate = b->accumulate_dw; g.M = 2 * h; g.N = d; g.K = 0;
     g.A = b0q; g.a_scale = b0s; g.B = b1q; g.b_scale = b1s; g.C = b->dw1;
-    return gemm_launch(&g, s);
+    if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
+    return stage_mark(b, 9, s);
 }
 
 size_t mxfp8_col_blocks(int64_t rows, int32_t n_groups) { return moe::mxfp8_col_blocks(rows, n_groups); }

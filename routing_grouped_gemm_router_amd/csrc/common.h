@@ -52,7 +52,7 @@ inline moe_status launch_status() {
     return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
-// Number of compute units of the current device (cached per device).
+// Number of compute units of the current device.
 int num_cus();
 
 }  // namespace moe

@@ -51,13 +51,19 @@ struct GemmArgs {
 // ---------------------------------------------------------------------------
 // tile table shared by the kernels
 
+// Copies offsets[0..E] (E + 1 entries, up to 257) into LDS with a strided
+// loop, so the copy is whole for any block size; ends with a barrier.
+MOE_DEV void load_offsets(const int32_t *offsets, int E, int32_t *s_off) {
+    for (int i = threadIdx.x; i <= E; i += blockDim.x) s_off[i] = offsets[i];
+    __syncthreads();
+}
+
 // Loads offsets[0..E] into s_off and builds s_tile[e] = sum_{e'<e} ceil(c_e'/BM).
-// Needs blockDim.x >= 256 (E <= 256). Returns the total number of m-tiles.
+// The scan needs blockDim.x >= 256 (E <= 256). Returns the total number of m-tiles.
 MOE_DEV int build_tile_table(const int32_t *offsets, int E, int BM, int32_t *s_off,
                              int32_t *s_tile) {
     const int tid = threadIdx.x;
-    if (tid <= E) s_off[tid] = offsets[tid];
-    __syncthreads();
+    load_offsets(offsets, E, s_off);
     int32_t c = tid < E ? (s_off[tid + 1] - s_off[tid] + BM - 1) / BM : 0;
     if (tid < 256) s_tile[tid + 1] = c;
     if (tid == 0) s_tile[0] = 0;
@@ -546,10 +552,7 @@ void gg_mfma(GemmArgs g) {
         // XCDs, the others whole). FP8: s_tile[e] = sum_{e'<e} ceil(c_e'/128), the 128-row step base of
         // each expert in the column-block MXFP8 layout.
         if constexpr (FP8) build_tile_table(g.offsets, E, 128, s_off, s_tile);
-        else {
-            if (tid <= E) s_off[tid] = g.offsets[tid];
-            __syncthreads();
-        }
+        else load_offsets(g.offsets, E, s_off);
         n_tiles = (g.N + BN - 1) / BN;
         const int per_e = ((g.M + BM - 1) / BM) * n_tiles;
         ws = build_wgrad_schedule(s_off, E, per_e, xcd, s_chunk, s_xpre);
@@ -1192,8 +1195,7 @@ __global__ __launch_bounds__(256) void gg_f32(GemmArgs g) {
 
     int n_tiles, total;
     if constexpr (MODE == MOE_GG_WGRAD) {
-        if (tid <= E) s_off[tid] = g.offsets[tid];
-        __syncthreads();
+        load_offsets(g.offsets, E, s_off);
         n_tiles = (g.N + BN - 1) / BN;
         total = E * ((g.M + BM - 1) / BM) * n_tiles;
     } else {

@@ -158,6 +158,11 @@ __global__ __launch_bounds__(256) void combine_rows(const uint4 *__restrict__ y,
 // combine backward with the router backward fused in:
 //   dy_perm[p_j] = round(g_j * dOut[t]),  dg_j = <dOut[t], y_perm[p_j]>
 //   dlogits[t, e_j] = g_j (dg_j - sum_i g_i dg_i); 0 for unselected experts
+// The gates sum to one, so the router term is evaluated as
+//   g_j sum_i g_i (dg_j - dg_i),
+// which equals it exactly but has no cancellation: with one gate near 1
+// (a confident router) the first form subtracts two nearly equal sums and
+// loses about log2(1 / (1 - g)) bits in fp32.
 
 template <bool BF16, int KMAX>
 __global__ __launch_bounds__(256) void combine_bwd_rows(
@@ -208,18 +213,24 @@ __global__ __launch_bounds__(256) void combine_bwd_rows(
             }
         }
     }
-    float s = 0.f;
 #pragma unroll
     for (int j = 0; j < KMAX; j++) {
         dot[j] = wave_sum(dot[j]);
         if (pos[j] < 0) dot[j] = 0.f;   // dropped row: its gate had no effect
-        s = fmaf(g[j], dot[j], s);
+    }
+    float rg[KMAX];                      // router gradient of slot j
+#pragma unroll
+    for (int j = 0; j < KMAX; j++) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < KMAX; i++) s = fmaf(g[i], dot[j] - dot[i], s);
+        rg[j] = g[j] * s;
     }
     for (int e = lane; e < E; e += 64) {
         float v = 0.f;
 #pragma unroll
         for (int j = 0; j < KMAX; j++)
-            if (ex[j] == e) v = g[j] * (dot[j] - s);
+            if (ex[j] == e) v = rg[j];
         dlogits[t * E + e] = v;
     }
     if (dgate && lane == 0) {
