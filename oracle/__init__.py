@@ -26,6 +26,7 @@ the full layer would (every routed row depends only on its token and expert).
 from __future__ import annotations
 
 import ctypes
+import time
 import os
 import subprocess
 
@@ -68,6 +69,8 @@ def _bind(lib):
     lib.oracle_unpermute_bwd.argtypes = [_I64, _I32, _I32, _I32, _P, _P, _P]
     lib.oracle_mxfp8_quantize.argtypes = [_P, _I64, _I64, _I32, _P, _I32, _P, _P]
     lib.oracle_mxfp8_quantize.restype = ctypes.c_int
+    lib.oracle_mxfp8_dequantize.argtypes = [_P, _P, _I64, _I64, _I32, _P, _I32, _P]
+    lib.oracle_mxfp8_dequantize.restype = ctypes.c_int
     lib.oracle_round_bf16.argtypes = [ctypes.c_double]
     lib.oracle_round_bf16.restype = ctypes.c_double
     lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
@@ -276,21 +279,41 @@ def _expert_mats(W, needed):
             for e in range(W.shape[0])]
 
 
+class _Clock:
+    """Adds the wall time of each named stage into `timings` (seconds), when
+    a dict is given; for reporting where the oracle's time goes."""
+
+    def __init__(self, timings):
+        self.t = timings
+        self.t0 = time.perf_counter()
+
+    def lap(self, name):
+        now = time.perf_counter()
+        if self.t is not None:
+            self.t[name] = self.t.get(name, 0.0) + now - self.t0
+        self.t0 = now
+
+
 def layer_forward(inp: dict, k: int, dtype: str, tile_m: int = 128, capacity: int | None = None,
-                  lib=None):
+                  lib=None, timings: dict | None = None):
     """Full forward of the layer. With `capacity`, each expert keeps only its
     first `capacity` rows in token order and the rest contribute nothing (the
-    padded-capacity alternative; gates are not renormalised)."""
+    padded-capacity alternative; gates are not renormalised). `timings`
+    (optional dict) receives the wall seconds of each stage."""
     lib = lib or load()
+    clk = _Clock(timings)
     logits, x, W1, W2 = inp["logits"], inp["x"], inp["w1"], inp["w2"]
     E = W1.shape[0]
     h = W1.shape[1] // 2
     r = route(logits, k, tile_m, lib)
+    clk.lap("route")
     x_perm = np.asarray(x, np.float64)[r["sorted_token"]]
+    clk.lap("permute")
     expert = expert_of_rows(r["counts"])
     needed = set(np.unique(expert).tolist())
     W1s, W2s = _expert_mats(W1, needed), _expert_mats(W2, needed)
     ab, hp, y = rows_fwd(x_perm, expert, W1s, W2s, h, dtype, lib=lib)
+    clk.lap("expert_ffn_fwd")
     gate = r["topk_gate"]
     keep = None
     if capacity is not None:
@@ -298,13 +321,17 @@ def layer_forward(inp: dict, k: int, dtype: str, tile_m: int = 128, capacity: in
         keep = rank < capacity
         gate = np.where(keep, gate, np.float32(0)).astype(np.float32)
     out = combine(gate, r["token_pos"], y, dtype, lib)
+    clk.lap("combine")
     return dict(route=r, x_perm=x_perm, expert=expert, ab=ab, hp=hp, y_perm=y, out=out,
                 keep=keep, W1s=W1s, W2s=W2s)
 
 
-def layer_backward(inp: dict, fwd: dict, k: int, dtype: str, lib=None):
-    """Full backward: dy_perm, dgate, dlogits, dAB, dx_perm, dX, dW1, dW2."""
+def layer_backward(inp: dict, fwd: dict, k: int, dtype: str, lib=None,
+                   timings: dict | None = None):
+    """Full backward: dy_perm, dgate, dlogits, dAB, dx_perm, dX, dW1, dW2.
+    `timings` (optional dict) receives the wall seconds of each stage."""
     lib = lib or load()
+    clk = _Clock(timings)
     r = fwd["route"]
     E = inp["w1"].shape[0]
     h = inp["w1"].shape[1] // 2
@@ -315,13 +342,16 @@ def layer_backward(inp: dict, fwd: dict, k: int, dtype: str, lib=None):
     if keep is not None:
         dg = np.where(keep, dg, 0.0)
     dlogits = router_bwd(r["topk_idx"], gate, dg, E, lib)
+    clk.lap("combine_bwd_router_bwd")
     dab, dxp = rows_bwd(dy, fwd["ab"], fwd["expert"], fwd["W1s"], fwd["W2s"], h, dtype, lib=lib)
     if keep is not None:
         kept_row = np.zeros(len(dy), bool)
         kept_row[r["token_pos"][keep]] = True
         dab[~kept_row] = 0.0
         dxp[~kept_row] = 0.0
+    clk.lap("expert_ffn_dgrad")
     dx = unpermute_bwd(r["token_pos"], dxp, dtype, lib)
+    clk.lap("unpermute_bwd")
     off = r["offsets"]
     d = inp["x"].shape[1]
     dW1 = np.zeros((E, 2 * h, d)); dW2 = np.zeros((E, d, h))
@@ -329,6 +359,7 @@ def layer_backward(inp: dict, fwd: dict, k: int, dtype: str, lib=None):
         a, b = off[e], off[e + 1]
         dW2[e] = wgrad(dy[a:b], fwd["hp"][a:b], lib)
         dW1[e] = wgrad(dab[a:b], fwd["x_perm"][a:b], lib)
+    clk.lap("wgrad")
     return dict(dy_perm=dy, dgate=dg, dlogits=dlogits, dab=dab, dx_perm=dxp, dx=dx,
                 dW1=dW1, dW2=dW2)
 
@@ -395,10 +426,24 @@ def layer_sampled(inp: dict, k: int, dtype: str, tokens, experts, tile_m: int = 
 # (kongchang.com, "caveats behind the numbers").
 
 
+def mxfp8_dequantize(q, s, rows: int, cols: int, axis: int, group_offsets=None, lib=None):
+    """Exact fp64 values, in [rows, cols] order, of mxfp8_quantize's output."""
+    lib = lib or load()
+    go = None if group_offsets is None else _c(group_offsets, np.int32)
+    ng = 0 if go is None else len(go) - 1
+    out = np.empty((rows, cols))
+    rc = lib.oracle_mxfp8_dequantize(_ptr(_c(q, np.uint8)), _ptr(_c(s, np.uint8)), rows, cols, axis,
+                                     _ptr(go), ng, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_mxfp8_dequantize: bad arguments")
+    return out
+
+
 def mx_rows(a, lib=None):
     """Dequantised values of `a` quantised along rows (blocks of 32 columns)."""
-    q, s = mxfp8_quantize(np.asarray(a, np.float32), 1, lib=lib)
-    return mxfp8_dequantize_rowwise(q, s)
+    a = np.asarray(a, np.float32)
+    q, s = mxfp8_quantize(a, 1, lib=lib)
+    return mxfp8_dequantize(q, s, a.shape[0], a.shape[1], 1, lib=lib)
 
 
 def mx_cols(a, lib=None):
@@ -406,8 +451,9 @@ def mx_cols(a, lib=None):
     one group), returned in a's own [rows, cols] layout."""
     a = np.asarray(a, np.float32)
     rows, cols = a.shape
-    q, s = mxfp8_quantize(a, 0, np.array([0, rows], np.int32), lib=lib)
-    return mx_cols_dequantize(q, s, np.array([0, rows], np.int32), cols)
+    go = np.array([0, rows], np.int32)
+    q, s = mxfp8_quantize(a, 0, go, lib=lib)
+    return mxfp8_dequantize(q, s, rows, cols, 0, go, lib=lib)
 
 
 def mx_cols_dequantize(q, s, group_offsets, cols):
@@ -420,49 +466,95 @@ def mx_cols_dequantize(q, s, group_offsets, cols):
         n = go[g + 1] - go[g]
         nb = 4 * (-(-n // 128))
         if nb:
-            qg = q[bb * 32 * cols:(bb + nb) * 32 * cols].reshape(cols, nb * 32)[:, :n]
+            qg = q[bb * 32 * cols:(bb + nb) * 32 * cols].reshape(cols, nb, 32)
             sg = s[bb * cols:(bb + nb) * cols].reshape(cols, nb).astype(np.int64)
-            sc = np.ldexp(1.0, np.repeat(sg, 32, axis=1)[:, :n] - 127)
-            out[go[g]:go[g + 1]] = (tab[qg] * sc).T
+            v = tab[qg] * np.ldexp(1.0, sg - 127)[:, :, None]      # [cols, nb, 32]
+            out[go[g]:go[g + 1]] = v.reshape(cols, nb * 32)[:, :n].T
         bb += nb
     return out
 
 
-def _mx_weights(W1, W2, experts, lib=None):
-    """Per expert: W1 along d, W2 along h (forward), W1 along 2h and W2 along d
-    (backward), all dequantised from the fp32 masters."""
+def _mx_weights_fwd(W1, W2, experts, lib=None):
+    """Per expert in `experts`: W1 along d and W2 along h (the forward GEMMs'
+    operands), dequantised from the fp32 masters; None for other experts."""
     E = W1.shape[0]
     w1f = [mx_rows(W1[e], lib) if e in experts else None for e in range(E)]
     w2f = [mx_rows(W2[e], lib) if e in experts else None for e in range(E)]
+    return w1f, w2f
+
+
+def _mx_weights_bwd(W1, W2, experts, lib=None):
+    """Per expert in `experts`: W1 along 2h and W2 along d (the dgrads'
+    operands), dequantised from the fp32 masters; None for other experts."""
+    E = W1.shape[0]
     w1b = [mx_cols(W1[e], lib) if e in experts else None for e in range(E)]
     w2b = [mx_cols(W2[e], lib) if e in experts else None for e in range(E)]
-    return w1f, w2f, w1b, w2b
+    return w1b, w2b
 
 
-def _mx_layer_rows(inp, k, rows, r, lib, backward):
-    """MXFP8 layer values for the routed rows `rows` (sorted positions)."""
+def _gemm2_operand(hp, lib=None):
+    """H' quantised along h: what GEMM2 consumes."""
+    return mx_rows(hp, lib)
+
+
+def _expert_chunks(expert, size):
+    """(experts, row indices) for blocks of up to `size` distinct experts.
+    Each routed row depends only on its token and its expert, so the rows can
+    be taken a block at a time with only that block's weights dequantised."""
+    uniq = np.unique(expert)
+    for i in range(0, len(uniq), size):
+        es = uniq[i:i + size]
+        yield set(int(e) for e in es), np.flatnonzero(np.isin(expert, es))
+
+
+def _mx_layer_rows(inp, k, rows, r, lib, backward, chunk=8, progress=None):
+    """MXFP8 layer values for the routed rows `rows` (sorted positions): the
+    forward (AB, H', y) and, with backward, dy, dAB and dx_perm. `progress`
+    (optional callable) gets a line after each block of experts."""
+    note = progress or (lambda msg: None)
     W1, W2 = inp["w1"], inp["w2"]
     h = W1.shape[1] // 2
-    expert_all = expert_of_rows(r["counts"])
-    expert = expert_all[rows]
-    needed = set(np.unique(expert).tolist())
-    w1f, w2f, w1b, w2b = _mx_weights(W1, W2, needed, lib)
+    d = W2.shape[1]
+    expert = expert_of_rows(r["counts"])[rows]
     src = r["sorted_token"][rows]
     x = np.asarray(inp["x"], np.float32)
-    xq = mx_rows(x[np.unique(src)], lib)                     # x quantised along d before dispatch
-    xq_full = {int(t): i for i, t in enumerate(np.unique(src))}
-    x_rows = xq[[xq_full[int(t)] for t in src]]
-    ab, hp, _ = rows_fwd(x_rows, expert, w1f, w2f, h, "bf16", lib=lib)
-    hq = mx_rows(hp, lib)                                    # H' along h for GEMM2
-    _, _, y = rows_fwd(x_rows, expert, w1f, w2f, h, "bf16", hp_in=hq, lib=lib)
-    res = dict(rows=rows, expert=expert, src=src, ab=ab, hp=hp, y=y,
-               w=(w1f, w2f, w1b, w2b))
+    toks = np.unique(src)
+    xq = mx_rows(x[toks], lib)                               # x quantised along d before dispatch
+    x_rows = xq[np.searchsorted(toks, src)]
+    n = len(rows)
+    ab, hp, y = np.empty((n, 2 * h)), np.empty((n, h)), np.empty((n, d))
+    for needed, sel in _expert_chunks(expert, chunk):
+        w1f, w2f = _mx_weights_fwd(W1, W2, needed, lib)
+        ab[sel], hp[sel], _ = rows_fwd(x_rows[sel], expert[sel], w1f, w2f, h, "bf16", lib=lib)
+        hq = _gemm2_operand(hp[sel], lib)                    # H' along h for GEMM2
+        y[sel] = rows_fwd(x_rows[sel], expert[sel], w1f, w2f, h, "bf16", hp_in=hq, lib=lib)[2]
+        note(f"oracle mxfp8 forward: experts {min(needed)}..{max(needed)} done")
+    res = dict(rows=rows, expert=expert, src=src, ab=ab, hp=hp, y=y)
+    if not backward:
+        return res
+    dout = np.asarray(inp["dout"], np.float64)
+    g_row = r["topk_gate"][src, r["sorted_slot"][rows]]
+    # dy rows: round(g * dOut[t]) via the combine-bwd routine on a one-slot view
+    dy, _ = combine_bwd(g_row.astype(np.float32)[:, None], np.arange(n, dtype=np.int32)[:, None],
+                        dout[src], y, "bf16", lib)
+    dyq = mx_rows(dy, lib)                                   # dy along d for GEMM2 dgrad
+    dab, dxp = np.empty((n, 2 * h)), np.empty((n, d))
+    for needed, sel in _expert_chunks(expert, chunk):
+        w1b, w2b = _mx_weights_bwd(W1, W2, needed, lib)
+        dab[sel] = rows_bwd(dyq[sel], ab[sel], expert[sel], w1b, w2b, h, "bf16", lib=lib)[0]
+        dabq = mx_rows(dab[sel], lib)                        # dAB along 2h for GEMM1 dgrad
+        dxp[sel] = rows_bwd(dyq[sel], ab[sel], expert[sel], w1b, w2b, h, "bf16", dab_in=dabq,
+                            lib=lib)[1]
+        note(f"oracle mxfp8 backward: experts {min(needed)}..{max(needed)} done")
+    res.update(dy=dy, dab=dab, dx_perm=dxp)
     return res
 
 
-def layer_mx(inp: dict, k: int, tokens=None, experts=None, backward: bool = True, lib=None):
+def layer_mx(inp: dict, k: int, tokens=None, experts=None, backward: bool = True, lib=None,
+             progress=None):
     """The MXFP8 layer, forward (+ backward) for the rows of `tokens` (all if
-    None) and the weight gradients of `experts` (all if None)."""
+    None) and the weight gradients of `experts` (all if None). `progress`
+    (optional callable) gets a line as each block of experts is done."""
     lib = lib or load()
     logits, x, W1, W2 = inp["logits"], inp["x"], inp["w1"], inp["w2"]
     E = W1.shape[0]
@@ -476,7 +568,7 @@ def layer_mx(inp: dict, k: int, tokens=None, experts=None, backward: bool = True
     exp_rows = np.concatenate([np.arange(r["offsets"][e], r["offsets"][e + 1]) for e in experts]) \
         if len(experts) else np.zeros(0, np.int64)
     rows = np.unique(np.concatenate([tok_rows, exp_rows]).astype(np.int64))
-    f = _mx_layer_rows(inp, k, rows, r, lib, backward)
+    f = _mx_layer_rows(inp, k, rows, r, lib, backward, progress=progress)
     row_index = {int(p): i for i, p in enumerate(rows)}
     pos_c = np.array([[row_index[int(p)] for p in r["token_pos"][t]] for t in tokens], np.int32)
     gate_s = r["topk_gate"][tokens]
@@ -484,19 +576,11 @@ def layer_mx(inp: dict, k: int, tokens=None, experts=None, backward: bool = True
     res = dict(route=r, rows=rows, out=out, ab=f["ab"], hp=f["hp"], y=f["y"])
     if not backward:
         return res
-    w1f, w2f, w1b, w2b = f["w"]
     dout = np.asarray(inp["dout"], np.float64)
-    src, slot, expert = f["src"], r["sorted_slot"][rows], f["expert"]
-    g_row = r["topk_gate"][src, slot]
-    dy, _ = combine_bwd(g_row.astype(np.float32)[:, None],
-                        np.arange(len(rows), dtype=np.int32)[:, None], dout[src], f["y"], "bf16",
-                        lib)
+    src = f["src"]
+    dy, dab, dxp = f["dy"], f["dab"], f["dx_perm"]
     _, dg = combine_bwd(gate_s, pos_c, dout[tokens], f["y"], "bf16", lib)
     dlogits = router_bwd(r["topk_idx"][tokens], gate_s, dg, E, lib)
-    dyq = mx_rows(dy, lib)                                   # dy along d for GEMM2 dgrad
-    dab, _ = rows_bwd(dyq, f["ab"], expert, w1b, w2b, h, "bf16", lib=lib)
-    dabq = mx_rows(dab, lib)                                 # dAB along 2h for GEMM1 dgrad
-    _, dxp = rows_bwd(dyq, f["ab"], expert, w1b, w2b, h, "bf16", dab_in=dabq, lib=lib)
     dx = unpermute_bwd(pos_c, dxp, "bf16", lib)
     xb = np.asarray(x, np.float32)                           # bf16 values of the layer input
     dW1, dW2 = {}, {}
@@ -510,6 +594,8 @@ def layer_mx(inp: dict, k: int, tokens=None, experts=None, backward: bool = True
         # wgrad operands along rows, blocks restarting at the expert's first row
         dW2[e] = wgrad(mx_cols(dy[sel], lib), mx_cols(f["hp"][sel], lib), lib)
         dW1[e] = wgrad(mx_cols(dab[sel], lib), mx_cols(xb[src[sel]], lib), lib)
+        if progress:
+            progress(f"oracle mxfp8 weight gradients of expert {e} done")
     res.update(dy=dy, dgate=dg, dlogits=dlogits, dab=dab, dx_perm=dxp, dx=dx, dW1=dW1, dW2=dW2)
     return res
 

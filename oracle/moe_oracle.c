@@ -421,21 +421,53 @@ uint8_t oracle_mx_scale(double amax) {
  *               scale[bb_g*cols + c*nb_g + b] = block b of column c of group g
  *               (blocks wholly past len_g hold scale byte 0).
  * Returns 0, or -1 on bad arguments. */
+/* One 32-element block of row r (axis 1). */
+struct mxq_rows_ctx { const float *in; int64_t cols; uint8_t *q, *scale; };
+static void mxq_rows_body(int64_t r, void *vc) {
+    const struct mxq_rows_ctx *c = (const struct mxq_rows_ctx *)vc;
+    const int64_t cols = c->cols;
+    for (int64_t b = 0; b < cols / 32; b++) {
+        const float *v = c->in + r * cols + b * 32;
+        double amax = 0.0;
+        for (int i = 0; i < 32; i++) if (fabs((double)v[i]) > amax) amax = fabs((double)v[i]);
+        uint8_t sb = oracle_mx_scale(amax);
+        c->scale[r * (cols / 32) + b] = sb;
+        for (int i = 0; i < 32; i++)
+            c->q[r * cols + b * 32 + i] = oracle_e4m3_encode(ldexp((double)v[i], 127 - sb));
+    }
+}
+
+/* Every block of column col of one group (axis 0). */
+struct mxq_cols_ctx { const float *in; int64_t cols, row0, len, nb; uint8_t *qg, *sg; };
+static void mxq_cols_body(int64_t col, void *vc) {
+    const struct mxq_cols_ctx *c = (const struct mxq_cols_ctx *)vc;
+    const int64_t cols = c->cols, len = c->len, nb = c->nb;
+    for (int64_t b = 0; b < nb; b++) {
+        int64_t i0 = b * 32, i1 = i0 + 32 < len ? i0 + 32 : len;
+        double amax = 0.0;
+        for (int64_t i = i0; i < i1; i++) {
+            double v = fabs((double)c->in[(c->row0 + i) * cols + col]);
+            if (v > amax) amax = v;
+        }
+        uint8_t sb = oracle_mx_scale(amax);
+        c->sg[col * nb + b] = sb;
+        for (int64_t i = i0; i < i0 + 32; i++)
+            c->qg[col * nb * 32 + i] = i < i1
+                ? oracle_e4m3_encode(ldexp((double)c->in[(c->row0 + i) * cols + col], 127 - sb))
+                : 0;
+    }
+}
+
+/* Blocks are independent and each is written by one thread (rows for axis 1,
+ * columns of a group for axis 0), so the bytes do not depend on the thread
+ * count. */
 int oracle_mxfp8_quantize(const float *in, int64_t rows, int64_t cols, int32_t axis,
                           const int32_t *group_offsets, int32_t n_groups,
                           uint8_t *q, uint8_t *scale) {
     if (axis == 1) {
         if (cols % 32) return -1;
-        for (int64_t r = 0; r < rows; r++)
-            for (int64_t b = 0; b < cols / 32; b++) {
-                const float *v = in + r * cols + b * 32;
-                double amax = 0.0;
-                for (int i = 0; i < 32; i++) if (fabs((double)v[i]) > amax) amax = fabs((double)v[i]);
-                uint8_t sb = oracle_mx_scale(amax);
-                scale[r * (cols / 32) + b] = sb;
-                for (int i = 0; i < 32; i++)
-                    q[r * cols + b * 32 + i] = oracle_e4m3_encode(ldexp((double)v[i], 127 - sb));
-            }
+        struct mxq_rows_ctx c = {in, cols, q, scale};
+        parallel_for(rows, mxq_rows_body, &c);
         return 0;
     }
     if (axis != 0) return -1;
@@ -445,23 +477,47 @@ int oracle_mxfp8_quantize(const float *in, int64_t rows, int64_t cols, int32_t a
     int64_t bb = 0;
     for (int g = 0; g < ng; g++) {
         int64_t len = go[g + 1] - go[g], nb = 4 * ((len + 127) / 128);
-        uint8_t *qg = q + bb * 32 * cols;
-        uint8_t *sg = scale + bb * cols;
-        for (int64_t c = 0; c < cols; c++)
-            for (int64_t b = 0; b < nb; b++) {
-                int64_t i0 = b * 32, i1 = i0 + 32 < len ? i0 + 32 : len;
-                double amax = 0.0;
-                for (int64_t i = i0; i < i1; i++) {
-                    double v = fabs((double)in[(go[g] + i) * cols + c]);
-                    if (v > amax) amax = v;
-                }
-                uint8_t sb = oracle_mx_scale(amax);
-                sg[c * nb + b] = sb;
-                for (int64_t i = i0; i < i0 + 32; i++)
-                    qg[c * nb * 32 + i] = i < i1
-                        ? oracle_e4m3_encode(ldexp((double)in[(go[g] + i) * cols + c], 127 - sb))
-                        : 0;
-            }
+        struct mxq_cols_ctx c = {in, cols, go[g], len, nb, q + bb * 32 * cols, scale + bb * cols};
+        if (nb) parallel_for(cols, mxq_cols_body, &c);
+        bb += nb;
+    }
+    return 0;
+}
+
+/* Exact values of an MXFP8 tensor in [rows, cols] order (the inverse of
+ * oracle_mxfp8_quantize's layouts): out[r, c] = E4M3 value * 2^(scale - 127). */
+struct mxd_ctx { const uint8_t *q, *scale; int64_t cols, row0, len, nb; double *out; int axis; };
+static void mxd_rows_body(int64_t r, void *vc) {
+    const struct mxd_ctx *c = (const struct mxd_ctx *)vc;
+    for (int64_t j = 0; j < c->cols; j++)
+        c->out[r * c->cols + j] = ldexp(oracle_e4m3_decode(c->q[r * c->cols + j]),
+                                        (int)c->scale[r * (c->cols / 32) + j / 32] - 127);
+}
+static void mxd_cols_body(int64_t col, void *vc) {
+    const struct mxd_ctx *c = (const struct mxd_ctx *)vc;
+    for (int64_t i = 0; i < c->len; i++)
+        c->out[(c->row0 + i) * c->cols + col] =
+            ldexp(oracle_e4m3_decode(c->q[col * c->nb * 32 + i]),
+                  (int)c->scale[col * c->nb + i / 32] - 127);
+}
+int oracle_mxfp8_dequantize(const uint8_t *q, const uint8_t *scale, int64_t rows, int64_t cols,
+                            int32_t axis, const int32_t *group_offsets, int32_t n_groups,
+                            double *out) {
+    if (axis == 1) {
+        if (cols % 32) return -1;
+        struct mxd_ctx c = {q, scale, cols, 0, rows, 0, out, 1};
+        parallel_for(rows, mxd_rows_body, &c);
+        return 0;
+    }
+    if (axis != 0) return -1;
+    int32_t single[2] = {0, (int32_t)rows};
+    const int32_t *go = group_offsets ? group_offsets : single;
+    int32_t ng = group_offsets ? n_groups : 1;
+    int64_t bb = 0;
+    for (int g = 0; g < ng; g++) {
+        int64_t len = go[g + 1] - go[g], nb = 4 * ((len + 127) / 128);
+        struct mxd_ctx c = {q + bb * 32 * cols, scale + bb * cols, cols, go[g], len, nb, out, 0};
+        if (nb) parallel_for(cols, mxd_cols_body, &c);
         bb += nb;
     }
     return 0;

@@ -74,21 +74,15 @@ def test_wiring_mistakes_are_caught(mutation, monkeypatch):
     inp = _inp()
     ref = brute.mx_layer(inp["logits"], inp["x"], inp["w1"], inp["w2"], inp["dout"], 2)
     if mutation == "hp_not_quantised":
-        real = oracle.mx_rows
-        calls = {"n": 0}
-
-        def fake(a, lib=None):
-            calls["n"] += 1
-            return np.asarray(a, np.float64) if calls["n"] == 3 else real(a, lib)
-        monkeypatch.setattr(oracle, "mx_rows", fake)
+        monkeypatch.setattr(oracle, "_gemm2_operand", lambda a, lib=None: np.asarray(a, np.float64))
     elif mutation == "w2_wrong_axis":
-        real_w = oracle._mx_weights
+        real_w = oracle._mx_weights_bwd
 
         def fake_w(W1, W2, experts, lib=None):
-            w1f, w2f, w1b, w2b = real_w(W1, W2, experts, lib)
-            return w1f, w2f, w1b, [oracle.mx_rows(W2[e]) if e in experts else None
-                                   for e in range(W2.shape[0])]
-        monkeypatch.setattr(oracle, "_mx_weights", fake_w)
+            w1b, _ = real_w(W1, W2, experts, lib)
+            return w1b, [oracle.mx_rows(W2[e]) if e in experts else None
+                         for e in range(W2.shape[0])]
+        monkeypatch.setattr(oracle, "_mx_weights_bwd", fake_w)
     else:
         real_c = oracle.mx_cols
         monkeypatch.setattr(oracle, "mx_cols", lambda a, lib=None: oracle.mx_rows(a, lib)
@@ -98,3 +92,18 @@ def test_wiring_mistakes_are_caught(mutation, monkeypatch):
            [_rel(m["dW1"][e], ref["dW1"][e]) for e in range(4)] + \
            [_rel(m["dW2"][e], ref["dW2"][e]) for e in range(4)]
     assert max(errs) > 2e-2, mutation
+
+
+def test_expert_chunking_leaves_values_unchanged():
+    """The MXFP8 layer takes its rows a few experts at a time (only those
+    experts' dequantised weights are held): every chunk size gives the same
+    bits, since each routed row depends only on its token and expert."""
+    inp = _inp(T=60, d=64, E=6, k=3, h=32)
+    r = oracle.route(inp["logits"], 3)
+    rows = np.arange(60 * 3)
+    lib = oracle.load()
+    ref = oracle._mx_layer_rows(inp, 3, rows, r, lib, True, chunk=6)
+    for chunk in (1, 4):
+        got = oracle._mx_layer_rows(inp, 3, rows, r, lib, True, chunk=chunk)
+        for key in ("ab", "hp", "y", "dy", "dab", "dx_perm"):
+            assert np.array_equal(got[key], ref[key]), (chunk, key)

@@ -118,3 +118,35 @@ def test_axis0_grouped_layout(groups):
         assert np.all(qg[:, n:] == 0)
         bb += nb
     assert len(s) == bb * cols
+
+
+def test_quantise_bytes_independent_of_threads():
+    """The quantiser splits blocks over threads; each block is written by one
+    thread, so the bytes are the same for any thread count."""
+    a = (np.random.default_rng(3).standard_normal((300, 160)) *
+         np.exp(np.random.default_rng(4).uniform(-6, 6, (300, 1)))).astype(np.float32)
+    go = np.array([0, 7, 7, 130, 300], np.int32)
+    n0 = oracle.threads()
+    try:
+        res = []
+        for n in (1, 5):
+            oracle.set_threads(n)
+            res.append((oracle.mxfp8_quantize(a, 1), oracle.mxfp8_quantize(a, 0, go)))
+    finally:
+        oracle.set_threads(n0)
+    for (q1, s1), (q2, s2) in zip(res[0], res[1]):
+        assert np.array_equal(q1, q2) and np.array_equal(s1, s2)
+
+
+def test_dequantize_matches_numpy_forms():
+    """The C dequantiser against the numpy decode-table forms of both layouts
+    (row blocks; column blocks with groups, a short last block, an empty group)."""
+    a = (np.random.default_rng(5).standard_normal((260, 96)) *
+         np.exp(np.random.default_rng(6).uniform(-20, 20, (260, 1)))).astype(np.float32)
+    q, s = oracle.mxfp8_quantize(a, 1)
+    assert np.array_equal(oracle.mxfp8_dequantize(q, s, 260, 96, 1),
+                          oracle.mxfp8_dequantize_rowwise(q, s))
+    go = np.array([0, 33, 33, 200, 260], np.int32)
+    q, s = oracle.mxfp8_quantize(a, 0, go)
+    assert np.array_equal(oracle.mxfp8_dequantize(q, s, 260, 96, 0, go),
+                          oracle.mx_cols_dequantize(q, s, go, 96))
