@@ -13,7 +13,13 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long CPU test")
 
 
-def pytest_collection_modifyitems(config, items):
-    # GPU tests must not silently pass without a GPU: they are skipped only when
-    # the marker is deselected; when selected on a machine without a GPU they fail.
-    pass
+@pytest.fixture(autouse=True)
+def _gpu_required(request):
+    """A selected `gpu` test fails (it is not skipped) when no GPU is visible:
+    a GPU suite run on a machine without one must not report success."""
+    if request.node.get_closest_marker("gpu") is not None:
+        import torch
+
+        if not torch.cuda.is_available():
+            pytest.fail("gpu test selected but no GPU is visible", pytrace=False)
+    yield

@@ -66,10 +66,10 @@ def test_wgrad_accumulate_mxfp8():
     c0 = torch.randn(E, M, N, device="cuda")
     over = torch.full((E, M, N), float("nan"), device="cuda")
     moe.moe_grouped_gemm(moe.MOE_GG_WGRAD, aq, bq, over, offd, M=M, N=N, a_scale=as_,
-                         b_scale=bs, dtype=moe.MOE_MXFP8)
+                         b_scale=bs, dtype=moe.MOE_MXFP8, rows=R)
     acc = c0.clone()
     moe.moe_grouped_gemm(moe.MOE_GG_WGRAD, aq, bq, acc, offd, M=M, N=N, a_scale=as_,
-                         b_scale=bs, dtype=moe.MOE_MXFP8, accumulate=True)
+                         b_scale=bs, dtype=moe.MOE_MXFP8, accumulate=True, rows=R)
     torch.cuda.synchronize()
     assert torch.equal(acc, c0 + over)
     assert torch.equal(acc[1], c0[1])

@@ -206,13 +206,24 @@ def test_mxfp8_gemm_stages(shape):
     moe.moe_grouped_gemm(moe.MOE_GG_DGRAD, u8(dq), u8(w1tq), dxp, offd, N=d, K=2 * h,
                          a_scale=u8(ds), b_scale=u8(w1ts), dtype=moe.MOE_MXFP8)
     assert rel_inf(to_np(dxp), dx_ref) <= TOL["bf16"]
-    # wgrads on column-block operands
+    # wgrads on column-block operands, in buffers of the size the library's
+    # contract asks for (mxfp8_col_blocks blocks: the kernel may read a few
+    # scale bytes past the last used block)
+    nbw = moe.mxfp8_col_blocks(R, E)
+
+    def sized(a, per_block):
+        buf = np.zeros(nbw * per_block, np.uint8)
+        buf[:a.size] = a.reshape(-1)
+        return buf
+
     for (lhs, rhs, M, N) in ((dy, hp_ref, d, h), (dab_ref, x_perm, 2 * h, d)):
         aq, as_ = oracle.mxfp8_quantize(lhs, 0, off)
         bq, bs = oracle.mxfp8_quantize(rhs, 0, off)
+        aq, as_ = sized(aq, 32 * M), sized(as_, M)
+        bq, bs = sized(bq, 32 * N), sized(bs, N)
         dw = torch.full((E, M, N), float("nan"), device="cuda")
         moe.moe_grouped_gemm(moe.MOE_GG_WGRAD, u8(aq), u8(bq), dw, offd, M=M, N=N,
-                             a_scale=u8(as_), b_scale=u8(bs), dtype=moe.MOE_MXFP8)
+                             a_scale=u8(as_), b_scale=u8(bs), dtype=moe.MOE_MXFP8, rows=R)
         for e in range(E):
             o0, o1 = off[e], off[e + 1]
             if o1 == o0:
@@ -279,6 +290,36 @@ def test_mxfp8_layer_end_to_end(shape):
             assert rel_inf(dw2[e], ref2[e]) <= tol, e
 
 
+@pytest.mark.parametrize("case", ["one_hot", "two_hot"])
+def test_mxfp8_hot_expert_split_wgrad(case):
+    """The MXFP8 weight gradients' hot-expert path (an expert with more than
+    twice the mean rows split over all XCDs; its 8- and 16-tile dW2 / dW1
+    meet the split's condition) against the oracle, expert by expert."""
+    T, d, E, k, h = 512, 1024, 8, 2, 256
+    inp = _mx_inputs(T, d, E, k, h, seed=23)
+    if case == "one_hot":           # every token's first choice is expert 3
+        inp["logits"][:, 3] += 10.0
+    else:                           # experts 2 and 5 take every token; the others none
+        inp["logits"][:, 2] += 20.0
+        inp["logits"][:, 5] += 10.0
+    m = oracle.layer_mx(inp, k)
+    counts = m["route"]["counts"]
+    thresh = 2 * -(-(T * k) // E)
+    assert [e for e in range(E) if counts[e] > thresh] == ([3] if case == "one_hot" else [2, 5])
+    layer, out, g = _run_mx(inp, k)
+    tol = TOL["mxfp8"]
+    assert rel_inf(to_np(out), m["out"]) <= tol
+    assert rel_inf(to_np(g["dx"]), m["dx"]) <= tol
+    assert rel_inf(to_np(g["dlogits"]), m["dlogits"]) <= tol
+    dw1, dw2 = to_np(g["dw1"]), to_np(g["dw2"])
+    for e in range(E):
+        if counts[e] == 0:
+            assert np.all(dw1[e] == 0) and np.all(dw2[e] == 0), e
+            continue
+        assert rel_inf(dw1[e], m["dW1"][e]) <= tol, e
+        assert rel_inf(dw2[e], m["dW2"][e]) <= tol, e
+
+
 @pytest.mark.parametrize("shape,empty", [((1, 128, 1, 1, 128), None),    # one token, one expert
                                          ((3, 128, 8, 8, 128), None),    # k = E
                                          ((200, 256, 6, 2, 128), -1),    # last expert empty
@@ -323,9 +364,11 @@ def test_mxfp8_recompute_matches_saved(shape):
     assert layer.held_bytes() < base.held_bytes()
 
 
+@pytest.mark.timeout(900)
 def test_mxfp8_full_size_sampled():
     """The 32768-token, d=4096, E=128, h=2048 workload in the launch
-    configuration the bench times; a few tokens and one expert are checked."""
+    configuration the bench times: 256 sampled tokens (out, dX, dlogits) and
+    the weight gradients of the hottest, a median and three random experts."""
     w = synth.WORKLOADS["e128_mxfp8"]
     d_in = synth.device_inputs(w, seed=0)
     layer = moe.MoELayerMX(d_in["w1"], d_in["w2"], w.k)
@@ -333,11 +376,14 @@ def test_mxfp8_full_size_sampled():
     g = layer.backward(d_in["dout"])
     torch.cuda.synchronize()
     counts = layer.route["counts"].cpu().numpy()
-    toks = synth.sample_indices(w.T, 3, seed=5)
+    toks = synth.sample_indices(w.T, 256, seed=5)
     nz = np.flatnonzero(counts)
-    med = int(nz[np.argsort(counts[nz])[len(nz) // 2]])
+    hot = int(np.argmax(counts))
+    med = int(nz[np.argsort(counts[nz], kind="stable")[len(nz) // 2]])
+    rest = np.array(sorted(set(nz.tolist()) - {hot, med}))
+    exps = sorted({hot, med} | {int(rest[i]) for i in synth.sample_indices(len(rest), 3, seed=6)})
     idx = layer.route["topk_idx"].cpu().numpy()
-    needed = sorted(set(idx[toks].reshape(-1).tolist()) | {med})
+    needed = sorted(set(idx[toks].reshape(-1).tolist()) | set(exps))
     # host copies of only the inputs the sample needs
     host = dict(logits=to_np(d_in["logits"]), x=to_np(d_in["x"]), dout=to_np(d_in["dout"]))
     E = w.E
@@ -347,10 +393,23 @@ def test_mxfp8_full_size_sampled():
         w1[e] = to_np(d_in["w1"][e])
         w2[e] = to_np(d_in["w2"][e])
     host.update(w1=w1, w2=w2)
-    m = oracle.layer_mx(host, w.k, toks, [med])
+    m = oracle.layer_mx(host, w.k, toks, exps, progress=lambda msg: print(msg, flush=True))
+    assert np.array_equal(m["route"]["counts"], counts)
     tol = TOL["mxfp8"]
     assert rel_inf(to_np(out)[toks], m["out"]) <= tol
     assert rel_inf(to_np(g["dx"])[toks], m["dx"]) <= tol
     assert rel_inf(to_np(g["dlogits"])[toks], m["dlogits"]) <= tol
-    assert rel_inf(to_np(g["dw1"][med]), m["dW1"][med]) <= tol
-    assert rel_inf(to_np(g["dw2"][med]), m["dW2"][med]) <= tol
+    # weight gradients with E = 128: each expert's slice by the relative
+    # Frobenius norm, as in the end-to-end check with more than 16 experts.
+    # Each side quantises its own bf16 dAB and dy, which differ by one bf16
+    # rounding in a few percent of the elements (the matrix core's fp8 dot
+    # products are not summed exactly in fp32); where that moves a value
+    # across an E4M3 step, one term of an expert's sum moves by up to an
+    # eighth, so a slice's infinity norm can reach the tolerance while its
+    # Frobenius error stays far below it. The infinity norms are printed.
+    for e in exps:
+        g1, g2 = to_np(g["dw1"][e]), to_np(g["dw2"][e])
+        f1, f2 = rel_fro(g1, m["dW1"][e]), rel_fro(g2, m["dW2"][e])
+        print(f"expert {e} rows {counts[e]}: dW1 fro {f1:.2e} inf {rel_inf(g1, m['dW1'][e]):.2e}; "
+              f"dW2 fro {f2:.2e} inf {rel_inf(g2, m['dW2'][e]):.2e}", flush=True)
+        assert f1 <= tol and f2 <= tol, e

@@ -119,6 +119,9 @@ SHAPES = [  # T, d, E, k, h: several tiles plus ragged tails, an empty expert
     # past K must not be read (the last expert's W2 ends there)
     (97, 32, 3, 3, 1024),
     (333, 96, 7, 3, 160),
+    # the most experts the library takes: the fp32 kernel's 256-thread
+    # workgroups load all 257 offsets (expert 1 empty, as below)
+    (400, 64, 256, 5, 96),
 ]
 
 
@@ -196,7 +199,7 @@ def _run_layer(inp, k, tdt):
                                       # K and GEMM2's N; h = 8192: GEMM1's N = 2h = 16384 and
                                       # GEMM2's K), and the largest E with the largest k
                                       ((64, 16384, 4, 2, 128), "bf16"), ((64, 128, 4, 2, 8192), "bf16"),
-                                      ((300, 128, 256, 8, 64), "bf16"),
+                                      ((300, 128, 256, 8, 64), "bf16"), ((300, 128, 256, 8, 64), "f32"),
                                       # h > d and d % 64 == 32
                                       ((333, 96, 7, 3, 160), "bf16"), ((200, 64, 8, 2, 512), "bf16")])
 def test_layer_end_to_end(shape, dt):
@@ -230,7 +233,9 @@ def _bias(col, by):
     ((1, 64, 8, 8, 32), None),                  # one token on every expert (k = E)
     ((200, 96, 6, 2, 64), _bias(-1, -100.0)),   # the last expert gets no rows
     ((200, 64, 6, 2, 96), _bias(0, -100.0)),    # the first expert gets no rows
-    ((300, 128, 8, 2, 128), _bias(1, 100.0)),   # every token's first choice is expert 1
+    # every token's first choice is expert 1 (a bias that fixes the choice
+    # while the other gates, e^-10 of it, stay normal fp32 numbers)
+    ((300, 128, 8, 2, 128), _bias(1, 10.0)),
 ])
 def test_layer_edge_cases(shape, mod, dt):
     T, d, E, k, h = shape
@@ -247,6 +252,62 @@ def test_layer_edge_cases(shape, mod, dt):
     for key, ref in (("dx", b["dx"]), ("dw1", b["dW1"]), ("dw2", b["dW2"]),
                      ("dlogits", b["dlogits"]), ("dgate", b["dgate"])):
         assert rel_inf(to_np(g[key]), ref) <= tol, key
+
+
+# The weight gradients' output tiles are 128 x 256 (MFMA kernels). An expert
+# with more than twice the mean rows is split into 8 tile chunks, one per XCD,
+# when its tile count is a multiple of 8; every other expert goes whole to one
+# XCD. These shapes meet both conditions for dW2 ([d, h] = [1024, 256]: 8
+# tiles) and dW1 ([2h, d] = [512, 1024]: 16 tiles).
+HOT_SHAPE = (512, 1024, 8, 2, 256)
+
+
+def _wgrad_split_experts(counts, T, E, k, d, h):
+    thresh = 2 * -(-(T * k) // E)
+    tiles = {"dW2": -(-d // 128) * -(-h // 256), "dW1": -(-(2 * h) // 128) * -(-d // 256)}
+    assert all(t % 8 == 0 for t in tiles.values()), tiles
+    return [e for e in range(E) if counts[e] > thresh]
+
+
+def _hot(inp, case):
+    # biases large enough to fix the choices, small enough that the other
+    # gates (e^-10 of the hot one) keep the gradients out of the fp32
+    # subnormal range
+    if case == "one_hot":           # every token's first choice is expert 3
+        inp["logits"][:, 3] += 10.0
+    else:                           # experts 2 and 5 take every token; the others none
+        inp["logits"][:, 2] += 20.0
+        inp["logits"][:, 5] += 10.0
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("case", ["one_hot", "two_hot"])
+def test_hot_expert_split_wgrad(case, dt):
+    """Skewed routing that takes the weight gradients' hot-expert path (an
+    expert split over all XCDs, beside whole experts and empty ones): the
+    whole layer against the oracle, each expert's dW on its own."""
+    T, d, E, k, h = HOT_SHAPE
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    inp = _layer_inputs(T, d, E, k, h, seed=21, dt=dt)
+    _hot(inp, case)
+    f = oracle.layer_forward(inp, k, dt)
+    b = oracle.layer_backward(inp, f, k, dt)
+    counts = f["route"]["counts"]
+    hot = _wgrad_split_experts(counts, T, E, k, d, h)
+    assert hot == ([3] if case == "one_hot" else [2, 5]), counts
+    layer, out, g = _run_layer(inp, k, tdt)
+    _route_eq(layer.route, f["route"])
+    tol = TOL[dt]
+    assert rel_inf(to_np(out), f["out"]) <= tol
+    for key, ref in (("dx", b["dx"]), ("dlogits", b["dlogits"]), ("dgate", b["dgate"])):
+        assert rel_inf(to_np(g[key]), ref) <= tol, key
+    dw1, dw2 = to_np(g["dw1"]), to_np(g["dw2"])
+    for e in range(E):
+        if counts[e] == 0:
+            assert np.all(dw1[e] == 0) and np.all(dw2[e] == 0), e
+        else:
+            assert rel_inf(dw1[e], b["dW1"][e]) <= tol, e
+            assert rel_inf(dw2[e], b["dW2"][e]) <= tol, e
 
 
 def _clobber_scratch():
@@ -368,8 +429,29 @@ def test_zero_tokens():
 # configuration the bench times
 
 
+def _sample_experts(counts, n_random, seed):
+    """The hottest expert, an empty one (if any), a median-load one and
+    n_random other experts with rows."""
+    nz = np.flatnonzero(counts)
+    hot = int(np.argmax(counts))
+    med = int(nz[np.argsort(counts[nz], kind="stable")[len(nz) // 2]])
+    pick = {hot, med}
+    empty = np.flatnonzero(counts == 0)
+    if len(empty):
+        pick.add(int(empty[len(empty) // 2]))
+    rest = np.array(sorted(set(nz.tolist()) - pick))
+    for i in synth.sample_indices(len(rest), n_random, seed=seed):
+        pick.add(int(rest[i]))
+    return sorted(pick)
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["e128_bf16", "e128_bf16_zipf", "e8_bf16_fwd"])
 def test_full_size_sampled(name):
+    """The full-size workloads in the launch configuration the bench times:
+    routing in full, 512 sampled tokens (out, dX, dlogits) and the weight
+    gradients of the hottest expert, an empty one, a median one and three
+    random ones against the oracle."""
     w = synth.WORKLOADS[name]
     d_in = synth.device_inputs(w, seed=0, with_dout=w.backward)
     layer = moe.MoELayer(d_in["w1"], d_in["w2"], w.k)
@@ -380,13 +462,8 @@ def test_full_size_sampled(name):
     r = oracle.route(host["logits"], w.k)
     _route_eq(layer.route, r)
     counts = r["counts"]
-    toks = synth.sample_indices(w.T, 48, seed=1)
-    nonzero = np.flatnonzero(counts)
-    # a median-load expert and a random one (the hottest zipf expert holds
-    # ~15k rows: its weight gradient is checked against torch below)
-    med = int(nonzero[np.argsort(counts[nonzero])[len(nonzero) // 2]])
-    rnd = int(synth.sample_indices(len(nonzero), 1, seed=2)[0])
-    exps = sorted({med, int(nonzero[rnd])}) if w.backward else []
+    toks = synth.sample_indices(w.T, 512, seed=1)
+    exps = _sample_experts(counts, 3, seed=2) if w.backward else []
     s = oracle.layer_sampled(host, w.k, "bf16", toks, exps, backward=w.backward)
     assert rel_inf(to_np(out)[toks], s["out"]) <= TOL["bf16"]
     if not w.backward:
@@ -394,16 +471,10 @@ def test_full_size_sampled(name):
     assert rel_inf(to_np(g["dx"])[toks], s["dx"]) <= TOL["bf16"]
     assert rel_inf(to_np(g["dlogits"])[toks], s["dlogits"]) <= TOL["bf16"]
     for e in exps:
+        if counts[e] == 0:
+            assert torch.all(g["dw1"][e] == 0) and torch.all(g["dw2"][e] == 0), e
+            continue
         assert rel_inf(to_np(g["dw1"][e]), s["dW1"][e]) <= TOL["bf16"], e
         assert rel_inf(to_np(g["dw2"][e]), s["dW2"][e]) <= TOL["bf16"], e
-    empty = np.flatnonzero(counts == 0)
-    for e in empty[:4]:
+    for e in np.flatnonzero(counts == 0):
         assert torch.all(g["dw1"][int(e)] == 0) and torch.all(g["dw2"][int(e)] == 0)
-    # hottest expert: the grouped wgrad equals a plain fp32 product of the
-    # same stored operands (property at any size)
-    hot = int(np.argmax(counts))
-    o0, o1 = int(r["offsets"][hot]), int(r["offsets"][hot + 1])
-    ref2 = g["dy_perm"][o0:o1].float().T @ layer.hp[o0:o1].float()
-    assert rel_inf(to_np(g["dw2"][hot]), to_np(ref2)) <= 1e-3
-    ref1 = g["dab"][o0:o1].float().T @ layer.x_perm[o0:o1].float()
-    assert rel_inf(to_np(g["dw1"][hot]), to_np(ref1)) <= 1e-3
