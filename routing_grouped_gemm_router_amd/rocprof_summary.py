@@ -2,12 +2,13 @@
 
     python -m routing_grouped_gemm_router_amd.rocprof_summary stats DIR TITLE CMD > out.md
     python -m routing_grouped_gemm_router_amd.rocprof_summary pmc FETCH_DIR WRITE_DIR \
-        KERNEL COPY_BYTES TITLE CMD_FETCH CMD_WRITE > out.md
+        KERNEL[#n/p] COPY_BYTES TITLE CMD_FETCH CMD_WRITE > out.md
 
 `stats` tabulates DIR/run_kernel_stats.csv (from --kernel-trace --stats
 --output-format csv). `pmc` reads two --pmc runs (FETCH_SIZE, then
 WRITE_SIZE; counter values in KiB per dispatch), averages them over the
-dispatches whose name contains KERNEL, and scales each by what the same
+dispatches whose name contains KERNEL (with #n/p: the n-th of every p such
+dispatches), and scales each by what the same
 counter reads for the largest device copy of COPY_BYTES bytes in the same
 run. The result carries the hash of the GEMM sources it was measured on, so
 a reader can tell whether it still describes the current kernel.
@@ -65,12 +66,25 @@ def _per_dispatch(d: str, counter: str):
     return vals, names
 
 
+def _select(kernel: str):
+    """KERNEL[#n/p]: dispatches whose name contains KERNEL; with #n/p only
+    the n-th of every p of them in dispatch order (e.g. the second of the two
+    weight-gradient launches of each step, which share one kernel name)."""
+    if "#" in kernel:
+        name, sel = kernel.rsplit("#", 1)
+        n, p = (int(v) for v in sel.split("/"))
+        return name, n, p
+    return kernel, 0, 1
+
+
 def pmc(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int, title: str,
         cmd_fetch: str, cmd_write: str) -> str:
     res = {}
+    kname, nth, period = _select(kernel)
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         vals, names = _per_dispatch(d, counter)
-        kv = [vals[i] * 1024 for i in vals if kernel in names[i]]
+        ids = sorted(i for i in vals if kname in names[i])
+        kv = [vals[i] * 1024 for j, i in enumerate(ids) if j % period == nth]
         copies = [vals[i] * 1024 for i in vals if "copyBuffer" in names[i]]
         if not kv or not copies:
             raise SystemExit(f"{counter}: no '{kernel}' or copy dispatch in {d}")
