@@ -106,6 +106,25 @@ moe_status moe_route(const float *logits, int64_t T, int32_t E, int32_t k, int32
                      int32_t *token_pos, int32_t *sorted_token, int32_t *sorted_slot,
                      int32_t *tile_offsets, void *ws, size_t ws_bytes, void *stream);
 
+/* moe_route for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, outputs and errors as moe_route without (ws, ws_bytes).
+ * Its scratch is a MOE_ROUTE_NOALLOC_SCRATCH_BYTES (4 MiB) array that the
+ * library holds on each GPU it runs on until the process ends; the call
+ * allocates nothing. Sizes whose moe_route_workspace_size(T, E, k) exceeds
+ * it (T > 524288 at E = 128, T > 262144 at E = 256) return
+ * MOE_ERR_WORKSPACE with nothing enqueued. All calls on one GPU share its
+ * array: calls that overlap in time on one GPU (different streams, or
+ * threads) race and must be serialised by the caller. What an earlier call
+ * left in the array is never read. The first call on a device looks up the
+ * array's address (with that device current); a failed lookup returns
+ * MOE_ERR_LAUNCH. */
+#define MOE_ROUTE_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+moe_status moe_route_noalloc(const float *logits, int64_t T, int32_t E, int32_t k, int32_t tile_m,
+                             int32_t *topk_idx, float *topk_gate, int32_t *counts,
+                             int32_t *offsets, int32_t *token_pos, int32_t *sorted_token,
+                             int32_t *sorted_slot, int32_t *tile_offsets, void *stream);
+
 /* ------------------------------------------------------------------ */
 /* Dispatch and combine                                                 */
 

@@ -79,6 +79,8 @@ def _load():
     lib.moe_route_workspace_size.restype = _SZ
     lib.moe_route.argtypes = [_P, _I64, _I32, _I32, _I32] + [_P] * 9 + [_SZ, _P]
     lib.moe_route.restype = _I32
+    lib.moe_route_noalloc.argtypes = [_P, _I64, _I32, _I32, _I32] + [_P] * 9
+    lib.moe_route_noalloc.restype = _I32
     lib.moe_permute.argtypes = [_P, _P, _I32, _I64, _I32, _I32, _P, _P, _P, _P]
     lib.moe_permute.restype = _I32
     lib.moe_combine.argtypes = [_P, _I32, _P, _P, _I64, _I32, _I32, _P, _P]
@@ -178,6 +180,32 @@ def moe_route(logits: torch.Tensor, k: int, tile_m: int = 128, out: dict | None 
         _p(logits), T, E, k, tile_m, _p(out["topk_idx"]), _p(out["topk_gate"]), _p(out["counts"]),
         _p(out["offsets"]), _p(out["token_pos"]), _p(out["sorted_token"]), _p(out["sorted_slot"]),
         _p(out["tile_offsets"]), _p(ws), ws.numel(), _stream()))
+    return out
+
+
+MOE_ROUTE_NOALLOC_SCRATCH_BYTES = 4 << 20
+
+
+def moe_route_noalloc(logits: torch.Tensor, k: int, tile_m: int = 128,
+                      out: dict | None = None) -> dict:
+    """moe_route with the library's own per-GPU scratch (see moe.h): the C
+    call allocates nothing. Pass `out` (as moe_route returns) to avoid the
+    output allocations here as well."""
+    T, E = logits.shape
+    dev = logits.device
+    R = T * k
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = dict(topk_idx=torch.empty((T, k), **i32),
+                   topk_gate=torch.empty((T, k), dtype=torch.float32, device=dev),
+                   counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+                   token_pos=torch.empty((T, k), **i32), sorted_token=torch.empty(R, **i32),
+                   sorted_slot=torch.empty(R, **i32), tile_offsets=torch.empty(E + 1, **i32))
+    _need(logits, (T, E), torch.float32, "logits")
+    _check("moe_route_noalloc", _lib.moe_route_noalloc(
+        _p(logits), T, E, k, tile_m, _p(out["topk_idx"]), _p(out["topk_gate"]), _p(out["counts"]),
+        _p(out["offsets"]), _p(out["token_pos"]), _p(out["sorted_token"]), _p(out["sorted_slot"]),
+        _p(out["tile_offsets"]), _stream()))
     return out
 
 

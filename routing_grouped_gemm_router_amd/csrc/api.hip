@@ -13,6 +13,10 @@ moe_status route_launch(const float *logits, int64_t T, int E, int k, int tile_m
                         int32_t *topk_idx, float *topk_gate, int32_t *counts, int32_t *offsets,
                         int32_t *token_pos, int32_t *sorted_token, int32_t *sorted_slot,
                         int32_t *tile_offsets, void *ws, hipStream_t s);
+moe_status route_noalloc_launch(const float *logits, int64_t T, int E, int k, int tile_m,
+                                int32_t *topk_idx, float *topk_gate, int32_t *counts,
+                                int32_t *offsets, int32_t *token_pos, int32_t *sorted_token,
+                                int32_t *sorted_slot, int32_t *tile_offsets, hipStream_t s);
 moe_status permute_launch(const void *x, const uint8_t *x_scale, moe_dtype dt, int64_t T, int d,
                           int k, const int32_t *token_pos, void *x_perm, uint8_t *x_perm_scale,
                           hipStream_t s);
@@ -137,6 +141,23 @@ moe_status moe_route(const float *logits, int64_t T, int32_t E, int32_t k, int32
     if (ws_bytes < moe_route_workspace_size(T, E, k)) return MOE_ERR_WORKSPACE;
     return route_launch(logits, T, E, k, tile_m, topk_idx, topk_gate, counts, offsets, token_pos,
                         sorted_token, sorted_slot, tile_offsets, ws, (hipStream_t)stream);
+}
+
+moe_status moe_route_noalloc(const float *logits, int64_t T, int32_t E, int32_t k, int32_t tile_m,
+                             int32_t *topk_idx, float *topk_gate, int32_t *counts,
+                             int32_t *offsets, int32_t *token_pos, int32_t *sorted_token,
+                             int32_t *sorted_slot, int32_t *tile_offsets, void *stream) {
+    if (!routing_shape_ok(T, E, k) || tile_m < 1) return MOE_ERR_SHAPE;
+    if (!counts || !offsets || !tile_offsets) return MOE_ERR_NULL;
+    if (T > 0 && (!logits || !topk_idx || !topk_gate || !token_pos || !sorted_token ||
+                  !sorted_slot))
+        return MOE_ERR_NULL;
+    if (T > 0 && !aligned16(logits)) return MOE_ERR_ALIGN;
+    if (moe_route_workspace_size(T, E, k) > MOE_ROUTE_NOALLOC_SCRATCH_BYTES)
+        return MOE_ERR_WORKSPACE;
+    return route_noalloc_launch(logits, T, E, k, tile_m, topk_idx, topk_gate, counts, offsets,
+                                token_pos, sorted_token, sorted_slot, tile_offsets,
+                                (hipStream_t)stream);
 }
 
 moe_status moe_permute(const void *x, const uint8_t *x_scale, moe_dtype dt, int64_t T, int32_t d,

@@ -55,4 +55,7 @@ inline moe_status launch_status() {
 // Number of compute units of the current device.
 int num_cus();
 
+// Bytes of the device array moe_route_noalloc uses instead of a workspace.
+constexpr size_t kRouteNoAllocScratchBytes = MOE_ROUTE_NOALLOC_SCRATCH_BYTES;
+
 }  // namespace moe

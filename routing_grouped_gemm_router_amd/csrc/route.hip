@@ -23,6 +23,8 @@
 //  3. route_place: scans the E totals (in LDS) into offsets / tile offsets
 //     and writes token_pos = offsets[e] + chunk base + rank and the inverse
 //     maps sorted_token / sorted_slot.
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
@@ -321,6 +323,42 @@ moe_status route_launch(const float *logits, int64_t T, int E, int k, int tile_m
                                              token_pos, sorted_token, sorted_slot, offsets,
                                              tile_offsets);
     return launch_status();
+}
+
+
+// ---------------------------------------------------------------------------
+// moe_route without a caller workspace: the per-chunk expert counts go to
+// this file-scope array, one copy per GPU, held until the process ends. In
+// host code `g_route_scratch` is only a stand-in for the symbol, not a device
+// address: the address comes from hipGetSymbolAddress, looked up once per
+// device with that device current, and only that address reaches a kernel.
+static __device__ __align__(256) uint8_t g_route_scratch[kRouteNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::once_flag g_scratch_once[kMaxDevices];
+static void *g_scratch_ptr[kMaxDevices];
+
+static void *route_scratch(int dev) {
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_ptr[dev] =
+            hipGetSymbolAddress(&p, HIP_SYMBOL(g_route_scratch)) == hipSuccess ? p : nullptr;
+    });
+    return g_scratch_ptr[dev];
+}
+
+moe_status route_noalloc_launch(const float *logits, int64_t T, int E, int k, int tile_m,
+                                int32_t *topk_idx, float *topk_gate, int32_t *counts,
+                                int32_t *offsets, int32_t *token_pos, int32_t *sorted_token,
+                                int32_t *sorted_slot, int32_t *tile_offsets, hipStream_t s) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_LAUNCH;
+    void *ws = route_scratch(dev);
+    if (!ws) return MOE_ERR_LAUNCH;
+    // every chunk count the kernels read is written first by route_select in
+    // the same call, so nothing left by an earlier call needs clearing
+    return route_launch(logits, T, E, k, tile_m, topk_idx, topk_gate, counts, offsets, token_pos,
+                        sorted_token, sorted_slot, tile_offsets, ws, s);
 }
 
 }  // namespace moe
