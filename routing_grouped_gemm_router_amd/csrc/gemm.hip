@@ -25,6 +25,12 @@
 //    each wave holds the gate and up columns of the same hidden unit in the
 //    same registers, so H' = silu(a) * b is formed from the fp32
 //    accumulators); SwiGLU backward (reads the stored a, b).
+//  * two kernels share the tiles, schedules, LDS layouts and MFMA order, so
+//    they give the same bits: gg_ws (bf16 FWD, DGRAD, WGRAD) splits the
+//    workgroup into consumer waves (fragment reads, MFMAs, epilogue) and
+//    producer waves (every global -> LDS copy), so the copies never wait on
+//    the epilogue's stores and the producers run ahead across tiles;
+//    gg_mfma (MXFP8, and the bf16 SwiGLU backward) has every wave do both.
 #include <type_traits>
 #include <utility>
 
@@ -1175,6 +1181,316 @@ void gg_mfma(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 grouped GEMM with split roles (FWD, DGRAD, WGRAD). The workgroup's waves
+// 0..NC-1 are consumers: LDS fragment reads, MFMAs and the tile's epilogue.
+// Waves NC..NC+NP-1 are producers: they issue every global -> LDS copy and
+// wait only on those. A wave's vector-memory counter covers its loads and
+// stores together, so with one role per wave the consumers never wait on the
+// copies and a tile's stores drain while the next tile is multiplied; the
+// producers run up to STAGES-1 steps ahead, across tile boundaries.
+// One workgroup barrier per K step, numbered over the workgroup's tiles:
+// before barrier G the producers have landed step G and the consumers have
+// finished reading step G-1, whose buffer the producers refill after it.
+// Tiles, schedules, LDS layouts and the order of every MFMA over K are those
+// of gg_mfma, so both kernels give the same bits.
+
+template <int MODE, int EPI, int BM, int BN, int WM, int WN, int NP, int STAGES, bool ACC = false>
+__global__ __launch_bounds__((WM * WN + NP) * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void gg_ws(GemmArgs g) {
+    constexpr int NC = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    static_assert(TM >= 1 && TN >= 1, "wave tile");
+    static_assert(EPI != MOE_EPI_SWIGLU_FWD || TN % 2 == 0, "SwiGLU pairs gate/up sub-tiles");
+    static_assert(EPI != MOE_EPI_SWIGLU_BWD, "the SwiGLU backward runs on gg_mfma");
+    constexpr bool A_KL = MODE != MOE_GG_WGRAD;
+    constexpr bool B_KL = MODE == MOE_GG_FWD;
+    using AT = DmaTile<BM, A_KL, NP>;
+    using BT = DmaTile<BN, B_KL, NP>;
+    constexpr int IPP = AT::IPW + BT::IPW;          // copies per producer wave per step
+    constexpr int STAGE_U4 = (BM + BN) * 8;
+    constexpr int ASTEP = A_KL ? kStepBytes : 64;   // K per step: bytes of A rows, or rows
+    __shared__ __attribute__((aligned(1024))) uint4 lds_pool[STAGES * STAGE_U4];
+    __shared__ int32_t s_off[257];
+    __shared__ int32_t s_tile[257];
+    __shared__ int32_t s_chunk[257];
+    __shared__ int32_t s_xpre[kXcdChunks + 1];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool producer = wave >= NC;
+    const int E = g.E;
+    const int xcd = blockIdx.x & 7, worker = blockIdx.x >> 3, workers = gridDim.x >> 3;
+    int n_tiles, total;
+    RowSchedule rs;
+    WgSchedule ws;
+    if constexpr (MODE == MOE_GG_WGRAD) {
+        load_offsets(g.offsets, E, s_off);
+        n_tiles = (g.N + BN - 1) / BN;
+        ws = build_wgrad_schedule(s_off, E, ((g.M + BM - 1) / BM) * n_tiles, xcd, s_chunk, s_xpre);
+        total = ws.total;
+    } else {
+        build_tile_table(g.offsets, E, BM, s_off, s_tile);
+        n_tiles = (EPI == MOE_EPI_SWIGLU_FWD) ? (g.h + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
+        rs = build_row_schedule(s_tile, E, n_tiles, xcd, s_chunk, s_xpre);
+        total = rs.total;
+    }
+    const char *A = reinterpret_cast<const char *>(g.A);
+    const char *B = reinterpret_cast<const char *>(g.B);
+
+    struct TileC {
+        int e, row0, row_end, m0, n0, nt, klim;
+    };
+    auto decode = [&](int pos) {
+        TileC t;
+        t.row_end = 0;
+        t.m0 = 0;
+        if constexpr (MODE == MOE_GG_WGRAD) {
+            const int mtiles = (g.M + BM - 1) / BM;
+            const int per_e = mtiles * n_tiles;
+            int tt;
+            if (pos < ws.n_split * ws.cs) {
+                t.e = s_xpre[pos / ws.cs];
+                tt = xcd * ws.cs + pos % ws.cs;
+            } else {
+                const int p2 = pos - ws.n_split * ws.cs;
+                t.e = s_xpre[128 + p2 / per_e];
+                tt = p2 % per_e;
+            }
+            const int grp = tt / (kWgGroupM * n_tiles), first_m = grp * kWgGroupM;
+            const int gm = min(mtiles - first_m, kWgGroupM);
+            const int tg = tt - grp * kWgGroupM * n_tiles;
+            t.nt = tg / gm;
+            t.m0 = (first_m + tg % gm) * BM;
+            t.row0 = s_off[t.e];
+            t.klim = s_off[t.e + 1] - t.row0;      // reduction over the group's rows
+        } else {
+            int mt_e;
+            decode_row_tile(rs, s_tile, s_chunk, s_xpre, E, xcd, pos, t.e, mt_e, t.nt);
+            t.row0 = s_off[t.e] + mt_e * BM;
+            t.row_end = s_off[t.e + 1];
+            t.klim = g.K * 2;                       // bytes of K per A row
+        }
+        t.n0 = t.nt * BN;
+        return t;
+    };
+    auto nk_of = [](int klim) { return (klim + ASTEP - 1) / ASTEP; };
+    auto stage = [&](int s) { return lds_pool + s * STAGE_U4; };
+
+    if (producer) {
+        const int pw = wave - NC;
+        AT ta;
+        BT tb;
+        // B row (in B's N rows) of tile column n, clamped into range; SwiGLU:
+        // each consumer wave's columns are gate rows then the up rows of the
+        // same hidden units
+        auto b_row_clamped = [&](const TileC &t, int n) -> int {
+            if constexpr (MODE == MOE_GG_FWD && EPI == MOE_EPI_SWIGLU_FWD) {
+                const int wc = n / WTN, off = n % WTN, half = WTN / 2;
+                const int j = min(t.nt * (BN / 2) + wc * half + (off % half), g.h - 1);
+                return off < half ? j : g.h + j;
+            } else {
+                return min(t.n0 + n, g.N - 1);
+            }
+        };
+        auto setup = [&](const TileC &t) {
+            if constexpr (MODE == MOE_GG_WGRAD) {
+                ta.setup_mn(A + ((int64_t)t.row0 * g.M + t.m0) * 2, (int64_t)g.M * 2, g.M - t.m0, pw, lane);
+                tb.setup_mn(B + ((int64_t)t.row0 * g.N + t.n0) * 2, (int64_t)g.N * 2, g.N - t.n0, pw, lane);
+            } else {
+                const int last = t.row_end - t.row0 - 1;
+                const uint32_t pitch = (uint32_t)(g.K * 2);
+                ta.setup_kl(A + (int64_t)t.row0 * g.K * 2,
+                            [&](int r) { return (uint32_t)min(r, last) * pitch; }, pw, lane);
+                if constexpr (B_KL) {
+                    tb.setup_kl(B + (int64_t)t.e * g.N * g.K * 2,
+                                [&](int n) { return (uint32_t)b_row_clamped(t, n) * pitch; }, pw, lane);
+                } else {
+                    tb.setup_mn(B + ((int64_t)t.e * g.K * g.N + t.n0) * 2, (int64_t)g.N * 2, g.N - t.n0,
+                                pw, lane);
+                }
+            }
+        };
+        // issue cursor over the workgroup's tiles that have steps
+        int ip = worker, ikt = 0, iklim = 0;
+        auto seek = [&]() {
+            while (ip < total) {
+                const TileC t = decode(ip);
+                if (nk_of(t.klim) > 0) {
+                    iklim = t.klim;
+                    setup(t);
+                    break;
+                }
+                ip += workers;
+            }
+            ikt = 0;
+        };
+        auto issue_next = [&](int gs) -> bool {
+            if (ip >= total) return false;
+            uint4 *st = stage(gs);
+            ta.issue(st, ikt, iklim, pw);
+            // bf16 DGRAD: iklim is A's K extent in bytes; B (MN layout) counts K rows
+            tb.issue(st + BM * 8, ikt, (A_KL && !B_KL) ? iklim / 2 : iklim, pw);
+            if (++ikt == nk_of(iklim)) {
+                ip += workers;
+                seek();
+            }
+            return true;
+        };
+        seek();
+        int issued = 0;
+        for (int s = 0; s < STAGES - 1; s++)
+            if (issue_next(s)) issued++;
+        for (int G = 0; G < issued; G++) {
+            // step G must have landed; the steps after it may stay in flight
+            if (issued - 1 - G >= STAGES - 2) wait_vmem<(STAGES - 2) * IPP>();
+            else wait_vmem<0>();
+            lds_sync();                  // barrier G
+            if (issue_next((G + STAGES - 1) % STAGES)) issued++;
+        }
+        return;
+    }
+
+    // consumers
+    const int wm = wave / WN, wn = wave % WN;
+    f32x16 acc[TM][TN];
+    auto zero = [&]() {
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+    };
+    // acc[i][j][v] holds row (v/4)*8 + (lane/32)*4 + v%4 and column lane%32
+    // of the wave's (i, j) 32x32 block
+    const int col_l = lane & 31;
+    auto row_in = [&](int i, int v) { return wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3); };
+    auto epilogue = [&](const TileC &t) {
+        if constexpr (MODE == MOE_GG_WGRAD) {
+            float *C = reinterpret_cast<float *>(g.C) + (int64_t)t.e * g.M * g.N;
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++) {
+                    const int n = t.n0 + wn * WTN + j * 32 + col_l;
+                    if constexpr (ACC) {
+                        // C += the block, one fp32 add per element; its old
+                        // values are all loaded before the first store
+                        float old[16];
+#pragma unroll
+                        for (int v = 0; v < 16; v++) {
+                            const int m = t.m0 + row_in(i, v);
+                            old[v] = (m < g.M && n < g.N) ? C[(int64_t)m * g.N + n] : 0.f;
+                        }
+                        wait_vmem<0>();
+#pragma unroll
+                        for (int v = 0; v < 16; v++) {
+                            const int m = t.m0 + row_in(i, v);
+                            if (m < g.M && n < g.N) store_f32(C + (int64_t)m * g.N + n, old[v] + acc[i][j][v]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < 16; v++) {
+                            const int m = t.m0 + row_in(i, v);
+                            if (m < g.M && n < g.N) store_f32(C + (int64_t)m * g.N + n, acc[i][j][v]);
+                        }
+                    }
+                }
+        } else if constexpr (EPI == MOE_EPI_SWIGLU_FWD) {
+            uint16_t *AB = reinterpret_cast<uint16_t *>(g.C);
+            uint16_t *HP = reinterpret_cast<uint16_t *>(g.aux_out);
+            const int h = g.h;
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN / 2; j++) {
+                    const int jj = t.nt * (BN / 2) + wn * (WTN / 2) + j * 32 + col_l;
+#pragma unroll
+                    for (int v = 0; v < 16; v++) {
+                        const int grow = t.row0 + row_in(i, v);
+                        if (grow < t.row_end && jj < h) {
+                            const float a = acc[i][j][v], b = acc[i][j + TN / 2][v];
+                            uint16_t *abr = AB + (int64_t)grow * 2 * h;
+                            abr[jj] = f32_to_bf16(a);
+                            abr[h + jj] = f32_to_bf16(b);
+                            HP[(int64_t)grow * h + jj] = f32_to_bf16(silu_f(a) * b);
+                        }
+                    }
+                }
+        } else {
+            uint16_t *C = reinterpret_cast<uint16_t *>(g.C);
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++) {
+                    const int n = t.n0 + wn * WTN + j * 32 + col_l;
+#pragma unroll
+                    for (int v = 0; v < 16; v++) {
+                        const int grow = t.row0 + row_in(i, v);
+                        if (grow < t.row_end && n < g.N) C[(int64_t)grow * g.N + n] = f32_to_bf16(acc[i][j][v]);
+                    }
+                }
+        }
+    };
+    // one K step from buffer st: fragments double-buffered in registers
+    auto step = [&](int st) {
+        const uint4 *sa = stage(st);
+        const uint4 *sb = sa + BM * 8;
+        bf16x8 fa[2][TM], fb[2][TN];
+#pragma unroll
+        for (int i = 0; i < TM; i++) fa[0][i] = AT::frag(sa, wm * WTM + i * 32, 0, lane);
+#pragma unroll
+        for (int j = 0; j < TN; j++) fb[0][j] = BT::frag(sb, wn * WTN + j * 32, 0, lane);
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+            const int cb = kk & 1, nb2 = cb ^ 1;
+            if constexpr (MODE != MOE_GG_WGRAD) {
+                // row GEMMs: one fragment read of the next slice between two MFMAs
+#pragma unroll
+                for (int t = 0; t < TM * TN; t++) {
+                    if (kk + 1 < 4) {
+                        if (t < TM) fa[nb2][t] = AT::frag(sa, wm * WTM + t * 32, kk + 1, lane);
+                        else if (t < TM + TN)
+                            fb[nb2][t - TM] = BT::frag(sb, wn * WTN + (t - TM) * 32, kk + 1, lane);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    acc[t / TN][t % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        fa[cb][t / TN], fb[cb][t % TN], acc[t / TN][t % TN], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                if (kk + 1 < 4) {
+#pragma unroll
+                    for (int i = 0; i < TM; i++) fa[nb2][i] = AT::frag(sa, wm * WTM + i * 32, kk + 1, lane);
+#pragma unroll
+                    for (int j = 0; j < TN; j++) fb[nb2][j] = BT::frag(sb, wn * WTN + j * 32, kk + 1, lane);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < TM; i++)
+#pragma unroll
+                    for (int j = 0; j < TN; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    int G = 0;
+    for (int pos = worker; pos < total; pos += workers) {
+        const TileC t = decode(pos);
+        const int nk = nk_of(t.klim);
+        if (ACC && nk == 0) continue;              // accumulating: an empty group leaves C as it is
+        zero();
+        for (int kt = 0; kt < nk; kt++, G++) {
+            lds_sync();                             // barrier G: step G is in buffer G % STAGES
+            step(G % STAGES);
+        }
+        epilogue(t);                                // its stores drain while the next tile runs
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel (correctness dtype): 64x64 tiles, 256 threads, 4x4 outputs per
 // thread, fp32 FMA. A thread owns rows 4*ty..4*ty+3 and columns
 // {2tx, 2tx+1, 32+2tx, 32+2tx+1}, so in the SwiGLU forward layout (tile
@@ -1372,8 +1688,29 @@ __global__ __launch_bounds__(256) void gg_f32(GemmArgs g) {
 #define MOE_WG_WN 4
 #endif
 
+// bf16: 8 consumer waves (2 x 4, 64 x 64 each) and 4 producer waves on the
+// same 128 x 256 tiles and 3 stages as gg_mfma
+template <int MODE, int EPI>
+static void launch_ws(const GemmArgs &a, hipStream_t s) {
+    const int grid = (num_cus() + 7) / 8 * 8;
+    if constexpr (MODE == MOE_GG_WGRAD) {
+        if (a.accumulate) {
+            gg_ws<MODE, EPI, 128, 256, 2, 4, 4, 3, true><<<grid, 12 * 64, 0, s>>>(a);
+            return;
+        }
+    }
+    gg_ws<MODE, EPI, 128, 256, 2, 4, 4, 3><<<grid, 12 * 64, 0, s>>>(a);
+}
+
 template <int MODE, int EPI, bool FP8>
 static void launch_mfma(const GemmArgs &a, hipStream_t s) {
+    // bf16 on the split-role kernel, except the SwiGLU backward, whose
+    // epilogue reads a, b through LDS-staged 16-byte rows (measured 2 % faster
+    // than the split kernel's register-direct form)
+    if constexpr (!FP8 && EPI != MOE_EPI_SWIGLU_BWD) {
+        launch_ws<MODE, EPI>(a, s);
+        return;
+    }
     if constexpr (MODE == MOE_GG_WGRAD) {
         const int grid = (num_cus() * MOE_WG_OCC + 7) / 8 * 8;
         if (a.accumulate)
