@@ -235,7 +235,9 @@ def dominant_roofline(w, roles: dict, traffic) -> dict:
     flops, nbytes = role_work(w)[name]
     mx = w.dtype == "mxfp8"
     mode = "WGRAD" if "wgrad" in name else ("DGRAD" if "dgrad" in name else "FWD")
-    kern = f"gg_mfma<{mode}, {'MXFP8' if mx else 'bf16'}> ({name})"
+    # bf16 roles run on the split-role kernel, except the SwiGLU backward
+    kname = "gg_mfma" if mx or name == "gemm2_dgrad_swiglu" else "gg_ws"
+    kern = f"{kname}<{mode}, {'MXFP8' if mx else 'bf16'}> ({name})"
     out = {"kernel": kern, "bound": r["bound"], "traffic": traffic,
            "avg_launch_ms": r["us"] * 1e-3, "flops_per_launch": flops, "bytes_per_launch": nbytes}
     if r["bound"] == "hbm":

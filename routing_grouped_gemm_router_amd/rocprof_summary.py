@@ -3,6 +3,9 @@
     python -m routing_grouped_gemm_router_amd.rocprof_summary stats DIR TITLE CMD > out.md
     python -m routing_grouped_gemm_router_amd.rocprof_summary pmc FETCH_DIR WRITE_DIR \
         KERNEL[#n/p] COPY_BYTES TITLE CMD_FETCH CMD_WRITE > out.md
+    python -m routing_grouped_gemm_router_amd.rocprof_summary api DIR_A DIR_B STEPS_A STEPS_B \
+        TITLE CMD_A CMD_B > out.md
+    python -m routing_grouped_gemm_router_amd.rocprof_summary sq DIR TITLE CMD [NAMES] > out.md
 
 `stats` tabulates DIR/run_kernel_stats.csv (from --kernel-trace --stats
 --output-format csv). `pmc` reads two --pmc runs (FETCH_SIZE, then
@@ -11,7 +14,10 @@ dispatches whose name contains KERNEL (with #n/p: the n-th of every p such
 dispatches), and scales each by what the same
 counter reads for the largest device copy of COPY_BYTES bytes in the same
 run. The result carries the hash of the GEMM sources it was measured on, so
-a reader can tell whether it still describes the current kernel.
+a reader can tell whether it still describes the current kernel. `api`
+compares the HIP API call counts of two runs that differ only in their
+number of timed steps (what one step issues); `sq` tabulates SQ counters
+per kernel.
 
 Only reads the CSV files; runs nothing.
 """
@@ -107,6 +113,47 @@ def pmc(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int, title: str
     return "\n".join(out)
 
 
+def api_diff(d_small: str, d_large: str, n_small: int, n_large: int, title: str, cmd_small: str,
+             cmd_large: str) -> str:
+    """HIP API calls of two runs that differ only in their number of timed
+    steps: the difference per extra step is what one step issues."""
+    def calls(d):
+        return {r["Name"]: int(r["Calls"])
+                for r in csv.DictReader(open(os.path.join(d, "run_hip_api_stats.csv")))}
+    a, b = calls(d_small), calls(d_large)
+    extra = n_large - n_small
+    out = [f"# {title}", "", "Commands (one MI355X):", "", "```", cmd_small, cmd_large, "```", "",
+           f"| HIP API call | {n_small} steps | {n_large} steps | per extra step |",
+           "|---|---|---|---|"]
+    for n in sorted(set(a) | set(b)):
+        out.append(f"| `{n}` | {a.get(n, 0)} | {b.get(n, 0)} | {(b.get(n, 0) - a.get(n, 0)) / extra:g} |")
+    return "\n".join(out) + "\n"
+
+
+def sq(d: str, title: str, cmd: str, select=None) -> str:
+    """SQ counters averaged per kernel name (all dispatches of each name)."""
+    vals = defaultdict(lambda: defaultdict(float))
+    names = {}
+    for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+        i = int(r["Dispatch_Id"])
+        vals[i][r["Counter_Name"]] += float(r["Counter_Value"])
+        names[i] = r["Kernel_Name"]
+    groups = defaultdict(list)
+    for i in sorted(vals):
+        if select and not any(s in names[i] for s in select):
+            continue
+        groups[_short(names[i].split("(")[0], 60)].append(vals[i])
+    cols = sorted({c for g in groups.values() for x in g for c in x})
+    out = [f"# {title}", "", "Command (one MI355X):", "", "```", cmd, "```", "",
+           "Per launch (summed over the GPU's counter instances, averaged over the launches).", "",
+           "| kernel | launches | " + " | ".join(c.replace("SQ_", "") for c in cols) + " |",
+           "|---|---|" + "---|" * len(cols)]
+    for k, lst in groups.items():
+        out.append(f"| `{k}` | {len(lst)} | " +
+                   " | ".join(f"{sum(x.get(c, 0) for x in lst) / len(lst):.4g}" for c in cols) + " |")
+    return "\n".join(out) + "\n"
+
+
 def read_traffic(md_path: str):
     """(bytes per launch, source hash) from a pmc summary, or None."""
     if not os.path.exists(md_path):
@@ -123,6 +170,12 @@ def read_traffic(md_path: str):
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         sys.stdout.write(stats(sys.argv[2], sys.argv[3], sys.argv[4]))
+    elif sys.argv[1] == "api":
+        sys.stdout.write(api_diff(sys.argv[2], sys.argv[3], int(sys.argv[4]), int(sys.argv[5]),
+                                  sys.argv[6], sys.argv[7], sys.argv[8]))
+    elif sys.argv[1] == "sq":
+        sys.stdout.write(sq(sys.argv[2], sys.argv[3], sys.argv[4],
+                            sys.argv[5].split(",") if len(sys.argv) > 5 else None))
     elif sys.argv[1] == "pmc":
         sys.stdout.write(pmc(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6],
                              sys.argv[7], sys.argv[8]))
