@@ -227,6 +227,38 @@ size_t moe_grouped_gemm_workspace_size(const moe_gemm_desc *g);
 
 moe_status moe_grouped_gemm(const moe_gemm_desc *g, void *stream);
 
+/* Host-side bound of the grouped GEMM's reads: no device work, no GPU
+ * needed. Walks, on the host, every global -> LDS copy that
+ * moe_grouped_gemm would issue for descriptor g, in the kernel
+ * configuration the library launches for g's dtype and mode, with the group
+ * offsets host_offsets[0 .. n_groups] (host memory, non-decreasing, from 0
+ * to g->rows). Only g's mode, dtype, epilogue, n_groups, rows, M, N and K
+ * are used; its pointers are neither read nor dereferenced. The walk
+ * computes each copy's source with the same code the kernels run
+ * (copy_plan.h), so it checks the copies against the operand extents the
+ * caller states: w->extent[i] bytes readable from A, B, a_scale, b_scale
+ * (i = 0..3; the scale extents matter for MXFP8 only). On return w holds
+ * the number of copies (16-byte operand chunks and MXFP8 scale reads) and
+ * of those that take zeros instead of memory (K past a group's end), the
+ * lowest and one-past-highest byte read from each operand, and the first
+ * read outside [0, extent) if any (first_bad = operand index, else -1).
+ * MOE_ERR_DTYPE for MOE_F32 (its kernel stages through registers, not
+ * through these copies) and for invalid modes; MOE_ERR_SHAPE for shapes
+ * moe_grouped_gemm rejects or offsets that do not match rows. */
+typedef struct moe_copy_walk {
+    int64_t extent[4];      /* in: readable bytes of A, B, a_scale, b_scale */
+    int64_t copies;         /* out */
+    int64_t zero_copies;
+    int64_t lowest[4];      /* INT64_MAX for an operand nothing was read from */
+    int64_t end[4];         /* 0 for an operand nothing was read from */
+    int32_t first_bad;      /* -1: every read in bounds */
+    int64_t bad_offset;     /* first out-of-bounds read: its byte offset */
+    int64_t bad_bytes;      /* and its size */
+} moe_copy_walk;
+
+moe_status moe_gemm_copy_walk(const moe_gemm_desc *g, const int32_t *host_offsets,
+                              moe_copy_walk *w);
+
 /* ------------------------------------------------------------------ */
 /* Backward of the whole layer                                          */
 
@@ -306,6 +338,21 @@ typedef struct moe_bwd_desc {
 #define MOE_BWD_MAX_STAGES 10
 
 size_t moe_backward_workspace_size(const moe_bwd_desc *b);
+
+/* Where the MXFP8 backward keeps its quantised operands inside ws (byte
+ * offsets, 256-aligned, in this order, each region up to the next offset):
+ *   row_q, row_s   dy along d, then dAB along 2h (row blocks) and scales;
+ *   col0_q, col0_s dy, then dAB, in the column-block layout per expert;
+ *   col1_q, col1_s H', then the gathered x rows, column-block layout;
+ *   total          = moe_backward_workspace_size(b).
+ * MOE_ERR_DTYPE unless b->dtype is MOE_MXFP8; MOE_ERR_SHAPE as
+ * moe_backward. Lets a caller (and the tests) check the regions against the
+ * operand sizes of mxfp8_quantize and the reads of moe_gemm_copy_walk. */
+typedef struct moe_bwd_ws_layout {
+    size_t row_q, row_s, col0_q, col0_s, col1_q, col1_s, total;
+} moe_bwd_ws_layout;
+
+moe_status moe_backward_workspace_layout(const moe_bwd_desc *b, moe_bwd_ws_layout *out);
 
 moe_status moe_backward(const moe_bwd_desc *b, void *stream);
 

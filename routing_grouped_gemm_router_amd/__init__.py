@@ -57,6 +57,17 @@ class BwdDesc(ctypes.Structure):
                 ("w2t_scale", _P), ("ws", _P), ("ws_bytes", _SZ), ("accumulate_dw", _I32),
                 ("stage_events", ctypes.POINTER(_P))]
 
+class CopyWalk(ctypes.Structure):
+    _fields_ = [("extent", _I64 * 4), ("copies", _I64), ("zero_copies", _I64),
+                ("lowest", _I64 * 4), ("end", _I64 * 4), ("first_bad", _I32),
+                ("bad_offset", _I64), ("bad_bytes", _I64)]
+
+
+class BwdWsLayout(ctypes.Structure):
+    _fields_ = [(n, _SZ) for n in ("row_q", "row_s", "col0_q", "col0_s", "col1_q", "col1_s",
+                                   "total")]
+
+
 MOE_BWD_MAX_STAGES = 10
 BWD_STAGES = {
     "bf16": ("combine_bwd", "gemm2_dgrad_swiglu", "gemm2_wgrad", "gemm1_dgrad", "unpermute_bwd",
@@ -93,6 +104,10 @@ def _load():
     lib.moe_backward.restype = _I32
     lib.moe_backward_workspace_size.argtypes = [ctypes.POINTER(BwdDesc)]
     lib.moe_backward_workspace_size.restype = _SZ
+    lib.moe_backward_workspace_layout.argtypes = [ctypes.POINTER(BwdDesc), ctypes.POINTER(BwdWsLayout)]
+    lib.moe_backward_workspace_layout.restype = _I32
+    lib.moe_gemm_copy_walk.argtypes = [ctypes.POINTER(GemmDesc), _P, ctypes.POINTER(CopyWalk)]
+    lib.moe_gemm_copy_walk.restype = _I32
     lib.mxfp8_quantize.argtypes = [_P, _I32, _I64, _I64, _I32, _P, _I32, _P, _P, _P, _P]
     lib.mxfp8_quantize.restype = _I32
     lib.mxfp8_col_blocks.argtypes = [_I64, _I32]
@@ -375,6 +390,42 @@ def moe_backward(saved: dict, dout: torch.Tensor, E: int, k: int, d: int, h: int
         b.stage_events = ctypes.cast(arr, ctypes.POINTER(_P))
     _check("moe_backward", _lib.moe_backward(ctypes.byref(b), _stream()))
     return out
+
+
+def moe_gemm_copy_walk(mode: int, dtype: int, epilogue: int, offsets, M: int = 0, N: int = 0,
+                       K: int = 0, extents=(0, 0, 0, 0)) -> dict:
+    """Host-side walk of every copy moe_grouped_gemm would issue (no GPU).
+    offsets: host sequence of n_groups + 1 ints; extents: readable bytes of
+    A, B, a_scale, b_scale."""
+    off = (ctypes.c_int32 * len(offsets))(*[int(v) for v in offsets])
+    g = GemmDesc()
+    g.mode, g.dtype, g.epilogue = mode, dtype, epilogue
+    g.n_groups = len(offsets) - 1
+    g.rows = int(offsets[-1])
+    g.M, g.N, g.K = M, N, K
+    w = CopyWalk()
+    for i, x in enumerate(extents):
+        w.extent[i] = int(x)
+    _check("moe_gemm_copy_walk", _lib.moe_gemm_copy_walk(ctypes.byref(g), off, ctypes.byref(w)))
+    return {"copies": w.copies, "zero_copies": w.zero_copies, "lowest": list(w.lowest),
+            "end": list(w.end), "first_bad": w.first_bad, "bad_offset": w.bad_offset,
+            "bad_bytes": w.bad_bytes}
+
+
+def moe_backward_workspace_layout(T: int, E: int, k: int, d: int, h: int) -> dict:
+    """Byte offsets of the MXFP8 backward's regions inside its workspace."""
+    b = BwdDesc()
+    b.dtype, b.T, b.E, b.k, b.d, b.h = MOE_MXFP8, T, E, k, d, h
+    L = BwdWsLayout()
+    _check("moe_backward_workspace_layout",
+           _lib.moe_backward_workspace_layout(ctypes.byref(b), ctypes.byref(L)))
+    return {n: getattr(L, n) for n, _ in BwdWsLayout._fields_}
+
+
+def moe_backward_workspace_size(T: int, E: int, k: int, d: int, h: int, dtype: int) -> int:
+    b = BwdDesc()
+    b.dtype, b.T, b.E, b.k, b.d, b.h = dtype, T, E, k, d, h
+    return _lib.moe_backward_workspace_size(ctypes.byref(b))
 
 
 def mxfp8_col_blocks(rows: int, n_groups: int) -> int:

@@ -28,6 +28,7 @@ moe_status combine_bwd_launch(const void *dout, const void *y, moe_dtype dt, con
                               int d, int k, int E, void *dy, float *dlogits, float *dgate,
                               hipStream_t s);
 moe_status gemm_launch(const moe_gemm_desc *d, hipStream_t s);
+moe_status gemm_copy_walk(const moe_gemm_desc *d, const int32_t *host_offsets, moe_copy_walk *w);
 moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
                                  int axis, const int32_t *group_offsets, int n_groups,
                                  const int32_t *row_map, uint8_t *q, uint8_t *scale,
@@ -187,7 +188,8 @@ moe_status moe_combine(const void *y_perm, moe_dtype dt, const float *topk_gate,
                           (hipStream_t)stream);
 }
 
-static moe_status check_gemm(const moe_gemm_desc *g) {
+// the descriptor's mode, dtype, epilogue and shapes (no pointers)
+static moe_status check_gemm_shape(const moe_gemm_desc *g) {
     if (!g) return MOE_ERR_NULL;
     if (g->mode < MOE_GG_FWD || g->mode > MOE_GG_WGRAD) return MOE_ERR_DTYPE;
     if (g->dtype != MOE_F32 && g->dtype != MOE_BF16 && g->dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
@@ -198,8 +200,6 @@ static moe_status check_gemm(const moe_gemm_desc *g) {
         // the group's rows rounded up to 128 bytes) are addressed with 32-bit
         // offsets from one base
         if (g->mode == MOE_GG_WGRAD && g->rows > ((int64_t)1 << 24)) return MOE_ERR_SHAPE;
-        if (!g->a_scale || !g->b_scale) return MOE_ERR_NULL;
-        if (!aligned4(g->a_scale) || !aligned4(g->b_scale)) return MOE_ERR_ALIGN;
     }
     if (g->epilogue == MOE_EPI_SWIGLU_FWD && g->mode != MOE_GG_FWD) return MOE_ERR_DTYPE;
     if (g->epilogue == MOE_EPI_SWIGLU_BWD && g->mode != MOE_GG_DGRAD) return MOE_ERR_DTYPE;
@@ -212,6 +212,16 @@ static moe_status check_gemm(const moe_gemm_desc *g) {
     } else {
         if (!width_ok(g->N) || !width_ok(g->K)) return MOE_ERR_SHAPE;
         if (g->epilogue == MOE_EPI_SWIGLU_FWD && (g->N / 2) % 32) return MOE_ERR_SHAPE;
+    }
+    return MOE_OK;
+}
+
+static moe_status check_gemm(const moe_gemm_desc *g) {
+    moe_status st = check_gemm_shape(g);
+    if (st != MOE_OK) return st;
+    if (g->dtype == MOE_MXFP8) {
+        if (!g->a_scale || !g->b_scale) return MOE_ERR_NULL;
+        if (!aligned4(g->a_scale) || !aligned4(g->b_scale)) return MOE_ERR_ALIGN;
     }
     // with no rows, the row-indexed operands may be empty (null) buffers; WGRAD
     // still writes its (zero) weight gradients
@@ -242,9 +252,35 @@ moe_status moe_grouped_gemm(const moe_gemm_desc *g, void *stream) {
     return gemm_launch(g, (hipStream_t)stream);
 }
 
+moe_status moe_gemm_copy_walk(const moe_gemm_desc *g, const int32_t *host_offsets,
+                              moe_copy_walk *w) {
+    moe_status st = check_gemm_shape(g);
+    if (st != MOE_OK) return st;
+    if (!host_offsets || !w) return MOE_ERR_NULL;
+    if (g->dtype == MOE_F32) return MOE_ERR_DTYPE;
+    if (host_offsets[0] != 0 || host_offsets[g->n_groups] != g->rows) return MOE_ERR_SHAPE;
+    for (int e = 0; e < g->n_groups; e++)
+        if (host_offsets[e + 1] < host_offsets[e]) return MOE_ERR_SHAPE;
+    return gemm_copy_walk(g, host_offsets, w);
+}
+
 size_t moe_backward_workspace_size(const moe_bwd_desc *b) {
     if (!b || b->dtype != MOE_MXFP8) return 0;
     return mx_bwd_layout(b->T * b->k, b->d, b->h, b->E).total;
+}
+
+moe_status moe_backward_workspace_layout(const moe_bwd_desc *b, moe_bwd_ws_layout *out) {
+    if (!b || !out) return MOE_ERR_NULL;
+    if (b->dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+    if (!routing_shape_ok(b->T, b->E, b->k) || !width_ok(b->d) || !hidden_ok(b->h) ||
+        b->d % 128 || b->h % 128 || b->T * b->k > ((int64_t)1 << 24))
+        return MOE_ERR_SHAPE;
+    const MxBwdLayout L = mx_bwd_layout(b->T * b->k, b->d, b->h, b->E);
+    out->row_q = L.a_q; out->row_s = L.a_s;
+    out->col0_q = L.b0_q; out->col0_s = L.b0_s;
+    out->col1_q = L.b1_q; out->col1_s = L.b1_s;
+    out->total = L.total;
+    return MOE_OK;
 }
 
 static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s);

@@ -33,26 +33,12 @@
 //    gg_mfma (MXFP8, and the bf16 SwiGLU backward) has every wave do both.
 #include <type_traits>
 #include <utility>
+#include <vector>
 
 #include "common.h"
+#include "copy_plan.h"
 
 namespace moe {
-
-struct GemmArgs {
-    const void *A;
-    const void *B;
-    void *C;
-    const void *aux;
-    void *aux_out;
-    const int32_t *offsets;
-    const uint8_t *a_scale;   // MXFP8 E8M0 scales
-    const uint8_t *b_scale;
-    int64_t rows;
-    int M, N, K;
-    int E;
-    int h;          // hidden width (SwiGLU epilogues)
-    int accumulate; // WGRAD: add to C instead of overwriting it
-};
 
 // ---------------------------------------------------------------------------
 // tile table shared by the kernels
@@ -254,12 +240,33 @@ MOE_DEV WgSchedule build_wgrad_schedule(const int32_t *s_off, int E, int per_e, 
     return w;
 }
 
+// position p of this XCD's WGRAD list -> (group e, output m-tile mi, n-tile nt).
+// An expert's tiles come in groups of kWgGroupM m-tiles, m-tile fastest within
+// a group: the XCD's concurrent tiles form a block of m-tiles x n-tiles, so
+// both operand panels are shared from L2 by several tiles.
+MOE_DEV void decode_wgrad_tile(const WgSchedule &ws, const int32_t *s_list, int xcd, int p,
+                               int mtiles, int n_tiles, int &e, int &mi, int &nt) {
+    const int per_e = mtiles * n_tiles;
+    int tt;
+    if (p < ws.n_split * ws.cs) {          // this XCD's chunk of a split expert
+        e = s_list[p / ws.cs];
+        tt = xcd * ws.cs + p % ws.cs;
+    } else {                               // a whole expert of this XCD
+        const int p2 = p - ws.n_split * ws.cs;
+        e = s_list[128 + p2 / per_e];
+        tt = p2 % per_e;
+    }
+    const int grp = tt / (kWgGroupM * n_tiles), first_m = grp * kWgGroupM;
+    const int gm = min(mtiles - first_m, kWgGroupM);
+    const int tg = tt - grp * kWgGroupM * n_tiles;
+    mi = first_m + tg % gm;
+    nt = tg / gm;
+}
+
 // ---------------------------------------------------------------------------
 // MFMA kernel: bf16 (v_mfma_f32_32x32x16_bf16) and MXFP8
 // (v_mfma_scale_f32_32x32x64_f8f6f4 with E8M0 block scales)
 
-// Each pipeline step covers 128 bytes of K per row: 64 bf16 or 128 fp8.
-constexpr int kStepBytes = 128;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 #define MOE_LDS __attribute__((address_space(3)))
@@ -268,13 +275,7 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // scale words of rows that have none): zero-initialised device memory.
 __device__ uint4 g_zero_chunk[64] = {};
 
-// K-layout LDS tile: [R rows][128 bytes]. LDS has 64 4-byte banks, i.e. two
-// 128-byte rows per bank cycle; XOR-swizzling the 16-byte chunks with
-// (row/2) % 8 puts the 16 rows that a ds_read_b128 serves per cycle on 16
-// different 16-byte bank groups (measured: 2x the read rate of a row % 8
-// swizzle, 7x that of no swizzle).
-MOE_DEV int kl_swz(int row) { return (row >> 1) & 7; }
-MOE_DEV int kl_chunk(int row, int kc) { return row * 8 + (kc ^ kl_swz(row)); }
+// (K-layout LDS tiles: kl_chunk in copy_plan.h)
 
 // MN-layout LDS tile (bf16 only): [64 k][R] bf16, i.e. the global tile copied
 // as is. Chunk c of row k sits at c ^ ((k & 3) << 2): the four k rows that one
@@ -368,63 +369,34 @@ MOE_DEV const char *uniform_ptr(const char *p) {
     return reinterpret_cast<const char *>((uintptr_t)((hi << 32) | lo));
 }
 
-// One operand tile per stage, copied HBM -> LDS by global_load_lds_dwordx4:
-// every instruction writes 64 lanes x 16 bytes to a contiguous 1 KiB of LDS,
-// so each lane picks the global chunk that belongs at its LDS position.
-// NW waves share the copy; IPW instructions per wave.
-//
-// KL = true : K-layout tile [R rows][128 bytes]; src rows are K-contiguous.
-// KL = false: MN-layout tile [64 k][R cols] bf16; src is [k][ld], cols contiguous.
-//
-// Rows past the operand's end (KL) and columns past it (MN) are read from the
-// last valid row / column instead: they meet only output rows or columns
-// that the epilogue does not store. K past the reduction's end is different
-// (it would add to valid outputs): a step that reaches past klim takes zeros
-// for those chunks.
+// One operand tile per stage, copied HBM -> LDS by global_load_lds_dwordx4
+// with the geometry of CopyGeom (copy_plan.h): the tile origin in SGPRs,
+// advanced by one scalar add per K step, plus a fixed 32-bit offset per lane
+// and instruction.
 template <int R, bool KL, int NW>
-struct DmaTile {
-    static constexpr int CHUNKS = R * 8;
-    static constexpr int IPW = CHUNKS / 64 / NW;
-    static constexpr int STEP = KL ? kStepBytes : 64;   // K per step: bytes (KL) or rows (MN)
-    static_assert(IPW >= 1 && CHUNKS % (64 * NW) == 0, "tile/wave mismatch");
-    static_assert(KL || R >= 128, "MN-layout swizzle needs >= 16 chunks per row");
+struct DmaTile : CopyGeom<R, KL, NW> {
+    using G = CopyGeom<R, KL, NW>;
+    static constexpr int IPW = G::IPW;
+    static constexpr int STEP = G::STEP;
     const char *base;          // tile origin at step 0 (wave-uniform)
     int64_t kstride;           // bytes to advance per step
     uint32_t voff[IPW];        // per lane and instruction: byte offset of its chunk
-
-    // chunk position of lane `lane`'s instruction i: (row, 16-byte column)
-    MOE_DEV static int pos(int i, int wave, int lane) { return (wave * IPW + i) * 64 + lane; }
-    // the chunk's K position: byte offset in the step (KL) or k row (MN)
-    MOE_DEV static int kpos(int i, int wave, int lane) {
-        const int p = pos(i, wave, lane);
-        if constexpr (KL) return ((p & 7) ^ kl_swz(p >> 3)) * 16;
-        else return p / (R / 8);
-    }
 
     // KL: row_off(r) -> byte offset from b of tile row r's K run (< 2^32)
     template <typename RowFn>
     MOE_DEV void setup_kl(const char *b, RowFn row_off, int wave, int lane) {
         base = uniform_ptr(b);
 #pragma unroll
-        for (int i = 0; i < IPW; i++) {
-            const int p = pos(i, wave, lane);
-            const int row = p >> 3, kc = (p & 7) ^ kl_swz(row);
-            voff[i] = row_off(row) + (uint32_t)(kc * 16);
-        }
-        kstride = kStepBytes;
+        for (int i = 0; i < IPW; i++) voff[i] = G::kl_off(i, wave, lane, row_off);
+        kstride = G::kstride(0);
     }
     // MN: b = element (k = 0, col 0) of the tile, ld = row pitch in bytes,
     // cvalid = valid columns (>= 1)
     MOE_DEV void setup_mn(const char *b, int64_t ld, int cvalid, int wave, int lane) {
         base = uniform_ptr(b);
 #pragma unroll
-        for (int i = 0; i < IPW; i++) {
-            const int p = pos(i, wave, lane);
-            const int k = p / (R / 8), c = (p % (R / 8)) ^ ((k & 3) << 2);
-            const int cs = c * 8 < cvalid ? c : (cvalid - 1) >> 3;
-            voff[i] = (uint32_t)(k * ld + cs * 16);
-        }
-        kstride = 64 * ld;
+        for (int i = 0; i < IPW; i++) voff[i] = G::mn_off(i, wave, lane, ld, cvalid);
+        kstride = G::kstride(ld);
     }
     // enqueue the copy of step kt; klim = K bytes (KL) or K rows (MN)
     MOE_DEV void issue(uint4 *lds, int kt, int klim, int wave) const {
@@ -437,7 +409,7 @@ struct DmaTile {
             const int lane = threadIdx.x & 63;
 #pragma unroll
             for (int i = 0; i < IPW; i++) {
-                const bool ok = k0 + kpos(i, wave, lane) < klim;
+                const bool ok = G::in_k(i, wave, lane, kt, klim);
                 const void *s = ok ? (const void *)(b + voff[i]) : (const void *)&g_zero_chunk[lane];
                 dma16(s, lds + (wave * IPW + i) * 64);
             }
@@ -499,7 +471,6 @@ void gg_mfma(GemmArgs g) {
     static_assert(EPI != MOE_EPI_SWIGLU_FWD || TN % 2 == 0, "SwiGLU pairs gate/up sub-tiles");
     // FP8: the stage's BM + BN scale words are copied SPW per lane
     constexpr int SPW = FP8 ? (BM + BN + NW * 64 - 1) / (NW * 64) : 0;
-    constexpr int ESZ = FP8 ? 1 : 2;
     constexpr bool A_KL = FP8 || MODE != MOE_GG_WGRAD;
     constexpr bool B_KL = FP8 || MODE == MOE_GG_FWD;
     using AT = DmaTile<BM, A_KL, NW>;
@@ -576,82 +547,21 @@ void gg_mfma(GemmArgs g) {
     const uint8_t *AS = g.a_scale;
     const uint8_t *BS = g.b_scale;
 
-    // FP8 with batched scales: FWD/DGRAD when every row's scales come in whole
-    // 16-byte groups; WGRAD always -- the column-block scale array is sized by
-    // mxfp8_col_blocks, whose spare blocks keep a 16-byte read past the end of
-    // a column's last (partial) group in bounds, and those bytes belong to
-    // steps that do not exist
-    const bool sbatch = FP8 && (MODE == MOE_GG_WGRAD || (g.K / 32) % 16 == 0);
+    using P = TilePlan<MODE, EPI, FP8, BM, BN, WTN>;
+    // FP8: scales batched 16 bytes per row every 4th step, or 4 bytes per step
+    const bool sbatch = P::scale_batched(g);
     (void)sbatch;
 
-    // coordinates of one output tile
-    struct TileC {
-        int e, row0, row_end, m0, n0, nt, klim, kpad, sb0;
-    };
     auto decode = [&](int pos) {
-        TileC t;
-        t.row0 = 0; t.row_end = 0; t.m0 = 0; t.kpad = 0; t.sb0 = 0;
         if constexpr (MODE == MOE_GG_WGRAD) {
-            const int mtiles = (g.M + BM - 1) / BM;
-            const int per_e = mtiles * n_tiles;
-            int tt;
-            if (pos < ws.n_split * ws.cs) {        // this XCD's chunk of a split expert
-                t.e = s_xpre[pos / ws.cs];
-                tt = xcd * ws.cs + pos % ws.cs;
-            } else {                               // a whole expert of this XCD
-                const int p2 = pos - ws.n_split * ws.cs;
-                t.e = s_xpre[128 + p2 / per_e];
-                tt = p2 % per_e;
-            }
-            // groups of kWgGroupM m-tiles, m-tile fastest within a group: the
-            // XCD's concurrent tiles form a block of m-tiles x n-tiles, so both
-            // operand panels are shared from L2 by several tiles
-            const int grp = tt / (kWgGroupM * n_tiles), first_m = grp * kWgGroupM;
-            const int gm = min(mtiles - first_m, kWgGroupM);
-            const int tg = tt - grp * kWgGroupM * n_tiles;
-            t.nt = tg / gm;
-            t.m0 = (first_m + tg % gm) * BM;
-            t.row0 = s_off[t.e];
-            if constexpr (FP8) {
-                t.sb0 = s_tile[t.e];
-                t.kpad = (s_tile[t.e + 1] - t.sb0) * 128;
-                t.klim = t.kpad;                   // bytes of K per row
-            } else {
-                t.klim = s_off[t.e + 1] - t.row0;  // reduction over the group's rows
-            }
+            int e, mi, nt;
+            decode_wgrad_tile(ws, s_xpre, xcd, pos, (g.M + BM - 1) / BM, n_tiles, e, mi, nt);
+            // FP8: s_tile holds each group's first 128-row block of the column layout
+            return P::wgrad_tile(s_off, s_tile, e, mi, nt);
         } else {
-            int mt_e;
-            decode_row_tile(rs, s_tile, s_chunk, s_xpre, E, xcd, pos, t.e, mt_e, t.nt);
-            t.row0 = s_off[t.e] + mt_e * BM;
-            t.row_end = s_off[t.e + 1];
-            t.klim = g.K * ESZ;
-        }
-        t.n0 = t.nt * BN;
-        return t;
-    };
-
-    // B row index (in B's N rows) of tile column n, or -1
-    auto b_row_index = [&](const TileC &t, int n) -> int {
-        if constexpr (MODE == MOE_GG_FWD && EPI == MOE_EPI_SWIGLU_FWD) {
-            // each wave's panel is laid out as [gate rows | up rows] of the
-            // same hidden units
-            const int wc = n / WTN, off = n % WTN, half = WTN / 2;
-            const int j = t.nt * (BN / 2) + wc * half + (off % half);
-            if (j >= g.h) return -1;
-            return off < half ? j : g.h + j;
-        } else {
-            const int r = t.n0 + n;
-            return r < g.N ? r : -1;
-        }
-    };
-    // the same with columns past the end mapped to the last valid B row
-    auto b_row_clamped = [&](const TileC &t, int n) -> int {
-        if constexpr (MODE == MOE_GG_FWD && EPI == MOE_EPI_SWIGLU_FWD) {
-            const int wc = n / WTN, off = n % WTN, half = WTN / 2;
-            const int j = min(t.nt * (BN / 2) + wc * half + (off % half), g.h - 1);
-            return off < half ? j : g.h + j;
-        } else {
-            return min(t.n0 + n, g.N - 1);
+            int e, mt_e, nt;
+            decode_row_tile(rs, s_tile, s_chunk, s_xpre, E, xcd, pos, e, mt_e, nt);
+            return P::row_tile(g, s_off, e, mt_e, nt);
         }
     };
 
@@ -660,59 +570,24 @@ void gg_mfma(GemmArgs g) {
     BT tb;
     const char *ssrc[SPW > 0 ? SPW : 1];
     auto setup = [&](const TileC &t) {
-        if constexpr (MODE == MOE_GG_WGRAD) {
-            if constexpr (FP8) {
-                // column-block layout: expert e's A is [M][kpad] at byte
-                // sb0*128*M (B likewise); offsets from the tile's first row
-                // stay below BN * kpad <= 2^32 (the host bounds the rows to 2^24)
-                const uint32_t kp = (uint32_t)t.kpad;
-                ta.setup_kl(A + (int64_t)t.sb0 * 128 * g.M + (int64_t)t.m0 * t.kpad,
-                            [&](int r) { return (uint32_t)min(r, g.M - 1 - t.m0) * kp; }, wave, lane);
-                tb.setup_kl(B + (int64_t)t.sb0 * 128 * g.N + (int64_t)t.n0 * t.kpad,
-                            [&](int n) { return (uint32_t)min(n, g.N - 1 - t.n0) * kp; }, wave, lane);
-            } else {
-                ta.setup_mn(A + ((int64_t)t.row0 * g.M + t.m0) * 2, (int64_t)g.M * 2, g.M - t.m0, wave, lane);
-                tb.setup_mn(B + ((int64_t)t.row0 * g.N + t.n0) * 2, (int64_t)g.N * 2, g.N - t.n0, wave, lane);
-            }
+        if constexpr (A_KL) {
+            ta.setup_kl(A + P::a_origin(g, t), [&](int r) { return P::a_row_off(g, t, r); }, wave, lane);
         } else {
-            const int last = t.row_end - t.row0 - 1;      // a tile has at least one row
-            const uint32_t pitch = (uint32_t)(g.K * ESZ);
-            ta.setup_kl(A + (int64_t)t.row0 * g.K * ESZ,
-                        [&](int r) { return (uint32_t)min(r, last) * pitch; }, wave, lane);
-            if constexpr (B_KL) {
-                tb.setup_kl(B + (int64_t)t.e * g.N * g.K * ESZ,
-                            [&](int n) { return (uint32_t)b_row_clamped(t, n) * pitch; }, wave, lane);
-            } else {
-                tb.setup_mn(B + ((int64_t)t.e * g.K * g.N + t.n0) * 2, (int64_t)g.N * 2, g.N - t.n0, wave,
-                            lane);
-            }
+            ta.setup_mn(A + P::a_origin(g, t), P::a_ld(g), P::a_cvalid(g, t), wave, lane);
+        }
+        if constexpr (B_KL) {
+            tb.setup_kl(B + P::b_origin(g, t), [&](int n) { return P::b_row_off(g, t, n); }, wave, lane);
+        } else {
+            tb.setup_mn(B + P::b_origin(g, t), P::b_ld(g), P::b_cvalid(g, t), wave, lane);
         }
         // FP8: sources of this lane's scale words (rows sr of the stage's
-        // [A rows | B rows | unused] scale array) for step 0; 4 bytes per step
+        // [A rows | B rows | unused] scale array) for step 0
         if constexpr (FP8) {
 #pragma unroll
             for (int q = 0; q < SPW; q++) {
                 const int sr = (q * NW + wave) * 64 + lane;
-                ssrc[q] = nullptr;
-                if constexpr (MODE == MOE_GG_WGRAD) {
-                    const int nbk = t.kpad / 32;           // scale blocks per row
-                    if (sr < BM) {
-                        const int m = t.m0 + sr;
-                        if (m < g.M) ssrc[q] = (const char *)AS + (int64_t)t.sb0 * 4 * g.M + (int64_t)m * nbk;
-                    } else if (sr < BM + BN) {
-                        const int c = t.n0 + sr - BM;
-                        if (c < g.N) ssrc[q] = (const char *)BS + (int64_t)t.sb0 * 4 * g.N + (int64_t)c * nbk;
-                    }
-                } else {
-                    const int nbk = g.K / 32;
-                    if (sr < BM) {
-                        const int gr = t.row0 + sr;
-                        if (gr < t.row_end) ssrc[q] = (const char *)AS + (int64_t)gr * nbk;
-                    } else if (sr < BM + BN) {
-                        const int br = b_row_index(t, sr - BM);
-                        if (br >= 0) ssrc[q] = (const char *)BS + ((int64_t)t.e * g.N + br) * nbk;
-                    }
-                }
+                const int64_t o = P::scale_off(g, t, sr);
+                ssrc[q] = o < 0 ? nullptr : (const char *)(P::scale_operand(sr) == 0 ? AS : BS) + o;
             }
         }
     };
@@ -741,7 +616,7 @@ void gg_mfma(GemmArgs g) {
         }
         ta.issue(st, kt, klim, wave);
         // bf16 DGRAD: klim is A's K extent in bytes; B (MN layout) counts K rows
-        tb.issue(st + BM * 8, kt, (A_KL && !B_KL) ? klim / ESZ : klim, wave);
+        tb.issue(st + BM * 8, kt, P::b_klim(klim), wave);
         if constexpr (FP8) {
             if (!sbatch) {
                 uint4 *sarea = lds_pool + STAGES * STAGE_U4 + si * SCALE_U4;
@@ -754,9 +629,7 @@ void gg_mfma(GemmArgs g) {
             }
         }
     };
-    auto nk_of = [](int klim) {
-        return (klim + (A_KL ? kStepBytes : 64) - 1) / (A_KL ? kStepBytes : 64);
-    };
+    auto nk_of = [](int klim) { return P::nk_of(klim); };
     // start the pipeline of a tile: its first STAGES-1 steps
     auto prologue = [&](const TileC &t) {
         const int n = nk_of(t.klim);
@@ -1181,20 +1054,27 @@ void gg_mfma(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 grouped GEMM with split roles (FWD, DGRAD, WGRAD). The workgroup's waves
-// 0..NC-1 are consumers: LDS fragment reads, MFMAs and the tile's epilogue.
-// Waves NC..NC+NP-1 are producers: they issue every global -> LDS copy and
-// wait only on those. A wave's vector-memory counter covers its loads and
-// stores together, so with one role per wave the consumers never wait on the
-// copies and a tile's stores drain while the next tile is multiplied; the
-// producers run up to STAGES-1 steps ahead, across tile boundaries.
+// Grouped GEMM with split roles (bf16 and MXFP8; FWD, DGRAD, WGRAD). The
+// workgroup's waves 0..NC-1 are consumers: LDS fragment reads, MFMAs and the
+// tile's epilogue. Waves NC..NC+NP-1 are producers: they issue every
+// global -> LDS copy and wait only on those. A wave's vector-memory counter
+// covers its loads and stores together, so with one role per wave the
+// consumers never wait on the copies and a tile's stores drain while the next
+// tile is multiplied; the producers run up to STAGES-1 steps ahead, across
+// tile boundaries.
 // One workgroup barrier per K step, numbered over the workgroup's tiles:
 // before barrier G the producers have landed step G and the consumers have
 // finished reading step G-1, whose buffer the producers refill after it.
+// MXFP8 block scales: either 4 bytes per row and step into the step's stage,
+// or (when batched) 16 bytes per row covering 4 steps of a tile into one slot
+// of a 2-slot ring. A batch is started only once the consumers are done with
+// the batch that last held its slot: when the batch before it has a single
+// step (a tile of K % 512 in (0, 128]), the producers wait one more barrier.
 // Tiles, schedules, LDS layouts and the order of every MFMA over K are those
 // of gg_mfma, so both kernels give the same bits.
 
-template <int MODE, int EPI, int BM, int BN, int WM, int WN, int NP, int STAGES, bool ACC = false>
+template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int NP, int STAGES,
+          bool ACC = false>
 __global__ __launch_bounds__((WM * WN + NP) * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void gg_ws(GemmArgs g) {
     constexpr int NC = WM * WN;
@@ -1203,14 +1083,20 @@ void gg_ws(GemmArgs g) {
     static_assert(TM >= 1 && TN >= 1, "wave tile");
     static_assert(EPI != MOE_EPI_SWIGLU_FWD || TN % 2 == 0, "SwiGLU pairs gate/up sub-tiles");
     static_assert(EPI != MOE_EPI_SWIGLU_BWD, "the SwiGLU backward runs on gg_mfma");
-    constexpr bool A_KL = MODE != MOE_GG_WGRAD;
-    constexpr bool B_KL = MODE == MOE_GG_FWD;
+    static_assert(STAGES == 3, "the producers' wait assumes one step in flight behind the next");
+    constexpr bool A_KL = FP8 || MODE != MOE_GG_WGRAD;
+    constexpr bool B_KL = FP8 || MODE == MOE_GG_FWD;
     using AT = DmaTile<BM, A_KL, NP>;
     using BT = DmaTile<BN, B_KL, NP>;
-    constexpr int IPP = AT::IPW + BT::IPW;          // copies per producer wave per step
+    constexpr int IPP = AT::IPW + BT::IPW;          // operand copies per producer wave per step
     constexpr int STAGE_U4 = (BM + BN) * 8;
-    constexpr int ASTEP = A_KL ? kStepBytes : 64;   // K per step: bytes of A rows, or rows
-    __shared__ __attribute__((aligned(1024))) uint4 lds_pool[STAGES * STAGE_U4];
+    // MXFP8 scales: SPW rows per producer lane; per-step areas (one per
+    // stage) or the batched 2-slot ring, in the same region
+    constexpr int SPW = FP8 ? (BM + BN + NP * 64 - 1) / (NP * 64) : 0;
+    constexpr int SCALE_U4 = SPW * NP * 64 * 4 / 16;
+    constexpr int SROWS = FP8 ? ((BM + BN + 63) / 64) * 64 : 0;
+    constexpr int SREG_U4 = FP8 ? (2 * SROWS > STAGES * SCALE_U4 ? 2 * SROWS : STAGES * SCALE_U4) : 0;
+    __shared__ __attribute__((aligned(1024))) uint4 lds_pool[STAGES * STAGE_U4 + SREG_U4];
     __shared__ int32_t s_off[257];
     __shared__ int32_t s_tile[257];
     __shared__ int32_t s_chunk[257];
@@ -1225,7 +1111,9 @@ void gg_ws(GemmArgs g) {
     RowSchedule rs;
     WgSchedule ws;
     if constexpr (MODE == MOE_GG_WGRAD) {
-        load_offsets(g.offsets, E, s_off);
+        // MXFP8: s_tile[e] = the group's first 128-row block of the column layout
+        if constexpr (FP8) build_tile_table(g.offsets, E, 128, s_off, s_tile);
+        else load_offsets(g.offsets, E, s_off);
         n_tiles = (g.N + BN - 1) / BN;
         ws = build_wgrad_schedule(s_off, E, ((g.M + BM - 1) / BM) * n_tiles, xcd, s_chunk, s_xpre);
         total = ws.total;
@@ -1238,76 +1126,45 @@ void gg_ws(GemmArgs g) {
     const char *A = reinterpret_cast<const char *>(g.A);
     const char *B = reinterpret_cast<const char *>(g.B);
 
-    struct TileC {
-        int e, row0, row_end, m0, n0, nt, klim;
-    };
+    using P = TilePlan<MODE, EPI, FP8, BM, BN, WTN>;
+    const bool sbatch = P::scale_batched(g);
+    (void)sbatch;
     auto decode = [&](int pos) {
-        TileC t;
-        t.row_end = 0;
-        t.m0 = 0;
         if constexpr (MODE == MOE_GG_WGRAD) {
-            const int mtiles = (g.M + BM - 1) / BM;
-            const int per_e = mtiles * n_tiles;
-            int tt;
-            if (pos < ws.n_split * ws.cs) {
-                t.e = s_xpre[pos / ws.cs];
-                tt = xcd * ws.cs + pos % ws.cs;
-            } else {
-                const int p2 = pos - ws.n_split * ws.cs;
-                t.e = s_xpre[128 + p2 / per_e];
-                tt = p2 % per_e;
-            }
-            const int grp = tt / (kWgGroupM * n_tiles), first_m = grp * kWgGroupM;
-            const int gm = min(mtiles - first_m, kWgGroupM);
-            const int tg = tt - grp * kWgGroupM * n_tiles;
-            t.nt = tg / gm;
-            t.m0 = (first_m + tg % gm) * BM;
-            t.row0 = s_off[t.e];
-            t.klim = s_off[t.e + 1] - t.row0;      // reduction over the group's rows
+            int e, mi, nt;
+            decode_wgrad_tile(ws, s_xpre, xcd, pos, (g.M + BM - 1) / BM, n_tiles, e, mi, nt);
+            return P::wgrad_tile(s_off, FP8 ? s_tile : nullptr, e, mi, nt);
         } else {
-            int mt_e;
-            decode_row_tile(rs, s_tile, s_chunk, s_xpre, E, xcd, pos, t.e, mt_e, t.nt);
-            t.row0 = s_off[t.e] + mt_e * BM;
-            t.row_end = s_off[t.e + 1];
-            t.klim = g.K * 2;                       // bytes of K per A row
+            int e, mt_e, nt;
+            decode_row_tile(rs, s_tile, s_chunk, s_xpre, E, xcd, pos, e, mt_e, nt);
+            return P::row_tile(g, s_off, e, mt_e, nt);
         }
-        t.n0 = t.nt * BN;
-        return t;
     };
-    auto nk_of = [](int klim) { return (klim + ASTEP - 1) / ASTEP; };
+    auto nk_of = [](int klim) { return P::nk_of(klim); };
     auto stage = [&](int s) { return lds_pool + s * STAGE_U4; };
 
     if (producer) {
         const int pw = wave - NC;
         AT ta;
         BT tb;
-        // B row (in B's N rows) of tile column n, clamped into range; SwiGLU:
-        // each consumer wave's columns are gate rows then the up rows of the
-        // same hidden units
-        auto b_row_clamped = [&](const TileC &t, int n) -> int {
-            if constexpr (MODE == MOE_GG_FWD && EPI == MOE_EPI_SWIGLU_FWD) {
-                const int wc = n / WTN, off = n % WTN, half = WTN / 2;
-                const int j = min(t.nt * (BN / 2) + wc * half + (off % half), g.h - 1);
-                return off < half ? j : g.h + j;
-            } else {
-                return min(t.n0 + n, g.N - 1);
-            }
-        };
+        const char *ssrc[SPW > 0 ? SPW : 1];
         auto setup = [&](const TileC &t) {
-            if constexpr (MODE == MOE_GG_WGRAD) {
-                ta.setup_mn(A + ((int64_t)t.row0 * g.M + t.m0) * 2, (int64_t)g.M * 2, g.M - t.m0, pw, lane);
-                tb.setup_mn(B + ((int64_t)t.row0 * g.N + t.n0) * 2, (int64_t)g.N * 2, g.N - t.n0, pw, lane);
+            if constexpr (A_KL) {
+                ta.setup_kl(A + P::a_origin(g, t), [&](int r) { return P::a_row_off(g, t, r); }, pw, lane);
             } else {
-                const int last = t.row_end - t.row0 - 1;
-                const uint32_t pitch = (uint32_t)(g.K * 2);
-                ta.setup_kl(A + (int64_t)t.row0 * g.K * 2,
-                            [&](int r) { return (uint32_t)min(r, last) * pitch; }, pw, lane);
-                if constexpr (B_KL) {
-                    tb.setup_kl(B + (int64_t)t.e * g.N * g.K * 2,
-                                [&](int n) { return (uint32_t)b_row_clamped(t, n) * pitch; }, pw, lane);
-                } else {
-                    tb.setup_mn(B + ((int64_t)t.e * g.K * g.N + t.n0) * 2, (int64_t)g.N * 2, g.N - t.n0,
-                                pw, lane);
+                ta.setup_mn(A + P::a_origin(g, t), P::a_ld(g), P::a_cvalid(g, t), pw, lane);
+            }
+            if constexpr (B_KL) {
+                tb.setup_kl(B + P::b_origin(g, t), [&](int n) { return P::b_row_off(g, t, n); }, pw, lane);
+            } else {
+                tb.setup_mn(B + P::b_origin(g, t), P::b_ld(g), P::b_cvalid(g, t), pw, lane);
+            }
+            if constexpr (FP8) {
+#pragma unroll
+                for (int q = 0; q < SPW; q++) {
+                    const int sr = (q * NP + pw) * 64 + lane;
+                    const int64_t o = P::scale_off(g, t, sr);
+                    ssrc[q] = o < 0 ? nullptr : (const char *)(P::scale_operand(sr) == 0 ? g.a_scale : g.b_scale) + o;
                 }
             }
         };
@@ -1325,28 +1182,67 @@ void gg_ws(GemmArgs g) {
             }
             ikt = 0;
         };
-        auto issue_next = [&](int gs) -> bool {
-            if (ip >= total) return false;
-            uint4 *st = stage(gs);
+        // batched scales: batches started, and the last step of the latest
+        // batch of each ring slot's parity
+        int nbatch = 0, bend[2] = {-1, -1};
+        // enqueue the next step (global index x) into stage x % STAGES
+        auto issue_next = [&](int x) {
+            uint4 *st = stage(x % STAGES);
+            if constexpr (FP8) {
+                // scales first: a wait for this step's operand copies then
+                // also covers them (copies complete in issue order)
+                if (sbatch) {
+                    if ((ikt & 3) == 0) {
+                        if (nbatch > 0) bend[(nbatch - 1) & 1] = x - 1;
+                        uint4 *ring = lds_pool + STAGES * STAGE_U4 + (nbatch & 1) * SROWS;
+#pragma unroll
+                        for (int q = 0; q < SPW; q++) {
+                            if ((q * NP + pw) * 64 >= BM + BN) continue;   // wave-uniform
+                            const void *src = ssrc[q] ? (const void *)(ssrc[q] + (ikt >> 2) * 16)
+                                                      : (const void *)&g_zero_chunk[lane];
+                            dma16(src, ring + (q * NP + pw) * 64);
+                        }
+                        nbatch++;
+                    }
+                } else {
+                    uint4 *sarea = lds_pool + STAGES * STAGE_U4 + (x % STAGES) * SCALE_U4;
+#pragma unroll
+                    for (int q = 0; q < SPW; q++) {
+                        const void *src = ssrc[q] ? (const void *)(ssrc[q] + ikt * 4)
+                                                  : (const void *)&g_zero_chunk[lane];
+                        dma4(src, sarea + (q * NP + pw) * 16);
+                    }
+                }
+            }
             ta.issue(st, ikt, iklim, pw);
             // bf16 DGRAD: iklim is A's K extent in bytes; B (MN layout) counts K rows
-            tb.issue(st + BM * 8, ikt, (A_KL && !B_KL) ? iklim / 2 : iklim, pw);
+            tb.issue(st + BM * 8, ikt, P::b_klim(iklim), pw);
             if (++ikt == nk_of(iklim)) {
                 ip += workers;
                 seek();
             }
-            return true;
+        };
+        // issue every step the consumers' progress allows: done = steps they
+        // have finished reading; a step's stage is free once the step
+        // STAGES before it is done, a batch's ring slot once the batch two
+        // before it is
+        int issued = 0;
+        auto pump = [&](int done, int limit) {
+            while (ip < total && issued <= limit) {
+                if (FP8 && sbatch && (ikt & 3) == 0 && bend[nbatch & 1] >= done) break;
+                issue_next(issued);
+                issued++;
+            }
         };
         seek();
-        int issued = 0;
-        for (int s = 0; s < STAGES - 1; s++)
-            if (issue_next(s)) issued++;
+        pump(0, STAGES - 2);
         for (int G = 0; G < issued; G++) {
-            // step G must have landed; the steps after it may stay in flight
+            // step G must have landed; at most one step after it is in flight
+            // (each step's last IPP copies are its operands, issued last)
             if (issued - 1 - G >= STAGES - 2) wait_vmem<(STAGES - 2) * IPP>();
             else wait_vmem<0>();
             lds_sync();                  // barrier G
-            if (issue_next((G + STAGES - 1) % STAGES)) issued++;
+            pump(G, G + STAGES - 1);
         }
         return;
     }
@@ -1476,7 +1372,73 @@ void gg_ws(GemmArgs g) {
             }
         }
     };
-    int G = 0;
+    // one MXFP8 K step (128 bytes: two 64-wide slices) from buffer st; the
+    // scale words from the ring slot of its batch (word kt % 4) or from the
+    // step's own area
+    auto step8 = [&](int st, int kt, int slot) {
+      if constexpr (FP8) {
+        const uint4 *sa = stage(st);
+        const uint4 *sb = sa + BM * 8;
+        uint32_t swa[TM], swb[TN];
+        if (sbatch) {
+            const uint32_t *rw =
+                reinterpret_cast<const uint32_t *>(lds_pool + STAGES * STAGE_U4 + slot * SROWS);
+            const int w = kt & 3;
+#pragma unroll
+            for (int i = 0; i < TM; i++) swa[i] = rw[(wm * WTM + i * 32 + (lane & 31)) * 4 + w];
+#pragma unroll
+            for (int j = 0; j < TN; j++) swb[j] = rw[(BM + wn * WTN + j * 32 + (lane & 31)) * 4 + w];
+        } else {
+            const uint32_t *sw =
+                reinterpret_cast<const uint32_t *>(lds_pool + STAGES * STAGE_U4 + st * SCALE_U4);
+#pragma unroll
+            for (int i = 0; i < TM; i++) swa[i] = sw[wm * WTM + i * 32 + (lane & 31)];
+#pragma unroll
+            for (int j = 0; j < TN; j++) swb[j] = sw[BM + wn * WTN + j * 32 + (lane & 31)];
+        }
+        i32x8 fa[2][TM], fb[2][TN];
+#pragma unroll
+        for (int i = 0; i < TM; i++) fa[0][i] = AT::frag8(sa, wm * WTM + i * 32, 0, lane);
+#pragma unroll
+        for (int j = 0; j < TN; j++) fb[0][j] = BT::frag8(sb, wn * WTN + j * 32, 0, lane);
+#pragma unroll
+        for (int sl = 0; sl < 2; sl++) {
+            // lane l supplies the scale of (row l % 32, block 2 sl + l / 32)
+            const int sh = 8 * (2 * sl + (lane >> 5));
+            if (MODE != MOE_GG_WGRAD && sl == 0) {
+                // row GEMMs: the reads of slice 1 go one between each two MFMAs
+#pragma unroll
+                for (int t = 0; t < TM * TN; t++) {
+                    if (t < TM) fa[1][t] = AT::frag8(sa, wm * WTM + t * 32, 1, lane);
+                    else if (t < TM + TN) fb[1][t - TM] = BT::frag8(sb, wn * WTN + (t - TM) * 32, 1, lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int i = t / TN, j = t % TN;
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fa[0][i], fb[0][j], acc[i][j], 0, 0, 0, (int)((swa[i] >> sh) & 0xff), 0,
+                        (int)((swb[j] >> sh) & 0xff));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                continue;
+            }
+            if (sl == 0) {
+#pragma unroll
+                for (int i = 0; i < TM; i++) fa[1][i] = AT::frag8(sa, wm * WTM + i * 32, 1, lane);
+#pragma unroll
+                for (int j = 0; j < TN; j++) fb[1][j] = BT::frag8(sb, wn * WTN + j * 32, 1, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch above the MFMAs
+#pragma unroll
+            for (int i = 0; i < TM; i++)
+#pragma unroll
+                for (int j = 0; j < TN; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0, (int)((swa[i] >> sh) & 0xff), 0,
+                        (int)((swb[j] >> sh) & 0xff));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    int G = 0, nbatch = 0;
     for (int pos = worker; pos < total; pos += workers) {
         const TileC t = decode(pos);
         const int nk = nk_of(t.klim);
@@ -1484,7 +1446,12 @@ void gg_ws(GemmArgs g) {
         zero();
         for (int kt = 0; kt < nk; kt++, G++) {
             lds_sync();                             // barrier G: step G is in buffer G % STAGES
-            step(G % STAGES);
+            if constexpr (FP8) {
+                if (sbatch && (kt & 3) == 0) nbatch++;
+                step8(G % STAGES, kt, (nbatch - 1) & 1);
+            } else {
+                step(G % STAGES);
+            }
         }
         epilogue(t);                                // its stores drain while the next tile runs
     }
@@ -1690,16 +1657,20 @@ __global__ __launch_bounds__(256) void gg_f32(GemmArgs g) {
 
 // bf16: 8 consumer waves (2 x 4, 64 x 64 each) and 4 producer waves on the
 // same 128 x 256 tiles and 3 stages as gg_mfma
-template <int MODE, int EPI>
+constexpr int kWsBM = 128, kWsBN = 256, kWsWM = 2, kWsWN = 4, kWsNP = 4, kWsStages = 3;
+
+template <int MODE, int EPI, bool FP8>
 static void launch_ws(const GemmArgs &a, hipStream_t s) {
     const int grid = (num_cus() + 7) / 8 * 8;
+    constexpr int threads = (kWsWM * kWsWN + kWsNP) * 64;
     if constexpr (MODE == MOE_GG_WGRAD) {
         if (a.accumulate) {
-            gg_ws<MODE, EPI, 128, 256, 2, 4, 4, 3, true><<<grid, 12 * 64, 0, s>>>(a);
+            gg_ws<MODE, EPI, FP8, kWsBM, kWsBN, kWsWM, kWsWN, kWsNP, kWsStages, true>
+                <<<grid, threads, 0, s>>>(a);
             return;
         }
     }
-    gg_ws<MODE, EPI, 128, 256, 2, 4, 4, 3><<<grid, 12 * 64, 0, s>>>(a);
+    gg_ws<MODE, EPI, FP8, kWsBM, kWsBN, kWsWM, kWsWN, kWsNP, kWsStages><<<grid, threads, 0, s>>>(a);
 }
 
 template <int MODE, int EPI, bool FP8>
@@ -1707,8 +1678,8 @@ static void launch_mfma(const GemmArgs &a, hipStream_t s) {
     // bf16 on the split-role kernel, except the SwiGLU backward, whose
     // epilogue reads a, b through LDS-staged 16-byte rows (measured 2 % faster
     // than the split kernel's register-direct form)
-    if constexpr (!FP8 && EPI != MOE_EPI_SWIGLU_BWD) {
-        launch_ws<MODE, EPI>(a, s);
+    if constexpr (EPI != MOE_EPI_SWIGLU_BWD) {
+        launch_ws<MODE, EPI, FP8>(a, s);
         return;
     }
     if constexpr (MODE == MOE_GG_WGRAD) {
@@ -1755,6 +1726,170 @@ moe_status gemm_launch(const moe_gemm_desc *d, hipStream_t s) {
     }
 #undef GO
     return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// host walk of the copies (moe_gemm_copy_walk)
+
+namespace {
+
+struct Walker {
+    moe_copy_walk *w;
+    void read(int op, int64_t off, int64_t bytes) {
+        w->copies++;
+        if (off < w->lowest[op]) w->lowest[op] = off;
+        if (off + bytes > w->end[op]) w->end[op] = off + bytes;
+        if (w->first_bad < 0 && (off < 0 || off + bytes > w->extent[op])) {
+            w->first_bad = op;
+            w->bad_offset = off;
+            w->bad_bytes = bytes;
+        }
+    }
+    void zero(int64_t n) {
+        w->copies += n;
+        w->zero_copies += n;
+    }
+};
+
+// One operand of one tile: every wave, lane and instruction of the copy
+// over nk steps. A source is affine in the step with a non-negative stride,
+// so its lowest and highest addresses are at the first and at the last
+// step that copies real data; the steps in between are counted.
+template <typename Geom, typename OffFn>
+void walk_operand(Walker &wk, int op, int nwaves, int64_t origin, int64_t kstride, int nk,
+                  int klim, OffFn voff_of) {
+    for (int wave = 0; wave < nwaves; wave++)
+        for (int lane = 0; lane < 64; lane++)
+            for (int i = 0; i < Geom::IPW; i++) {
+                const int64_t base = origin + voff_of(i, wave, lane);
+                int last = -1, n_in = 0;
+                for (int kt = nk - 1; kt >= 0 && kt >= nk - 2; kt--)
+                    if (Geom::in_k(i, wave, lane, kt, klim)) { last = kt; break; }
+                // only the last step can be partial: steps before it copy real data
+                if (last >= 0) n_in = last + 1;
+                if (n_in > 0) {
+                    wk.read(op, base, 16);
+                    if (last > 0) wk.read(op, base + (int64_t)last * kstride, 16);
+                    wk.w->copies += n_in - (last > 0 ? 2 : 1);
+                }
+                wk.zero(nk - n_in);
+            }
+}
+
+template <int MODE, int EPI, bool FP8, int BM, int BN, int WM, int WN, int NCOPY>
+void walk_kernel(const GemmArgs &g, const int32_t *off, moe_copy_walk *w) {
+    using P = TilePlan<MODE, EPI, FP8, BM, BN, BN / WN>;
+    using AG = CopyGeom<BM, P::A_KL, NCOPY>;
+    using BG = CopyGeom<BN, P::B_KL, NCOPY>;
+    // MXFP8: SPW scale rows per lane of the NCOPY copying waves
+    constexpr int SPW = FP8 ? (BM + BN + NCOPY * 64 - 1) / (NCOPY * 64) : 0;
+    Walker wk{w};
+    const int E = g.E;
+    const int n_tiles = P::n_tiles(g);
+    const bool sbatch = P::scale_batched(g);
+    std::vector<int32_t> blk(E + 1, 0);
+    for (int e = 0; e < E; e++) blk[e + 1] = blk[e] + (off[e + 1] - off[e] + 127) / 128;
+    auto walk_tile = [&](const TileC &t) {
+        const int nk = P::nk_of(t.klim);
+        if (nk == 0) return;
+        if constexpr (P::A_KL) {
+            walk_operand<AG>(wk, 0, NCOPY, P::a_origin(g, t), AG::kstride(0), nk, t.klim,
+                             [&](int i, int wave, int lane) {
+                                 return (int64_t)AG::kl_off(i, wave, lane, [&](int r) { return P::a_row_off(g, t, r); });
+                             });
+        } else {
+            walk_operand<AG>(wk, 0, NCOPY, P::a_origin(g, t), AG::kstride(P::a_ld(g)), nk, t.klim,
+                             [&](int i, int wave, int lane) {
+                                 return (int64_t)AG::mn_off(i, wave, lane, P::a_ld(g), P::a_cvalid(g, t));
+                             });
+        }
+        const int bk = P::b_klim(t.klim);
+        if constexpr (P::B_KL) {
+            walk_operand<BG>(wk, 1, NCOPY, P::b_origin(g, t), BG::kstride(0), nk, bk,
+                             [&](int i, int wave, int lane) {
+                                 return (int64_t)BG::kl_off(i, wave, lane, [&](int n) { return P::b_row_off(g, t, n); });
+                             });
+        } else {
+            walk_operand<BG>(wk, 1, NCOPY, P::b_origin(g, t), BG::kstride(P::b_ld(g)), nk, bk,
+                             [&](int i, int wave, int lane) {
+                                 return (int64_t)BG::mn_off(i, wave, lane, P::b_ld(g), P::b_cvalid(g, t));
+                             });
+        }
+        if constexpr (FP8) {
+            for (int q = 0; q < SPW; q++)
+                for (int wave = 0; wave < NCOPY; wave++) {
+                    if (sbatch && (q * NCOPY + wave) * 64 >= BM + BN) continue;
+                    for (int lane = 0; lane < 64; lane++) {
+                        const int sr = (q * NCOPY + wave) * 64 + lane;
+                        const int64_t o = P::scale_off(g, t, sr);
+                        const int op = 2 + (P::scale_operand(sr) == 1 ? 1 : 0);
+                        const int n = sbatch ? (nk + 3) / 4 : nk;   // batched: steps 0, 4, 8, ...
+                        if (o < 0) { wk.zero(n); continue; }
+                        const int64_t step = sbatch ? 16 : 4;
+                        wk.read(op, o, step);
+                        if (n > 1) wk.read(op, o + (int64_t)(n - 1) * step, step);
+                        w->copies += n - (n > 1 ? 2 : 1);
+                    }
+                }
+        }
+    };
+    if constexpr (MODE == MOE_GG_WGRAD) {
+        const int mtiles = (g.M + BM - 1) / BM;
+        for (int e = 0; e < E; e++)
+            for (int mi = 0; mi < mtiles; mi++)
+                for (int nt = 0; nt < n_tiles; nt++) walk_tile(P::wgrad_tile(off, blk.data(), e, mi, nt));
+    } else {
+        for (int e = 0; e < E; e++) {
+            const int mt = (off[e + 1] - off[e] + BM - 1) / BM;
+            for (int m = 0; m < mt; m++)
+                for (int nt = 0; nt < n_tiles; nt++) walk_tile(P::row_tile(g, off, e, m, nt));
+        }
+    }
+}
+
+template <int MODE, int EPI>
+void walk_mode(const GemmArgs &a, const int32_t *off, bool fp8, moe_copy_walk *w) {
+    // the SwiGLU backward runs on gg_mfma (every wave copies), the rest on
+    // the split-role kernel (its producer waves copy)
+    if constexpr (EPI == MOE_EPI_SWIGLU_BWD) {
+        if (fp8)
+            walk_kernel<MODE, EPI, true, MOE_ROW_BM, MOE_ROW_BN, MOE_ROW_WM, MOE_ROW_WN,
+                        MOE_ROW_WM * MOE_ROW_WN>(a, off, w);
+        else
+            walk_kernel<MODE, EPI, false, MOE_ROW_BM, MOE_ROW_BN, MOE_ROW_WM, MOE_ROW_WN,
+                        MOE_ROW_WM * MOE_ROW_WN>(a, off, w);
+    } else {
+        if (fp8) walk_kernel<MODE, EPI, true, kWsBM, kWsBN, kWsWM, kWsWN, kWsNP>(a, off, w);
+        else walk_kernel<MODE, EPI, false, kWsBM, kWsBN, kWsWM, kWsWN, kWsNP>(a, off, w);
+    }
+}
+
+}  // namespace
+
+// the launch configuration of gemm_launch, walked on the host
+moe_status gemm_copy_walk(const moe_gemm_desc *d, const int32_t *off, moe_copy_walk *w) {
+    GemmArgs a{};
+    a.rows = d->rows; a.M = d->M; a.N = d->N; a.K = d->K;
+    a.E = d->n_groups;
+    a.h = d->epilogue == MOE_EPI_SWIGLU_FWD ? d->N / 2 : d->N;
+    w->copies = w->zero_copies = 0;
+    for (int i = 0; i < 4; i++) {
+        w->lowest[i] = INT64_MAX;
+        w->end[i] = 0;
+    }
+    w->first_bad = -1;
+    w->bad_offset = w->bad_bytes = 0;
+    const bool fp8 = d->dtype == MOE_MXFP8;
+    if (d->mode == MOE_GG_FWD) {
+        if (d->epilogue == MOE_EPI_SWIGLU_FWD) walk_mode<MOE_GG_FWD, MOE_EPI_SWIGLU_FWD>(a, off, fp8, w);
+        else walk_mode<MOE_GG_FWD, MOE_EPI_NONE>(a, off, fp8, w);
+    } else if (d->mode == MOE_GG_DGRAD) {
+        if (d->epilogue == MOE_EPI_SWIGLU_BWD) walk_mode<MOE_GG_DGRAD, MOE_EPI_SWIGLU_BWD>(a, off, fp8, w);
+        else walk_mode<MOE_GG_DGRAD, MOE_EPI_NONE>(a, off, fp8, w);
+    } else {
+        walk_mode<MOE_GG_WGRAD, MOE_EPI_NONE>(a, off, fp8, w);
+    }
+    return MOE_OK;
 }
 
 }  // namespace moe
