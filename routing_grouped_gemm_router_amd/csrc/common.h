@@ -43,6 +43,18 @@ MOE_DEV T wave_sum(T v) {
     return v;
 }
 
+// lane moves inside a quad of lanes (DPP, no LDS)
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+template <int CTRL>
+MOE_DEV int dpp_move(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+MOE_DEV float dpp_move(float v) {
+    return __int_as_float(dpp_move<CTRL>(__float_as_int(v)));
+}
+
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }

@@ -26,11 +26,14 @@
 //    same registers, so H' = silu(a) * b is formed from the fp32
 //    accumulators); SwiGLU backward (reads the stored a, b).
 //  * two kernels share the tiles, schedules, LDS layouts and MFMA order, so
-//    they give the same bits: gg_ws (bf16 FWD, DGRAD, WGRAD) splits the
-//    workgroup into consumer waves (fragment reads, MFMAs, epilogue) and
+//    they give the same bits: gg_ws (bf16 and MXFP8 FWD, DGRAD, WGRAD) splits
+//    the workgroup into consumer waves (fragment reads, MFMAs, epilogue) and
 //    producer waves (every global -> LDS copy), so the copies never wait on
 //    the epilogue's stores and the producers run ahead across tiles;
-//    gg_mfma (MXFP8, and the bf16 SwiGLU backward) has every wave do both.
+//    gg_mfma (the SwiGLU backward, bf16 and MXFP8, whose epilogue stages dH'
+//    in the stage buffers) has every wave do both.
+//  * copy sources come from copy_plan.h, which moe_gemm_copy_walk also runs on
+//    the host to bound every copy of a launch.
 #include <type_traits>
 #include <utility>
 #include <vector>
@@ -1609,8 +1612,9 @@ __global__ __launch_bounds__(256) void gg_f32(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // launch
 
-// Tile configurations: rows x columns of the output tile, the wave grid, LDS
-// stages and workgroups per CU of the persistent grid.
+// Tile configuration of gg_mfma (the SwiGLU backward): rows x columns of the
+// output tile, the wave grid, LDS stages and workgroups per CU of the
+// persistent grid.
 #ifndef MOE_ROW_BM
 #define MOE_ROW_BM 128      // FWD / DGRAD: routed rows per tile
 #endif
@@ -1626,33 +1630,12 @@ __global__ __launch_bounds__(256) void gg_f32(GemmArgs g) {
 #ifndef MOE_ROW_WPE
 #define MOE_ROW_WPE 2
 #endif
-#ifndef MOE_WG_BM
-#define MOE_WG_BM 128       // WGRAD: weight-gradient rows per tile
-#endif
-#ifndef MOE_WG_BN
-#define MOE_WG_BN 256
-#endif
-#ifndef MOE_WG_STAGES
-#define MOE_WG_STAGES 3
-#endif
-#ifndef MOE_WG_OCC
-#define MOE_WG_OCC 1
-#endif
-#ifndef MOE_WG_WPE
-#define MOE_WG_WPE 2
-#endif
 
 #ifndef MOE_ROW_WM
 #define MOE_ROW_WM 2
 #endif
 #ifndef MOE_ROW_WN
 #define MOE_ROW_WN 4
-#endif
-#ifndef MOE_WG_WM
-#define MOE_WG_WM 2
-#endif
-#ifndef MOE_WG_WN
-#define MOE_WG_WN 4
 #endif
 
 // bf16: 8 consumer waves (2 x 4, 64 x 64 each) and 4 producer waves on the
@@ -1675,21 +1658,11 @@ static void launch_ws(const GemmArgs &a, hipStream_t s) {
 
 template <int MODE, int EPI, bool FP8>
 static void launch_mfma(const GemmArgs &a, hipStream_t s) {
-    // bf16 on the split-role kernel, except the SwiGLU backward, whose
-    // epilogue reads a, b through LDS-staged 16-byte rows (measured 2 % faster
-    // than the split kernel's register-direct form)
+    // every role on the split-role kernel except the SwiGLU backward, whose
+    // epilogue stages dH' through the LDS stage buffers and reads a, b as
+    // 16-byte rows (measured 2 % faster than a register-direct form)
     if constexpr (EPI != MOE_EPI_SWIGLU_BWD) {
         launch_ws<MODE, EPI, FP8>(a, s);
-        return;
-    }
-    if constexpr (MODE == MOE_GG_WGRAD) {
-        const int grid = (num_cus() * MOE_WG_OCC + 7) / 8 * 8;
-        if (a.accumulate)
-            gg_mfma<MODE, EPI, FP8, MOE_WG_BM, MOE_WG_BN, MOE_WG_WM, MOE_WG_WN, MOE_WG_STAGES,
-                    MOE_WG_WPE, true><<<grid, MOE_WG_WM * MOE_WG_WN * 64, 0, s>>>(a);
-        else
-            gg_mfma<MODE, EPI, FP8, MOE_WG_BM, MOE_WG_BN, MOE_WG_WM, MOE_WG_WN, MOE_WG_STAGES,
-                    MOE_WG_WPE><<<grid, MOE_WG_WM * MOE_WG_WN * 64, 0, s>>>(a);
     } else {
         const int grid = (num_cus() * MOE_ROW_OCC + 7) / 8 * 8;
         gg_mfma<MODE, EPI, FP8, MOE_ROW_BM, MOE_ROW_BN, MOE_ROW_WM, MOE_ROW_WN, MOE_ROW_STAGES,

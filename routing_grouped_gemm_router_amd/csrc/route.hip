@@ -103,13 +103,7 @@ MOE_DEV void route_take1(float (&bv)[KP], int (&bi)[KP], float x, int e) {
 // quads, then the half-row mirror. Applied in this order, each pairs every
 // lane with one holding the other half of the lists merged so far, so after
 // the three rounds all 8 lanes of an aligned group hold the merge of all 8.
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141;
-template <int CTRL>
-MOE_DEV int dpp_move(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
 
 template <int KP, int CTRL>
 MOE_DEV void route_merge_lanes(float (&bv)[KP], int (&bi)[KP]) {
