@@ -31,7 +31,7 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 # the sources that make up the grouped GEMM kernel
-GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "../include/moe.h")
+GEMM_SOURCES = ("csrc/gemm.hip", "csrc/copy_plan.h", "csrc/common.h", "../include/moe.h")
 
 
 def gemm_source_hash() -> str:
