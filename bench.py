@@ -162,10 +162,14 @@ def make_layer(moe, w, inp):
     return moe.MoELayer(inp["w1"], inp["w2"], w.k)
 
 
-def run_layer(moe, torch, w, inp, steps, warmup, layer=None):
+def run_layer(moe, torch, w, inp, steps, warmup, layer=None, flush=None):
     """Warm-up, then `steps` timed steps (barrier + synchronize on both sides)
     with HIP events between the stages. Returns (layer, ms per step by the
-    wall clock, {stage: average ms})."""
+    wall clock, {stage: average ms}). With `flush` (a tensor of at least
+    1 GiB), every step is preceded by a write of the whole tensor, which
+    evicts the 256 MB last-level cache: the stages then start cold, as a
+    layer does between other layers' work (the wall-clock time then includes
+    the writes and is not a step time)."""
     mx = w.dtype == "mxfp8"
     layer = layer or make_layer(moe, w, inp)
     x, logits, dout = inp["x"], inp["logits"], inp["dout"]
@@ -215,12 +219,16 @@ def run_layer(moe, torch, w, inp, steps, warmup, layer=None):
         if w.backward:
             layer.backward(dout, stage_events=ev[len(fwd_names) + 1:] if ev is not None else None)
 
-    for _ in range(warmup):
+    for i in range(warmup):
+        if flush is not None:
+            flush.fill_(float(i))
         step(None)
     evs = StageEvents(torch, stream, steps, len(fwd_names) + len(bwd_names))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
+        if flush is not None:
+            flush.fill_(float(i))
         step(evs.ev[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -333,6 +341,13 @@ def main():
         rc["throughput_frac"] = ms / rc["ms_per_step"]
         res["recompute"] = rc
     if extras:
+        # every stage again, each step preceded by a 1 GiB write that evicts
+        # the last-level cache: what the row movers reach on cold data
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        _, _, st_cold = run_layer(moe, torch, w, inp, min(a.steps, 10), 2, layer=layer, flush=flush)
+        del flush
+        res["roles_flushed"] = role_table(w, st_cold)
+        res["sclk"] = sample_sclk(torch, lambda: run_layer(moe, torch, w, inp, 1, 0, layer=layer))
         res["load_balance"] = load_balance_report(moe, torch, inp, layer, w)
         if w.backward:
             res["grad_accumulation"] = grad_accumulation(moe, torch, layer, inp, w, a.steps, ms)
@@ -569,6 +584,61 @@ def padded_baseline(moe, torch, inp, w, steps, warmup, ms_dropless, capacity=Non
             "tokens_per_s": w.T * steps / el, "dropless_speedup": ms / ms_dropless}
 
 
+def sample_sclk(torch, run_step, seconds: float = 0.6):
+    """The GPU's graphics clock (MHz) sampled every 10 ms while the step runs
+    back to back, from amd-smi; the GPU with the most graphics activity
+    meanwhile is the one reported. None if amd-smi is not usable."""
+    try:
+        import threading
+        import amdsmi
+    except ImportError:
+        return None
+    try:
+        amdsmi.amdsmi_init()
+    except Exception:
+        return None
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        clk = {i: [] for i in range(len(handles))}
+        act = {i: [] for i in range(len(handles))}
+        stop = threading.Event()
+
+        def poll():
+            while not stop.is_set():
+                for i, hdl in enumerate(handles):
+                    try:
+                        clk[i].append(amdsmi.amdsmi_get_clock_info(hdl, amdsmi.AmdSmiClkType.GFX)["clk"])
+                        act[i].append(amdsmi.amdsmi_get_gpu_activity(hdl)["gfx_activity"])
+                    except Exception:
+                        pass
+                time.sleep(0.01)
+
+        th = threading.Thread(target=poll, daemon=True)
+        th.start()
+        t0 = time.time()
+        while time.time() - t0 < seconds:
+            run_step()
+            torch.cuda.synchronize()
+        stop.set()
+        th.join(timeout=5)
+        busy = [i for i in clk if clk[i] and act[i]]
+        if not busy:
+            return None
+        i = max(busy, key=lambda j: sum(act[j]) / len(act[j]))
+        c = sorted(v for v in clk[i] if isinstance(v, (int, float)))
+        if not c:
+            return None
+        return {"median_mhz": c[len(c) // 2], "min_mhz": c[0], "max_mhz": c[-1], "samples": len(c),
+                "spec_mhz": 2400}
+    except Exception:
+        return None
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -602,7 +672,36 @@ def cpu_baseline(inp, w, n_tok):
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"first {n_tok} of {w.T} tokens of {w.name} (all {w.E} experts), "
                       f"{'fwd+bwd' if w.backward else 'fwd'}, fp64 oracle, {dt:.1f} s",
-            "cpu_model": cpu_model(), "stage_s": stages}
+            "cpu_model": cpu_model(), "stage_s": stages, "single_thread": cpu_single_thread()}
+
+
+def cpu_single_thread() -> dict:
+    """The oracle on one host thread: the whole tiny_fp32 workload (fwd+bwd)
+    and the first 32 tokens of e8_bf16_fwd (its forward), in tokens/s."""
+    import oracle
+    import synth
+
+    n0 = oracle.threads()
+    out = {}
+    try:
+        oracle.set_threads(1)
+        for name, n_tok in (("tiny_fp32", None), ("e8_bf16_fwd", 32)):
+            w = synth.WORKLOADS[name]
+            h = synth.host_inputs(w, seed=0, with_dout=w.backward)
+            n = w.T if n_tok is None else n_tok
+            sub = dict(logits=h["logits"][:n], x=h["x"][:n], w1=h["w1"], w2=h["w2"],
+                       dout=h["dout"][:n] if w.backward else None)
+            dt = "f32" if w.dtype == "f32" else "bf16"
+            t0 = time.perf_counter()
+            f = oracle.layer_forward(sub, w.k, dt)
+            if w.backward:
+                oracle.layer_backward(sub, f, w.k, dt)
+            el = time.perf_counter() - t0
+            out[name] = {"tokens": n, "pass": "fwd+bwd" if w.backward else "fwd",
+                         "seconds": el, "tokens_per_s": n / el}
+    finally:
+        oracle.set_threads(n0)
+    return out
 
 
 if __name__ == "__main__":

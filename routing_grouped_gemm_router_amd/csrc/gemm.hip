@@ -90,9 +90,9 @@ MOE_DEV float silu_f(float a) { return a / (1.f + __expf(-a)); }
 // MI355X has 8 XCDs with a private L2 each, and consecutive workgroup ids go
 // to consecutive XCDs. The persistent grid (a multiple of 8 workgroups) is
 // therefore split per XCD: workgroup b serves XCD x = b % 8 as its (b / 8)-th
-// worker. Each expert's m-tiles are cut into chunks of at most CHM m-tiles
-// (an expert of up to kChunkM m-tiles is one chunk); chunk c belongs to XCD
-// c % 8, and an XCD walks its chunks' tiles in order with the m-tile fastest.
+// worker. Each expert's m-tiles are cut into chunks of about kChunkM m-tiles
+// (below); chunk c belongs to XCD c % 8, and an XCD walks its chunks' tiles in
+// order with the m-tile fastest.
 // The ~32 CUs of an XCD thus work on all m-tiles of one chunk and a few of its
 // weight panels at a time: each weight panel is fetched into that XCD's L2
 // once and shared by all of the chunk's m-tiles, and the chunk's activation
@@ -109,9 +109,14 @@ MOE_DEV float silu_f(float a) { return a / (1.f + __expf(-a)); }
 constexpr int kMaxChunks = 1920;      // chunk list: kMaxChunks/8 entries per XCD (+1)
 constexpr int kXcdChunks = kMaxChunks / 8;
 #ifndef MOE_CHUNK_M
-#define MOE_CHUNK_M 16
+#define MOE_CHUNK_M 8
 #endif
-constexpr int kChunkM = MOE_CHUNK_M;   // m-tiles per chunk (an expert of up to this many stays on one XCD)
+// m-tiles per chunk: an expert of fewer than twice this many stays on one XCD.
+// Measured (bf16 GEMM1, GEMM2, GEMM1 dgrad): E = 8 with 32 m-tiles per expert
+// 20 % faster with chunks of 8 than of 16; Zipf routing 7-8 % faster; E = 128
+// (4-9 m-tiles per expert: one chunk either way) unchanged; chunks of 4 lose
+// 10 % at E = 128 bf16 and MXFP8, where they split experts.
+constexpr int kChunkM = MOE_CHUNK_M;
 #ifndef MOE_WG_GROUP_M
 #define MOE_WG_GROUP_M 8
 #endif
@@ -126,6 +131,16 @@ struct RowSchedule {
 // s_tile: exclusive prefix of m-tiles per group (from build_tile_table).
 // Builds s_chunk (chunk prefix per group, E+1) and s_xpre (tile prefix over
 // this XCD's chunks, up to kMaxChunks/8 + 1 entries). blockDim.x >= 256.
+// A group of mt_e m-tiles is cut into max(1, mt_e / chm) chunks of chm
+// m-tiles, the last one taking the remainder (chm to 2 chm - 1 m-tiles): a
+// chunk of a few m-tiles would cost its XCD a read of the whole weight
+// matrix for little work.
+MOE_DEV int chunk_count(int mt_e, int chm) { return mt_e > 0 ? max(1, mt_e / chm) : 0; }
+// m-tiles of chunk ci of a group of mt_e m-tiles
+MOE_DEV int chunk_mtiles(int mt_e, int chm, int ci) {
+    return ci == chunk_count(mt_e, chm) - 1 ? mt_e - ci * chm : chm;
+}
+
 MOE_DEV RowSchedule build_row_schedule(const int32_t *s_tile, int E, int n_tiles, int xcd,
                                        int32_t *s_chunk, int32_t *s_xpre) {
     const int tid = threadIdx.x;
@@ -133,7 +148,7 @@ MOE_DEV RowSchedule build_row_schedule(const int32_t *s_tile, int E, int n_tiles
     // chunk size: at least kChunkM m-tiles, more when needed to stay within kMaxChunks
     const int chm = max(kChunkM, (mt_total + (kMaxChunks - 256) - 1) / (kMaxChunks - 256));
     int32_t nc = 0;
-    if (tid < E) nc = (s_tile[tid + 1] - s_tile[tid] + chm - 1) / chm;
+    if (tid < E) nc = chunk_count(s_tile[tid + 1] - s_tile[tid], chm);
     if (tid < 256) s_chunk[tid + 1] = nc;
     if (tid == 0) s_chunk[0] = 0;
     __syncthreads();
@@ -151,7 +166,7 @@ MOE_DEV RowSchedule build_row_schedule(const int32_t *s_tile, int E, int n_tiles
         const int e = find_group(s_chunk, E, c);
         const int ci = c - s_chunk[e];
         const int mt_e = s_tile[e + 1] - s_tile[e];
-        t = min(chm, mt_e - ci * chm) * n_tiles;
+        t = chunk_mtiles(mt_e, chm, ci) * n_tiles;
     }
     // (C <= kMaxChunks by the choice of chm, so cx <= kXcdChunks)
     if (tid < kXcdChunks) s_xpre[tid + 1] = t;
@@ -188,7 +203,7 @@ MOE_DEV void decode_row_tile(const RowSchedule &rs, const int32_t *s_tile, const
     // of the chunk's m-tiles and a few weight panels, so each weight panel
     // is fetched into the XCD's L2 once and shared by the chunk's m-tiles
     const int ci = c - s_chunk[e];
-    const int cm = min(rs.chm, s_tile[e + 1] - s_tile[e] - ci * rs.chm);
+    const int cm = chunk_mtiles(s_tile[e + 1] - s_tile[e], rs.chm, ci);
     mt_e = ci * rs.chm + o % cm;
     nt = o / cm;
 }
