@@ -46,6 +46,9 @@ MOE_DEV T wave_sum(T v) {
 // lane moves inside a quad of lanes (DPP, no LDS)
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7 - i within each 8 lanes
+constexpr int kDppRowShl4 = 0x104;    // lane i <- lane i + 4 within each 16 lanes (others keep 0)
+constexpr int kDppRowShl8 = 0x108;    // lane i <- lane i + 8 within each 16 lanes (others keep 0)
 template <int CTRL>
 MOE_DEV int dpp_move(int v) {
     return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void mx_quant_rows(const void *__restrict__ in
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(f[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, dpp_move<kDppXor1>(amax));
     const uint32_t sb = mx_scale_byte(amax);
     if (!ok) return;
     const int sh = 127 - (int)sb;
@@ -264,9 +264,10 @@ __global__ __launch_bounds__(256) void mx_quant_cols_f32(const float *__restrict
                 // from 0, so that NaN elements never enter the block maximum
                 float am = fmaxf(fmaxf(fmaxf(0.f, fabsf(v[p].x)), fabsf(v[p].y)),
                                  fmaxf(fabsf(v[p].z), fabsf(v[p].w)));
-                am = fmaxf(am, __shfl_xor(am, 1, 64));
-                am = fmaxf(am, __shfl_xor(am, 2, 64));
-                am = fmaxf(am, __shfl_xor(am, 4, 64));
+                // max over the 8 lanes of the block (lane moves, no LDS)
+                am = fmaxf(am, dpp_move<kDppXor1>(am));
+                am = fmaxf(am, dpp_move<kDppXor2>(am));
+                am = fmaxf(am, dpp_move<kDppHalfMirror>(am));
                 if (r < u.n && cok) {
                     const uint32_t sb = mx_scale_byte(am);
                     const int sh = 127 - (int)sb;
@@ -378,7 +379,6 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
             }
         }
         if constexpr (BOTH) {             // 32-column block = 4 neighbouring lanes of one row
-            const int rl = lane & ~15;    // the row's first lane in the wave
 #pragma unroll
             for (int p = 0; p < 8; p++) {
                 const int r = 2 * qr + (p & 1) + 32 * (p >> 1);
@@ -389,16 +389,20 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
                 float am = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; e++) am = fmaxf(am, fabsf(f[e]));
-                am = fmaxf(am, __shfl_xor(am, 1, 64));
-                am = fmaxf(am, __shfl_xor(am, 2, 64));
+                // max over the block's 4 lanes (lane moves, no LDS)
+                am = fmaxf(am, dpp_move<kDppXor1>(am));
+                am = fmaxf(am, dpp_move<kDppXor2>(am));
                 const uint32_t sb = mx_scale_byte(am);
                 const int sh = 127 - (int)sb;
                 const uint32_t lo4 = e4m3x4(f[0], f[1], f[2], f[3], sh);
                 const uint32_t hi4 = e4m3x4(f[4], f[5], f[6], f[7], sh);
                 // the odd lane's 8 bytes go out with the even lane's store
-                const uint32_t plo = __shfl_xor(lo4, 1, 64), phi = __shfl_xor(hi4, 1, 64);
-                const uint32_t s4 = __shfl(sb, rl, 64) | (__shfl(sb, rl + 4, 64) << 8) |
-                                    (__shfl(sb, rl + 8, 64) << 16) | (__shfl(sb, rl + 12, 64) << 24);
+                const uint32_t plo = (uint32_t)dpp_move<kDppXor1>((int)lo4);
+                const uint32_t phi = (uint32_t)dpp_move<kDppXor1>((int)hi4);
+                // the row's four scale bytes (lanes rl, rl + 4, rl + 8, rl + 12)
+                // as one word in lane rl
+                const uint32_t s2 = sb | ((uint32_t)dpp_move<kDppRowShl4>((int)sb) << 8);
+                const uint32_t s4 = s2 | ((uint32_t)dpp_move<kDppRowShl8>((int)s2) << 16);
                 if (r < u.n && cok) {
                     uint8_t *qrow = q1 + (u.r0 + r) * cols + c0;
                     if ((ch & 1) == 0)

@@ -103,7 +103,6 @@ MOE_DEV void route_take1(float (&bv)[KP], int (&bi)[KP], float x, int e) {
 // quads, then the half-row mirror. Applied in this order, each pairs every
 // lane with one holding the other half of the lists merged so far, so after
 // the three rounds all 8 lanes of an aligned group hold the merge of all 8.
-constexpr int kDppHalfMirror = 0x141;
 
 template <int KP, int CTRL>
 MOE_DEV void route_merge_lanes(float (&bv)[KP], int (&bi)[KP]) {
