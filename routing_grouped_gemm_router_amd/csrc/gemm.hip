@@ -131,14 +131,20 @@ struct RowSchedule {
 // s_tile: exclusive prefix of m-tiles per group (from build_tile_table).
 // Builds s_chunk (chunk prefix per group, E+1) and s_xpre (tile prefix over
 // this XCD's chunks, up to kMaxChunks/8 + 1 entries). blockDim.x >= 256.
-// A group of mt_e m-tiles is cut into max(1, mt_e / chm) chunks of chm
-// m-tiles, the last one taking the remainder (chm to 2 chm - 1 m-tiles): a
-// chunk of a few m-tiles would cost its XCD a read of the whole weight
-// matrix for little work.
-MOE_DEV int chunk_count(int mt_e, int chm) { return mt_e > 0 ? max(1, mt_e / chm) : 0; }
-// m-tiles of chunk ci of a group of mt_e m-tiles
+// A group of mt_e m-tiles is cut into max(1, round(mt_e / chm)) chunks of
+// equal size up to one m-tile (the first mt_e % n chunks one larger): no
+// chunk is a sliver that would cost its XCD a whole weight-matrix read for
+// little work, and the chunks dealt to the XCDs are alike, so the XCDs'
+// totals are too.
+MOE_DEV int chunk_count(int mt_e, int chm) { return mt_e > 0 ? max(1, (mt_e + chm / 2) / chm) : 0; }
+// m-tiles of chunk ci of a group of mt_e m-tiles, and its first m-tile
 MOE_DEV int chunk_mtiles(int mt_e, int chm, int ci) {
-    return ci == chunk_count(mt_e, chm) - 1 ? mt_e - ci * chm : chm;
+    const int n = chunk_count(mt_e, chm);
+    return mt_e / n + (ci < mt_e % n ? 1 : 0);
+}
+MOE_DEV int chunk_first(int mt_e, int chm, int ci) {
+    const int n = chunk_count(mt_e, chm);
+    return ci * (mt_e / n) + min(ci, mt_e % n);
 }
 
 MOE_DEV RowSchedule build_row_schedule(const int32_t *s_tile, int E, int n_tiles, int xcd,
@@ -204,7 +210,7 @@ MOE_DEV void decode_row_tile(const RowSchedule &rs, const int32_t *s_tile, const
     // is fetched into the XCD's L2 once and shared by the chunk's m-tiles
     const int ci = c - s_chunk[e];
     const int cm = chunk_mtiles(s_tile[e + 1] - s_tile[e], rs.chm, ci);
-    mt_e = ci * rs.chm + o % cm;
+    mt_e = chunk_first(s_tile[e + 1] - s_tile[e], rs.chm, ci) + o % cm;
     nt = o / cm;
 }
 
