@@ -82,7 +82,11 @@ MOE_DEV int find_group(const int32_t *s_tile, int E, int mt) {
     return lo;
 }
 
-MOE_DEV float silu_f(float a) { return a / (1.f + __expf(-a)); }
+// silu(a) = a * sigmoid(a), the sigmoid by the hardware reciprocal (1 ulp)
+// instead of a correctly rounded divide: the SwiGLU epilogues' VALU work is
+// exposed between tiles (GEMM2 dgrad + SwiGLU backward 6 % faster; the
+// results differ from the divided form in a few bf16 roundings)
+MOE_DEV float silu_f(float a) { return a * __builtin_amdgcn_rcpf(1.f + __expf(-a)); }
 
 // ---------------------------------------------------------------------------
 // XCD-aware tile schedule
@@ -1033,7 +1037,7 @@ void gg_mfma(GemmArgs g) {
                                 for (int hh = 0; hh < 2; hh++) {
                                     const float a = hh ? hi_bf16(wa[w]) : lo_bf16(wa[w]);
                                     const float b = hh ? hi_bf16(wb[w]) : lo_bf16(wb[w]);
-                                    const float sg = 1.f / (1.f + __expf(-a));
+                                    const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-a));
                                     const float d = dh[2 * w + hh];
                                     da2[hh] = d * b * sg * (1.f + a * (1.f - sg));
                                     db2[hh] = d * a * sg;
