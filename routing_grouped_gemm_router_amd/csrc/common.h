@@ -21,16 +21,14 @@ constexpr int kWave = 64;
 // bfloat16 <-> fp32 on raw 16-bit patterns.
 MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
-MOE_DEV uint16_t f32_to_bf16(float f) {
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;   // nearest, ties to even
-    const uint32_t q = (u >> 16) | 0x40u;                          // NaN stays a quiet NaN
-    return (uint16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? q : r);  // a select, no branch
-}
+// fp32 -> bf16, round to nearest even (IEEE conversion; CDNA4 does it in one
+// instruction, v_cvt_pk_bf16_f32, two values at a time); NaN stays a NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+MOE_DEV uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 MOE_DEV float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
