@@ -243,8 +243,8 @@ def dominant_roofline(w, roles: dict, traffic) -> dict:
     flops, nbytes = role_work(w)[name]
     mx = w.dtype == "mxfp8"
     mode = "WGRAD" if "wgrad" in name else ("DGRAD" if "dgrad" in name else "FWD")
-    # bf16 roles run on the split-role kernel, except the SwiGLU backward
-    kname = "gg_mfma" if mx or name == "gemm2_dgrad_swiglu" else "gg_ws"
+    # every role runs on the split-role kernel except the SwiGLU backward
+    kname = "gg_mfma" if name == "gemm2_dgrad_swiglu" else "gg_ws"
     kern = f"{kname}<{mode}, {'MXFP8' if mx else 'bf16'}> ({name})"
     out = {"kernel": kern, "bound": r["bound"], "traffic": traffic,
            "avg_launch_ms": r["us"] * 1e-3, "flops_per_launch": flops, "bytes_per_launch": nbytes}
@@ -607,10 +607,12 @@ def sample_sclk(torch, run_step, seconds: float = 0.6):
             while not stop.is_set():
                 for i, hdl in enumerate(handles):
                     try:
-                        clk[i].append(amdsmi.amdsmi_get_clock_info(hdl, amdsmi.AmdSmiClkType.GFX)["clk"])
-                        act[i].append(amdsmi.amdsmi_get_gpu_activity(hdl)["gfx_activity"])
+                        c = amdsmi.amdsmi_get_clock_info(hdl, amdsmi.AmdSmiClkType.GFX)["clk"]
+                        a = amdsmi.amdsmi_get_gpu_activity(hdl)["gfx_activity"]
                     except Exception:
-                        pass
+                        continue
+                    clk[i].append(c)
+                    act[i].append(a)
                 time.sleep(0.01)
 
         th = threading.Thread(target=poll, daemon=True)
@@ -625,11 +627,15 @@ def sample_sclk(torch, run_step, seconds: float = 0.6):
         if not busy:
             return None
         i = max(busy, key=lambda j: sum(act[j]) / len(act[j]))
-        c = sorted(v for v in clk[i] if isinstance(v, (int, float)))
+        # the samples taken while the graphics engine was busy (activity of
+        # at least half), so that gaps between steps do not count
+        pairs = [(c, a) for c, a in zip(clk[i], act[i])
+                 if isinstance(c, (int, float)) and isinstance(a, (int, float))]
+        c = sorted(c for c, a in pairs if a >= 50)
         if not c:
             return None
         return {"median_mhz": c[len(c) // 2], "min_mhz": c[0], "max_mhz": c[-1], "samples": len(c),
-                "spec_mhz": 2400}
+                "all_samples": len(pairs), "spec_mhz": 2400}
     except Exception:
         return None
     finally:
