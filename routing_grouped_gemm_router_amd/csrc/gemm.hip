@@ -346,6 +346,23 @@ MOE_DEV void store16(void *p, uint4 v) {
     }
 }
 
+// A condition that holds for the whole wave or for none of its lanes, taken
+// from lane 0 so that the branch on it is a scalar one.
+MOE_DEV bool wave_full(bool c) { return __builtin_amdgcn_readfirstlane((int)c) != 0; }
+
+// Byte address of element (row, col) of a row-major matrix with ld elements
+// per row, for wave-uniform row and col (kept in scalar registers), and the
+// byte offset of lane l's first accumulator element from there: row
+// (l / 32) * 4, column l % 32 of the MFMA output layout.
+template <typename T>
+MOE_DEV char *wave_base(T *p, int row, int col, int ld) {
+    row = __builtin_amdgcn_readfirstlane(row);
+    col = __builtin_amdgcn_readfirstlane(col);
+    return reinterpret_cast<char *>(p + ((int64_t)row * ld + col));
+}
+template <int ES>
+MOE_DEV uint32_t lane_off(int lane, int ld) { return (uint32_t)(((lane >> 5) * 4 * ld + (lane & 31)) * ES); }
+
 // Wait until at most N vector-memory instructions of this wave are in flight
 // (they complete in issue order).
 template <int N>
@@ -1313,6 +1330,11 @@ void gg_ws(GemmArgs g) {
     auto epilogue = [&](const TileC &t) {
         if constexpr (MODE == MOE_GG_WGRAD) {
             float *C = reinterpret_cast<float *>(g.C) + (int64_t)t.e * g.M * g.N;
+            // the wave's 64x64 part lies inside C: stores without per-element
+            // checks, from one per-lane base (row (lane/32)*4, column lane%32)
+            const bool full = wave_full(t.m0 + wm * WTM + WTM <= g.M && t.n0 + wn * WTN + WTN <= g.N);
+            const char *Cw = wave_base(C, t.m0 + wm * WTM, t.n0 + wn * WTN, g.N);
+            const uint32_t lo = lane_off<4>(lane, g.N);
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
@@ -1333,6 +1355,12 @@ void gg_ws(GemmArgs g) {
                             const int m = t.m0 + row_in(i, v);
                             if (m < g.M && n < g.N) store_f32(C + (int64_t)m * g.N + n, old[v] + acc[i][j][v]);
                         }
+                    } else if (full) {
+#pragma unroll
+                        for (int v = 0; v < 16; v++)
+                            store_f32(reinterpret_cast<float *>(
+                                          (char *)Cw + ((int64_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * g.N + j * 32) * 4 + lo),
+                                      acc[i][j][v]);
                     } else {
 #pragma unroll
                         for (int v = 0; v < 16; v++) {
@@ -1345,11 +1373,33 @@ void gg_ws(GemmArgs g) {
             uint16_t *AB = reinterpret_cast<uint16_t *>(g.C);
             uint16_t *HP = reinterpret_cast<uint16_t *>(g.aux_out);
             const int h = g.h;
+            const int r0 = t.row0 + wm * WTM, j0 = t.nt * (BN / 2) + wn * (WTN / 2);
+            if (wave_full(r0 + WTM <= t.row_end && j0 + WTN / 2 <= h)) {
+                // the wave's rows and hidden units are all in range
+                char *abw = wave_base(AB, r0, j0, 2 * h);
+                char *hpw = wave_base(HP, r0, j0, h);
+                const uint32_t lab = lane_off<2>(lane, 2 * h), lhp = lane_off<2>(lane, h);
+#pragma unroll
+                for (int i = 0; i < TM; i++)
+#pragma unroll
+                    for (int j = 0; j < TN / 2; j++)
+#pragma unroll
+                        for (int v = 0; v < 16; v++) {
+                            const int64_t ro = i * 32 + (v >> 2) * 8 + (v & 3);
+                            const float a = acc[i][j][v], b = acc[i][j + TN / 2][v];
+                            char *abr = abw + (ro * 2 * h + j * 32) * 2;
+                            *reinterpret_cast<uint16_t *>(abr + lab) = f32_to_bf16(a);
+                            *reinterpret_cast<uint16_t *>(abr + (int64_t)h * 2 + lab) = f32_to_bf16(b);
+                            *reinterpret_cast<uint16_t *>(hpw + (ro * h + j * 32) * 2 + lhp) =
+                                f32_to_bf16(silu_f(a) * b);
+                        }
+                return;
+            }
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
                 for (int j = 0; j < TN / 2; j++) {
-                    const int jj = t.nt * (BN / 2) + wn * (WTN / 2) + j * 32 + col_l;
+                    const int jj = j0 + j * 32 + col_l;
 #pragma unroll
                     for (int v = 0; v < 16; v++) {
                         const int grow = t.row0 + row_in(i, v);
@@ -1364,11 +1414,26 @@ void gg_ws(GemmArgs g) {
                 }
         } else {
             uint16_t *C = reinterpret_cast<uint16_t *>(g.C);
+            const int r0 = t.row0 + wm * WTM, n0 = t.n0 + wn * WTN;
+            if (wave_full(r0 + WTM <= t.row_end && n0 + WTN <= g.N)) {
+                char *cw = wave_base(C, r0, n0, g.N);
+                const uint32_t lo = lane_off<2>(lane, g.N);
+#pragma unroll
+                for (int i = 0; i < TM; i++)
+#pragma unroll
+                    for (int j = 0; j < TN; j++)
+#pragma unroll
+                        for (int v = 0; v < 16; v++)
+                            *reinterpret_cast<uint16_t *>(
+                                cw + ((int64_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * g.N + j * 32) * 2 + lo) =
+                                f32_to_bf16(acc[i][j][v]);
+                return;
+            }
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
                 for (int j = 0; j < TN; j++) {
-                    const int n = t.n0 + wn * WTN + j * 32 + col_l;
+                    const int n = n0 + j * 32 + col_l;
 #pragma unroll
                     for (int v = 0; v < 16; v++) {
                         const int grow = t.row0 + row_in(i, v);
