@@ -151,6 +151,7 @@ def sq(d: str, title: str, cmd: str, select=None) -> str:
     for k, lst in groups.items():
         out.append(f"| `{k}` | {len(lst)} | " +
                    " | ".join(f"{sum(x.get(c, 0) for x in lst) / len(lst):.4g}" for c in cols) + " |")
+    out += ["", f"gemm_source_hash = {gemm_source_hash()}"]
     return "\n".join(out) + "\n"
 
 
