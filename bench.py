@@ -129,6 +129,9 @@ def role_table(w, times_ms: dict) -> dict:
             r["frac_hbm"] = r["gbps"] / PEAK_HBM_GBS
         r["bound"] = "mfma" if t_mfma >= t_hbm else "hbm"
         r["frac_roof"] = max(t_mfma, t_hbm) / t
+        sp = getattr(times_ms, "spread", {}).get(name)
+        if sp is not None:
+            r["us_median"], r["us_min"] = sp[0] * 1e3, sp[1] * 1e3
         out[name] = r
     return out
 
@@ -150,10 +153,28 @@ class StageEvents:
         torch.cuda.synchronize()
 
     def stage_ms(self, names):
-        """Average ms of stage j over the steps: event j+1 minus event j."""
+        """Average ms of stage j over the steps (event j+1 minus event j), as
+        a StageTimes carrying each stage's median and minimum too, and the
+        median and minimum of the whole step (first event to last)."""
         n = len(self.ev)
-        return {nm: sum(r[j].elapsed_time(r[j + 1]) for r in self.ev) / n
-                for j, nm in enumerate(names)}
+        out = StageTimes()
+        for j, nm in enumerate(names):
+            t = sorted(r[j].elapsed_time(r[j + 1]) for r in self.ev)
+            out[nm] = sum(t) / n
+            out.spread[nm] = (t[n // 2], t[0])
+        span = sorted(r[0].elapsed_time(r[len(names)]) for r in self.ev)
+        out.step = (span[n // 2], span[0])
+        return out
+
+
+class StageTimes(dict):
+    """{stage: average ms}, with .spread = {stage: (median ms, min ms)} and
+    .step = (median ms, min ms) of the step from its first to last event."""
+
+    def __init__(self):
+        super().__init__()
+        self.spread = {}
+        self.step = None
 
 
 def make_layer(moe, w, inp):
@@ -317,6 +338,8 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": ms,
+        "step_ms_median": stages.step[0] if getattr(stages, "step", None) else None,
+        "step_ms_min": stages.step[1] if getattr(stages, "step", None) else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

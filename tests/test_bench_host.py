@@ -106,3 +106,14 @@ def test_committed_counter_summaries_name_their_sources():
     for f in pmc:
         r = rps.read_traffic(os.path.join(prof, f))
         assert r is not None and len(r[1]) == 16, f
+
+
+def test_role_table_carries_median_and_min():
+    w = synth.WORKLOADS["e128_bf16"]
+    st = bench.StageTimes()
+    st["gemm2"] = 0.350
+    st.spread["gemm2"] = (0.348, 0.341)
+    r = bench.role_table(w, st)["gemm2"]
+    assert r["us"] == pytest.approx(350.0)
+    assert r["us_median"] == pytest.approx(348.0) and r["us_min"] == pytest.approx(341.0)
+    assert "us_median" not in bench.role_table(w, {"gemm2": 0.350})["gemm2"]
