@@ -24,7 +24,9 @@
 //  * epilogues: plain store; SwiGLU forward (the weight panel is laid out so
 //    each wave holds the gate and up columns of the same hidden unit in the
 //    same registers, so H' = silu(a) * b is formed from the fp32
-//    accumulators); SwiGLU backward (reads the stored a, b).
+//    accumulators); SwiGLU backward (reads the stored a, b). A wave tile
+//    that lies wholly inside the output is stored without per-element
+//    checks, from a scalar base and one 32-bit offset per lane.
 //  * two kernels share the tiles, schedules, LDS layouts and MFMA order, so
 //    they give the same bits: gg_ws (bf16 and MXFP8 FWD, DGRAD, WGRAD) splits
 //    the workgroup into consumer waves (fragment reads, MFMAs, epilogue) and
@@ -1748,8 +1750,8 @@ __global__ __launch_bounds__(256) void gg_f32(GemmArgs g) {
 #define MOE_ROW_WN 4
 #endif
 
-// bf16: 8 consumer waves (2 x 4, 64 x 64 each) and 4 producer waves on the
-// same 128 x 256 tiles and 3 stages as gg_mfma
+// gg_ws, bf16 and MXFP8: 8 consumer waves (2 x 4, 64 x 64 each) and 4
+// producer waves on the same 128 x 256 tiles and 3 stages as gg_mfma
 constexpr int kWsBM = 128, kWsBN = 256, kWsWM = 2, kWsWN = 4, kWsNP = 4, kWsStages = 3;
 
 template <int MODE, int EPI, bool FP8>
