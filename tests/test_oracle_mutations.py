@@ -38,6 +38,14 @@ MUTATIONS = {
                               "for (int j = 0; j < c->nn; j++) out[j] = out[j] * (1.0 + 1e-3);"),
     "unpermute_drops_last_slot": ("for (int j = 0; j < k; j++) s += dx_perm[",
                                   "for (int j = 0; j < k - 1; j++) s += dx_perm["),
+    "mx_rows_amax_skips_first": ("for (int i = 0; i < 32; i++) if (fabs((double)v[i]) > amax)",
+                                 "for (int i = 1; i < 32; i++) if (fabs((double)v[i]) > amax)"),
+    "mx_cols_amax_drops_last": ("for (int64_t i = i0; i < i1; i++) {\n            double v = fabs(",
+                                "for (int64_t i = i0; i < i1 - 1; i++) {\n            double v = fabs("),
+    "mx_cols_padding_nonzero": ("                : 0;\n", "                : 1;\n"),
+    "mx_groups_padded_to_64": (
+        "nb = 4 * ((len + 127) / 128);\n        struct mxq_cols_ctx",
+        "nb = 2 * ((len + 63) / 64);\n        struct mxq_cols_ctx"),
 }
 
 
@@ -100,9 +108,40 @@ def pins_pass(lib) -> bool:
         ref8 = torch.from_numpy(vals.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         if not np.array_equal(ours, ref8):
             return False
-        return True
+        return _mx_layouts_pass(lib)
     except (AssertionError, ValueError, IndexError):
         return False
+
+
+def _mx_layouts_pass(lib) -> bool:
+    """MXFP8 quantisation in both layouts against the torch-cast round trip,
+    with row groups (one empty, a short last block) for the column layout,
+    whose padding past a group's rows must hold zero bytes and zero scales."""
+    rng = np.random.default_rng(4)
+    # magnitudes drawn per element, and an outlier on the diagonal, so that
+    # every position of a row block and of a column block is its maximum in
+    # some block
+    a = rng.standard_normal((70, 64)) * np.exp(rng.uniform(-6, 6, (70, 64)))
+    for i in range(64):
+        a[i, i] = 1e4 * (1.0 + rng.uniform())
+    a = a.astype(np.float32)
+    if not np.array_equal(oracle.mx_rows(a, lib=lib), brute.mx_rows_torch(a)):
+        return False
+    go = np.array([0, 45, 45, 70], np.int32)
+    q, sc = oracle.mxfp8_quantize(a, 0, go, lib=lib)
+    vals = oracle.mxfp8_dequantize(q, sc, a.shape[0], a.shape[1], 0, go)
+    bb = 0
+    for g in range(len(go) - 1):
+        r0, r1 = int(go[g]), int(go[g + 1])
+        nb = 4 * -(-(r1 - r0) // 128)
+        if r1 > r0 and not np.array_equal(vals[r0:r1], brute.mx_cols_torch(a[r0:r1])):
+            return False
+        qg = q[bb * 32 * a.shape[1]:(bb + nb) * 32 * a.shape[1]].reshape(a.shape[1], nb * 32)
+        sg = sc[bb * a.shape[1]:(bb + nb) * a.shape[1]].reshape(a.shape[1], nb)
+        if np.any(qg[:, r1 - r0:] != 0) or np.any(sg[:, -(-(r1 - r0) // 32):] != 0):
+            return False
+        bb += nb
+    return q.size == bb * 32 * a.shape[1]
 
 
 def test_unmutated_oracle_passes_the_compact_pins():
