@@ -80,3 +80,52 @@ def test_gerrymandering_is_visible():
 def test_zero_tokens():
     st, g = oracle.load_balance(np.zeros((0, 4)), np.zeros(4), 2, 1.0)
     assert np.all(st == 0) and g.shape == (0, 4)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes in a private copy of the function must fail the pins above
+
+
+LB_MUTATIONS = {
+    "balance_without_E": ("balance = E * np.dot(f, P)", "balance = np.dot(f, P)"),
+    "fraction_without_k": ("f = counts / (T * k)", "f = counts / T"),
+    "gradient_sign": ("(f[None, :] - (p @ f)[:, None])", "((p @ f)[:, None] - f[None, :])"),
+    "probability_of_first_token": ("P = p.mean(axis=0)", "P = p[0]"),
+    "sample_std": ("counts.std() / mean", "counts.std(ddof=1) / mean"),
+    "gradient_without_alpha": ("grad = (alpha * E / T)", "grad = (E / T)"),
+}
+
+
+def _mutated(name):
+    import inspect
+    import textwrap
+    old, new = LB_MUTATIONS[name]
+    src = textwrap.dedent(inspect.getsource(oracle.load_balance))
+    assert src.count(old) == 1, name
+    ns = {"np": np}
+    exec(src.replace(old, new), ns)
+    return ns["load_balance"]
+
+
+def _pins_hold(lb) -> bool:
+    saved = oracle.load_balance
+    oracle.load_balance = lb
+    try:
+        for pin in (test_uniform_closed_form, test_one_expert_closed_form,
+                    test_gradient_finite_differences, test_invariants,
+                    test_gerrymandering_is_visible, test_zero_tokens):
+            pin()
+        return True
+    except AssertionError:
+        return False
+    finally:
+        oracle.load_balance = saved
+
+
+def test_unmutated_load_balance_passes():
+    assert _pins_hold(oracle.load_balance)
+
+
+@pytest.mark.parametrize("name", sorted(LB_MUTATIONS))
+def test_load_balance_mutation_is_caught(name):
+    assert not _pins_hold(_mutated(name)), f"planted mistake '{name}' went unnoticed"
