@@ -33,7 +33,8 @@
 //    producer waves (every global -> LDS copy), so the copies never wait on
 //    the epilogue's stores and the producers run ahead across tiles;
 //    gg_mfma (the SwiGLU backward, bf16 and MXFP8, whose epilogue stages dH'
-//    in the stage buffers) has every wave do both.
+//    in the stage buffers; every role with -DMOE_GG_MFMA_ALL=1) has every
+//    wave do both.
 //  * copy sources come from copy_plan.h, which moe_gemm_copy_walk also runs on
 //    the host to bound every copy of a launch.
 #include <type_traits>
@@ -1768,12 +1769,19 @@ static void launch_ws(const GemmArgs &a, hipStream_t s) {
     gg_ws<MODE, EPI, FP8, kWsBM, kWsBN, kWsWM, kWsWN, kWsNP, kWsStages><<<grid, threads, 0, s>>>(a);
 }
 
+// A build with -DMOE_GG_MFMA_ALL=1 runs every role on gg_mfma (every wave
+// copies and multiplies), the kernel gg_ws was split from: the same tiles,
+// schedules and MFMA order, so the same bits, for comparing the two.
+#ifndef MOE_GG_MFMA_ALL
+#define MOE_GG_MFMA_ALL 0
+#endif
+
 template <int MODE, int EPI, bool FP8>
 static void launch_mfma(const GemmArgs &a, hipStream_t s) {
     // every role on the split-role kernel except the SwiGLU backward, whose
     // epilogue stages dH' through the LDS stage buffers and reads a, b as
     // 16-byte rows (measured 2 % faster than a register-direct form)
-    if constexpr (EPI != MOE_EPI_SWIGLU_BWD) {
+    if constexpr (EPI != MOE_EPI_SWIGLU_BWD && !MOE_GG_MFMA_ALL) {
         launch_ws<MODE, EPI, FP8>(a, s);
     } else {
         const int grid = (num_cus() * MOE_ROW_OCC + 7) / 8 * 8;
