@@ -97,10 +97,14 @@ def role_work(w) -> dict:
         "gemm1_wgrad": (4 * R * d * h, R * 2 * h * q + R * d * q + 8 * E * d * h),
     }
     if mx:
+        # the MXFP8 backward stores no dy_perm: the combine backward writes one
+        # fp32 gate per routed row, and the dy quantiser reads the dOut rows
+        # (each token's once at the least) and those gates
+        W["combine_bwd"] = (0, a * T * d + a * R * d + 12 * T * k + 4 * R + 4 * T * E + 4 * T * k)
         W.update({
             "quant_x": (0, a * T * d + T * d * q),
             "quant_hp": (0, a * R * h + R * h * q),
-            "quant_dy_both": (0, a * R * d + 2 * R * d * q),
+            "quant_dy_both": (0, a * T * d + 8 * R + 2 * R * d * q),     # + gates, row map
             "quant_hp_cols": (0, a * R * h + R * h * q),
             "quant_dab_both": (0, a * R * 2 * h + 2 * R * 2 * h * q),
             "quant_x_cols": (0, a * R * d + R * d * q),

@@ -278,7 +278,10 @@ moe_status moe_gemm_copy_walk(const moe_gemm_desc *g, const int32_t *host_offset
  * (x_perm is not needed; x and sorted_token are); the four backward GEMMs
  * run in MXFP8 on operands the call quantises itself into ws: dy_perm along
  * d and along rows, H' along rows, dAB along 2h and along rows, and the rows
- * x[sorted_token] along rows. The weights come pre-quantised in their second
+ * x[sorted_token] along rows. dy_perm is quantised as it is formed from the
+ * dOut rows and the gates, and never stored: the dy_perm buffer serves as
+ * scratch (its first 4*T*k bytes receive each routed row's gate, fp32) and
+ * does not hold dy_perm on return. The weights come pre-quantised in their second
  * orientation (w1t/w1t_scale = W1[e] along 2h as [E, d, 2h];
  * w2t/w2t_scale = W2[e] along d as [E, h, d]; see mxfp8_quantize axis 0),
  * i.e. once per weight update. Needs d % 128 == 0, h % 128 == 0 and

@@ -26,7 +26,7 @@ moe_status combine_launch(const void *y, moe_dtype dt, const float *gate,
 moe_status combine_bwd_launch(const void *dout, const void *y, moe_dtype dt, const float *gate,
                               const int32_t *topk_idx, const int32_t *token_pos, int64_t T,
                               int d, int k, int E, void *dy, float *dlogits, float *dgate,
-                              hipStream_t s);
+                              hipStream_t s, bool row_gate_only = false);
 moe_status gemm_launch(const moe_gemm_desc *d, hipStream_t s);
 moe_status gemm_copy_walk(const moe_gemm_desc *d, const int32_t *host_offsets, moe_copy_walk *w);
 moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
@@ -35,7 +35,9 @@ moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, 
                                  hipStream_t s);
 moe_status mxfp8_quantize_both_launch(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
                                       const int32_t *group_offsets, int n_groups, uint8_t *q1,
-                                      uint8_t *s1, uint8_t *q0, uint8_t *s0, hipStream_t s);
+                                      uint8_t *s1, uint8_t *q0, uint8_t *s0, hipStream_t s,
+                                      const int32_t *row_map = nullptr,
+                                      const float *row_scale = nullptr);
 size_t mxfp8_col_blocks(int64_t rows, int n_groups);
 moe_status capacity_pad_launch(const int32_t *topk_idx, const int32_t *token_pos,
                                const int32_t *offsets, int64_t T, int E, int k, int C,
@@ -375,10 +377,14 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
     uint8_t *b0q = (uint8_t *)(ws + L.b0_q), *b0s = (uint8_t *)(ws + L.b0_s);
     uint8_t *b1q = (uint8_t *)(ws + L.b1_q), *b1s = (uint8_t *)(ws + L.b1_s);
     moe_status st;
-    // combine backward + router backward (bf16)
+    // combine backward + router backward (bf16). dy_perm is not stored: the
+    // combine backward leaves each routed row's gate in its first 4*T*k bytes
+    // and the quantiser below forms dy = round_bf16(gate * dOut[token]) as it
+    // reads the dOut rows
+    float *row_gate = reinterpret_cast<float *>(b->dy_perm);
     if ((st = combine_bwd_launch(b->dout, b->y_perm, MOE_BF16, b->topk_gate, b->topk_idx,
-                                 b->token_pos, b->T, d, b->k, E, b->dy_perm, b->dlogits,
-                                 b->dgate, s)) != MOE_OK ||
+                                 b->token_pos, b->T, d, b->k, E, row_gate, b->dlogits,
+                                 b->dgate, s, true)) != MOE_OK ||
         (st = stage_mark(b, 0, s)) != MOE_OK)
         return st;
     moe_gemm_desc g;
@@ -387,11 +393,11 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
     g.n_groups = E;
     g.rows = R;
     g.offsets = b->offsets;
-    // dy along d (GEMM2 dgrad) and along rows per expert (GEMM2 wgrad), one read
-    if ((st = R > 0 ? mxfp8_quantize_both_launch(b->dy_perm, MOE_BF16, R, d, b->offsets, E, aq, as, b0q,
-                                                  b0s, s)
-                    : mxfp8_quantize_launch(b->dy_perm, MOE_BF16, R, d, 0, b->offsets, E,
-                                            nullptr, b0q, b0s, s)) != MOE_OK ||
+    // dy along d (GEMM2 dgrad) and along rows per expert (GEMM2 wgrad), from
+    // one read of the dOut rows
+    if ((st = R > 0 ? mxfp8_quantize_both_launch(b->dout, MOE_BF16, R, d, b->offsets, E, aq, as, b0q,
+                                                  b0s, s, b->sorted_token, row_gate)
+                    : MOE_OK) != MOE_OK ||
         (st = stage_mark(b, 1, s)) != MOE_OK)
         return st;
     if (R > 0) {

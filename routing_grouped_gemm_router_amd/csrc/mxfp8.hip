@@ -313,12 +313,17 @@ __global__ __launch_bounds__(256) void mx_quant_cols_f32(const float *__restrict
 // second read of tensors needed in both orientations. Each lane pair writes
 // 16 bytes, so a row's 128 bytes go out as one full line, and its four scale
 // bytes as one word.
+// row_scale (with row_map): the rows quantised are round_bf16(row_scale[r] *
+// in[row_map[r]]), formed as they are loaded: the MXFP8 backward's dy rows
+// (each routed row's gate times its token's dOut row, rounded to bf16 as the
+// combine backward would store them) without a stored copy.
 template <bool BOTH>
 __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__restrict__ in,
                                                           int64_t rows, int64_t cols,
                                                           const int32_t *__restrict__ group_offsets,
                                                           int n_groups,
                                                           const int32_t *__restrict__ row_map,
+                                                          const float *__restrict__ row_scale,
                                                           uint8_t *__restrict__ q,
                                                           uint8_t *__restrict__ scale,
                                                           uint8_t *__restrict__ q1,
@@ -338,14 +343,18 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
     const bool full_row = c0 + 128 <= cols && cols % 128 == 0 && ((uintptr_t)s1 & 3) == 0;
 
     uint4 v[8];                           // v[p]: row 2qr + (p & 1) + 32 (p >> 1)
-    // row_map: this thread's source rows of the next unit to load, read one
-    // unit ahead so that the tile loads do not wait on the index loads
+    // row_map: this thread's source rows (and row_scale: their scales) of the
+    // next unit to load, read one unit ahead so that the tile loads do not
+    // wait on the index loads
     int32_t ri[8];
+    float rs[8], rs_v[8];                 // scales of the next unit; of the loaded one
     auto rows_of = [&](const UnitGeom &u) {
 #pragma unroll
         for (int p = 0; p < 8; p++) {
             const int r = 2 * qr + (p & 1) + 32 * (p >> 1);
-            ri[p] = (r < u.n && cok) ? row_map[u.r0 + r] : 0;
+            const bool ok = r < u.n && cok;
+            ri[p] = ok ? row_map[u.r0 + r] : 0;
+            if (row_scale) rs[p] = ok ? row_scale[u.r0 + r] : 0.f;
         }
     };
     auto load = [&](const UnitGeom &u) {
@@ -357,6 +366,7 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
                 const int64_t src = row_map ? (int64_t)ri[p] : u.r0 + r;
                 v[p] = *reinterpret_cast<const uint4 *>(in + src * cols + c0 + 8 * ch);
             }
+            if (row_scale) rs_v[p] = rs[p];
         }
     };
     int unit = blockIdx.y;
@@ -366,6 +376,15 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
     load(u);
     if (row_map && unit + (int)gridDim.y < n_units) rows_of(unit_geom(cu, ng, unit + gridDim.y));
     while (true) {
+        if (row_scale) {                  // the scaled rows, rounded to bf16
+#pragma unroll
+            for (int p = 0; p < 8; p++) {
+                uint32_t w[4] = {v[p].x, v[p].y, v[p].z, v[p].w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) w[e] = pack_bf16x2(rs_v[p] * lo_bf16(w[e]), rs_v[p] * hi_bf16(w[e]));
+                v[p] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
         // registers -> LDS (packed row pairs)
 #pragma unroll
         for (int k = 0; k < 4; k++) {
@@ -479,8 +498,8 @@ moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, 
         const int ng = group_offsets ? n_groups : 1;
         if (bf)
             mx_quant_cols_bf16<false><<<cols_grid(rows, cols, ng, kColsPerCU, 128), 256, 0, s>>>(
-                (const uint16_t *)in, rows, cols, group_offsets, n_groups, row_map, q, scale,
-                nullptr, nullptr);
+                (const uint16_t *)in, rows, cols, group_offsets, n_groups, row_map, nullptr, q,
+                scale, nullptr, nullptr);
         else
             mx_quant_cols_f32<false><<<cols_grid(rows, cols, ng, kColsPerCUF32, 64), 256, 0, s>>>(
                 (const float *)in, rows, cols, group_offsets, n_groups, row_map, q, scale, nullptr,
@@ -494,11 +513,15 @@ moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, 
 // one read.
 moe_status mxfp8_quantize_both_launch(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
                                       const int32_t *group_offsets, int n_groups, uint8_t *q1,
-                                      uint8_t *s1, uint8_t *q0, uint8_t *s0, hipStream_t s) {
+                                      uint8_t *s1, uint8_t *q0, uint8_t *s0, hipStream_t s,
+                                      const int32_t *row_map, const float *row_scale) {
     const int ng = group_offsets ? n_groups : 1;
+    if ((row_map || row_scale) && in_dt != MOE_BF16) return MOE_ERR_DTYPE;
+    if (row_scale && !row_map) return MOE_ERR_NULL;
     if (in_dt == MOE_BF16)
         mx_quant_cols_bf16<true><<<cols_grid(rows, cols, ng, kColsPerCU, 128), 256, 0, s>>>(
-            (const uint16_t *)in, rows, cols, group_offsets, n_groups, nullptr, q0, s0, q1, s1);
+            (const uint16_t *)in, rows, cols, group_offsets, n_groups, row_map, row_scale, q0, s0,
+            q1, s1);
     else
         mx_quant_cols_f32<true><<<cols_grid(rows, cols, ng, kColsPerCUF32, 64), 256, 0, s>>>(
             (const float *)in, rows, cols, group_offsets, n_groups, nullptr, q0, s0, q1, s1);

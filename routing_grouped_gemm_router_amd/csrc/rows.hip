@@ -163,8 +163,10 @@ __global__ __launch_bounds__(256) void combine_rows(const uint4 *__restrict__ y,
 // which equals it exactly but has no cancellation: with one gate near 1
 // (a confident router) the first form subtracts two nearly equal sums and
 // loses about log2(1 / (1 - g)) bits in fp32.
+// DY = false (the MXFP8 backward, whose quantiser forms dy_perm itself from
+// dOut and the gates): no dy rows; row_gate[p_j] = g_j instead.
 
-template <bool BF16, int KMAX>
+template <bool BF16, int KMAX, bool DY = true>
 __global__ __launch_bounds__(256) void combine_bwd_rows(
     const uint4 *__restrict__ dout, const uint4 *__restrict__ y, const float *__restrict__ gate,
     const int32_t *__restrict__ topk_idx, const int32_t *__restrict__ token_pos, int64_t T,
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(256) void combine_bwd_rows(
                     dot[j] = fmaf(fo[i], fy[i], dot[j]);
                     fd[i] = g[j] * fo[i];
                 }
-                dy[(int64_t)pos[j] * n16 + c] = store_f32<BF16>(fd);
+                if constexpr (DY) dy[(int64_t)pos[j] * n16 + c] = store_f32<BF16>(fd);
             }
         }
     }
@@ -237,6 +239,12 @@ __global__ __launch_bounds__(256) void combine_bwd_rows(
 #pragma unroll
         for (int j = 0; j < KMAX; j++)
             if (j < k) dgate[t * k + j] = dot[j];
+    }
+    if (!DY && lane == 0) {
+        float *row_gate = reinterpret_cast<float *>(dy);
+#pragma unroll
+        for (int j = 0; j < KMAX; j++)
+            if (pos[j] >= 0) row_gate[pos[j]] = g[j];
     }
 }
 
@@ -282,19 +290,24 @@ moe_status combine_launch(const void *y, moe_dtype dt, const float *gate,
     return launch_status();
 }
 
+// row_gate_only (bf16): dy receives the gate of each routed row (fp32, T*k
+// entries) instead of the dy rows.
 moe_status combine_bwd_launch(const void *dout, const void *y, moe_dtype dt, const float *gate,
                               const int32_t *topk_idx, const int32_t *token_pos, int64_t T,
                               int d, int k, int E, void *dy, float *dlogits, float *dgate,
-                              hipStream_t s) {
+                              hipStream_t s, bool row_gate_only) {
     if (T == 0) return MOE_OK;
     const bool bf = dt == MOE_BF16;
+    if (row_gate_only && !bf) return MOE_ERR_DTYPE;
     const int n16 = d * (bf ? 2 : 4) / 16;
     const unsigned nb = (unsigned)((T + kRowWaves - 1) / kRowWaves);
     const uint4 *dd = reinterpret_cast<const uint4 *>(dout);
     const uint4 *yy = reinterpret_cast<const uint4 *>(y);
     uint4 *oo = reinterpret_cast<uint4 *>(dy);
 #define L(K)                                                                                        \
-    (bf ? (combine_bwd_rows<true, K><<<nb, 256, 0, s>>>(dd, yy, gate, topk_idx, token_pos, T, n16, \
+    (row_gate_only ? (combine_bwd_rows<true, K, false><<<nb, 256, 0, s>>>(dd, yy, gate, topk_idx,  \
+                                                        token_pos, T, n16, k, E, oo, dlogits, dgate), 0) \
+    : bf ? (combine_bwd_rows<true, K><<<nb, 256, 0, s>>>(dd, yy, gate, topk_idx, token_pos, T, n16, \
                                                         k, E, oo, dlogits, dgate), 0)               \
         : (combine_bwd_rows<false, K><<<nb, 256, 0, s>>>(dd, yy, gate, topk_idx, token_pos, T,   \
                                                          n16, k, E, oo, dlogits, dgate), 0))
