@@ -654,11 +654,12 @@ def sample_sclk(torch, run_step, seconds: float = 0.6):
         if not busy:
             return None
         i = max(busy, key=lambda j: sum(act[j]) / len(act[j]))
-        # the samples taken while the graphics engine was busy (activity of
-        # at least half), so that gaps between steps do not count
+        # the samples taken while the graphics engine was busy (at least half
+        # the highest activity read), so that gaps between steps do not count
         pairs = [(c, a) for c, a in zip(clk[i], act[i])
                  if isinstance(c, (int, float)) and isinstance(a, (int, float))]
-        c = sorted(c for c, a in pairs if a >= 50)
+        top = max((a for _, a in pairs), default=0)
+        c = sorted(c for c, a in pairs if top > 0 and a >= top / 2)
         if not c:
             return None
         return {"median_mhz": c[len(c) // 2], "min_mhz": c[0], "max_mhz": c[-1], "samples": len(c),
