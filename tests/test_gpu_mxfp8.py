@@ -413,3 +413,38 @@ def test_mxfp8_full_size_sampled():
         print(f"expert {e} rows {counts[e]}: dW1 fro {f1:.2e} inf {rel_inf(g1, m['dW1'][e]):.2e}; "
               f"dW2 fro {f2:.2e} inf {rel_inf(g2, m['dW2'][e]):.2e}", flush=True)
         assert f1 <= tol and f2 <= tol, e
+
+
+def test_mxfp8_backward_forms_dy_bit_exact():
+    """The MXFP8 backward forms dy_perm inside its quantiser from the dOut rows
+    and each routed row's gate, without storing it. Its dAB and dW2 must equal,
+    bit for bit, the same MXFP8 GEMMs run on dy_perm as the bf16 combine
+    backward stores it (bf16 layer on the same routing and dOut), quantised
+    by mxfp8_quantize_both, with the MXFP8 layer's own saved a, b and H'."""
+    T, d, E, k, h = 300, 256, 8, 2, 128
+    inp = _mx_inputs(T, d, E, k, h, seed=11)
+    inp["logits"][:, 1] -= 100.0                      # an empty expert
+    layer, _, g = _run_mx(inp, k)
+    off = layer.route["offsets"]
+    R = T * k
+    # dy_perm rows as the combine backward stores them (independent of the
+    # weights): the bf16 layer on the same logits and dOut
+    lb = moe.MoELayer(dev(inp["w1"], torch.bfloat16), dev(inp["w2"], torch.bfloat16), k)
+    lb.forward(dev(inp["x"], torch.bfloat16), dev(inp["logits"], torch.float32))
+    gb = lb.backward(dev(inp["dout"], torch.bfloat16))
+    torch.cuda.synchronize()
+    assert torch.equal(lb.route["offsets"], off) and torch.equal(lb.route["token_pos"], layer.route["token_pos"])
+    (dyq, dys), (dyc, dycs) = moe.mxfp8_quantize_both(gb["dy_perm"], off)
+    # GEMM2 dgrad + SwiGLU backward on the rows layout
+    dab = torch.empty((R, 2 * h), dtype=torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(moe.MOE_GG_DGRAD, dyq, layer.w2t, dab, off, moe.MOE_EPI_SWIGLU_BWD,
+                         N=h, K=d, aux=layer.ab, a_scale=dys, b_scale=layer.w2ts,
+                         dtype=moe.MOE_MXFP8)
+    assert torch.equal(dab, g["dab"])
+    # GEMM2 wgrad on the column layouts of dy and H'
+    hc, hcs = moe.mxfp8_quantize(layer.hp, 0, off)
+    dw2 = torch.full((E, d, h), float("nan"), device="cuda")
+    moe.moe_grouped_gemm(moe.MOE_GG_WGRAD, dyc, hc, dw2, off, M=d, N=h, a_scale=dycs,
+                         b_scale=hcs, dtype=moe.MOE_MXFP8, rows=R)
+    torch.cuda.synchronize()
+    assert torch.equal(dw2, g["dw2"])
