@@ -103,9 +103,11 @@ def role_work(w) -> dict:
         W["combine_bwd"] = (0, a * T * d + a * R * d + 12 * T * k + 4 * R + 4 * T * E + 4 * T * k)
         W.update({
             "quant_x": (0, a * T * d + T * d * q),
-            "quant_hp": (0, a * R * h + R * h * q),
+            # H' in both layouts from one read (GEMM2's operand and GEMM2
+            # wgrad's), so the backward's H' quantiser has no work
+            "quant_hp": (0, a * R * h + 2 * R * h * q),
             "quant_dy_both": (0, a * T * d + 8 * R + 2 * R * d * q),     # + gates, row map
-            "quant_hp_cols": (0, a * R * h + R * h * q),
+            "quant_hp_cols": (0, 0),
             "quant_dab_both": (0, a * R * 2 * h + 2 * R * 2 * h * q),
             "quant_x_cols": (0, a * R * d + R * d * q),
         })
@@ -220,7 +222,7 @@ def run_layer(moe, torch, w, inp, steps, warmup, layer=None, flush=None):
                                  moe.MOE_EPI_SWIGLU_FWD, N=2 * h, K=d, aux_out=layer.hp,
                                  a_scale=layer.xps, b_scale=layer.w1s, dtype=moe.MOE_MXFP8)
             mark(4)
-            moe.mxfp8_quantize(layer.hp, 1, q=layer.hpq, scale=layer.hps)
+            layer.quantize_hp(r["offsets"])
             mark(5)
             moe.moe_grouped_gemm(moe.MOE_GG_FWD, layer.hpq, layer.w2q, layer.y_perm, r["offsets"],
                                  N=d, K=h, a_scale=layer.hps, b_scale=layer.w2s,

@@ -333,9 +333,16 @@ typedef struct moe_bwd_desc {
      *   2 GEMM2 dgrad + SwiGLU-bwd, 3 quantise H' (columns), 4 GEMM2 wgrad,
      *   5 quantise dAB (both layouts), 6 GEMM1 dgrad, 7 unpermute-bwd,
      *   8 quantise x[sorted_token] (columns), 9 GEMM1 wgrad.
-     * A stage with no work (T = 0) still records its event. A failed record
-     * returns MOE_ERR_LAUNCH. */
+     * A stage with no work (T = 0, or stage 3 with hp_cols given) still
+     * records its event. A failed record returns MOE_ERR_LAUNCH. */
     void *const *stage_events;
+    /* MXFP8 only, optional (null = none): H' already quantised along rows per
+     * expert (the column-block layout of mxfp8_quantize axis 0 with `offsets`,
+     * mxfp8_col_blocks(T*k, E) blocks; e.g. from the forward's
+     * mxfp8_quantize_both of H', which also gives GEMM2's operand). When
+     * given, GEMM2-wgrad uses it and `hp` is not read (it may be null). */
+    const uint8_t *hp_cols;        /* mxfp8_col_blocks(T*k, E) * 32 * h bytes */
+    const uint8_t *hp_cols_scale;  /* mxfp8_col_blocks(T*k, E) * h bytes */
 } moe_bwd_desc;
 
 #define MOE_BWD_MAX_STAGES 10

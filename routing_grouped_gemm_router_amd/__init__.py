@@ -55,7 +55,7 @@ class BwdDesc(ctypes.Structure):
                 ("dgate", _P), ("dy_perm", _P), ("dab", _P), ("dx_perm", _P), ("x", _P),
                 ("sorted_token", _P), ("w1t", _P), ("w1t_scale", _P), ("w2t", _P),
                 ("w2t_scale", _P), ("ws", _P), ("ws_bytes", _SZ), ("accumulate_dw", _I32),
-                ("stage_events", ctypes.POINTER(_P))]
+                ("stage_events", ctypes.POINTER(_P)), ("hp_cols", _P), ("hp_cols_scale", _P)]
 
 class CopyWalk(ctypes.Structure):
     _fields_ = [("extent", _I64 * 4), ("copies", _I64), ("zero_copies", _I64),
@@ -164,6 +164,14 @@ def _need(t, shape, dtype, name):
         raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on GPU, got "
                          f"{t.dtype} {tuple(t.shape)} (contiguous={t.is_contiguous()}, "
                          f"device={t.device})")
+
+
+def _need_bytes(t, nbytes, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != torch.uint8 or not t.is_contiguous() or not t.is_cuda or t.numel() < nbytes:
+        raise ValueError(f"{name}: expected a contiguous uint8 GPU buffer of at least {nbytes} "
+                         f"bytes, got {t.dtype} {tuple(t.shape)}")
 
 
 # ---------------------------------------------------------------------------
@@ -370,7 +378,12 @@ def moe_backward(saved: dict, dout: torch.Tensor, E: int, k: int, d: int, h: int
     names += (("x", "sorted_token", "w1t", "w1t_scale", "w2t", "w2t_scale") if mxfp8
               else ("x_perm", "w1", "w2"))
     for name in names:
+        if name == "hp" and saved.get(name) is None and mxfp8:
+            continue                               # H' brought in its column layout instead
         setattr(b, name, saved[name].data_ptr())
+    if mxfp8 and saved.get("hp_cols") is not None:
+        b.hp_cols = saved["hp_cols"].data_ptr()
+        b.hp_cols_scale = saved["hp_cols_scale"].data_ptr()
     b.dout = dout.data_ptr()
     for name in ("dx", "dlogits", "dw1", "dw2", "dy_perm", "dab", "dx_perm"):
         setattr(b, name, out[name].data_ptr())
@@ -457,17 +470,26 @@ def mxfp8_quantize(x: torch.Tensor, axis: int = 1, group_offsets: torch.Tensor |
     return q, scale
 
 
-def mxfp8_quantize_both(x: torch.Tensor, group_offsets: torch.Tensor | None = None):
+def mxfp8_quantize_both(x: torch.Tensor, group_offsets: torch.Tensor | None = None,
+                        out: tuple | None = None):
     """Both orientations from one read (see moe.h): returns (q_rows, s_rows)
-    as mxfp8_quantize axis=1 and (q_cols, s_cols) as axis=0 with these groups."""
+    as mxfp8_quantize axis=1 and (q_cols, s_cols) as axis=0 with these groups,
+    into `out` = (q_rows, s_rows, q_cols, s_cols) when given."""
     rows, cols = x.shape
     dev = x.device
     ng = 0 if group_offsets is None else group_offsets.numel() - 1
-    q1 = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
-    s1 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
     nb = mxfp8_col_blocks(rows, max(ng, 1))
-    q0 = torch.empty(nb * 32 * cols, dtype=torch.uint8, device=dev)
-    s0 = torch.empty(nb * cols, dtype=torch.uint8, device=dev)
+    if out is not None:
+        q1, s1, q0, s0 = out
+        _need(q1, (rows, cols), torch.uint8, "q_rows")
+        _need(s1, (rows, cols // 32), torch.uint8, "s_rows")
+        _need_bytes(q0, nb * 32 * cols, "q_cols")
+        _need_bytes(s0, nb * cols, "s_cols")
+    else:
+        q1 = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        s1 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+        q0 = torch.empty(nb * 32 * cols, dtype=torch.uint8, device=dev)
+        s0 = torch.empty(nb * cols, dtype=torch.uint8, device=dev)
     _check("mxfp8_quantize_both", _lib.mxfp8_quantize_both(
         _p(x), _dt(x), rows, cols, _p(group_offsets), ng, _p(q1), _p(s1), _p(q0), _p(s0),
         _stream()))
@@ -808,9 +830,16 @@ class MoELayerMX:
         self.xpq = tmp("xpq", (R, d), torch.uint8)
         self.xps = tmp("xps", (R, d // 32), torch.uint8)
         self.ab = tmp("ab", (R, 2 * h), torch.bfloat16)
-        self.hp = tmp("hp", (R, h), torch.bfloat16)
-        self.hpq = tmp("hpq", (R, h), torch.uint8)
-        self.hps = tmp("hps", (R, h // 32), torch.uint8)
+        # H' and its GEMM2 operand are read in the forward only
+        self.hp = _scratch("mx_hp", (R, h), torch.bfloat16, dev)
+        self.hpq = _scratch("mx_hpq", (R, h), torch.uint8, dev)
+        self.hps = _scratch("mx_hps", (R, h // 32), torch.uint8, dev)
+        # H' along rows per expert (GEMM2 wgrad's operand), quantised in the
+        # forward from the same read as GEMM2's; held instead of bf16 H'
+        if not self.recompute:
+            nb = mxfp8_col_blocks(R, E)
+            self.hpc = torch.empty(nb * 32 * h, **u8)
+            self.hpcs = torch.empty(nb * h, **u8)
         self.y_perm = torch.empty((R, d), **bf)
         self.out = torch.empty((T, d), **bf)
         self.grads = None
@@ -841,18 +870,30 @@ class MoELayerMX:
         if self.balance is not None:
             self.lb_stats = self.balance.forward(logits, r["counts"], self.k)
         self._gemm1(x, r["offsets"], r["token_pos"])
-        mxfp8_quantize(self.hp, 1, q=self.hpq, scale=self.hps)
+        self.quantize_hp(r["offsets"])
         moe_grouped_gemm(MOE_GG_FWD, self.hpq, self.w2q, self.y_perm, r["offsets"], N=d, K=h,
                          a_scale=self.hps, b_scale=self.w2s, dtype=MOE_MXFP8)
         moe_combine(self.y_perm, r["topk_gate"], r["token_pos"], self.out)
         return self.out
 
+    def quantize_hp(self, offsets):
+        """H' along h for GEMM2 and, unless recomputing (the backward then
+        quantises the H' it recomputes), along rows per expert for GEMM2's
+        weight gradient, both from one read."""
+        if self.recompute:
+            mxfp8_quantize(self.hp, 1, q=self.hpq, scale=self.hps)
+        else:
+            mxfp8_quantize_both(self.hp, offsets, out=(self.hpq, self.hps, self.hpc, self.hpcs))
+
     def saved(self) -> dict:
         r = self.route
-        return dict(x=self.x, sorted_token=r["sorted_token"], ab=self.ab, hp=self.hp,
-                    y_perm=self.y_perm, topk_gate=r["topk_gate"], topk_idx=r["topk_idx"],
-                    token_pos=r["token_pos"], offsets=r["offsets"], w1t=self.w1t,
-                    w1t_scale=self.w1ts, w2t=self.w2t, w2t_scale=self.w2ts)
+        sv = dict(x=self.x, sorted_token=r["sorted_token"], ab=self.ab, hp=self.hp,
+                  y_perm=self.y_perm, topk_gate=r["topk_gate"], topk_idx=r["topk_idx"],
+                  token_pos=r["token_pos"], offsets=r["offsets"], w1t=self.w1t,
+                  w1t_scale=self.w1ts, w2t=self.w2t, w2t_scale=self.w2ts)
+        if not self.recompute:
+            sv.update(hp=None, hp_cols=self.hpc, hp_cols_scale=self.hpcs)
+        return sv
 
     def held_bytes(self) -> int:
         """Bytes of activations held from forward to backward (x and the
@@ -860,7 +901,7 @@ class MoELayerMX:
         meta = _nbytes(self.route.values())
         if self.recompute:
             return meta + _nbytes([self.y_perm])
-        return meta + _nbytes([self.ab, self.hp, self.y_perm])
+        return meta + _nbytes([self.ab, self.hpc, self.hpcs, self.y_perm])
 
     def backward(self, dout: torch.Tensor, accumulate_dw: bool = False,
                  stage_events=None) -> dict:

@@ -359,15 +359,17 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
         !b->w2t_scale)
         return MOE_ERR_NULL;
     const bool any = b->T > 0;
-    if (any && (!b->x || !b->sorted_token || !b->ab || !b->hp || !b->y_perm || !b->topk_gate ||
+    if (!b->hp_cols != !b->hp_cols_scale) return MOE_ERR_NULL;
+    if (any && (!b->x || !b->sorted_token || !b->ab || (!b->hp && !b->hp_cols) || !b->y_perm || !b->topk_gate ||
                 !b->topk_idx || !b->token_pos || !b->dout || !b->dx || !b->dlogits ||
                 !b->dy_perm || !b->dab || !b->dx_perm || !b->ws))
         return MOE_ERR_NULL;
     const void *al[] = {b->x, b->ab, b->hp, b->y_perm, b->dout, b->dx, b->dw1, b->dw2,
-                        b->dy_perm, b->dab, b->dx_perm, b->w1t, b->w2t, b->ws};
+                        b->dy_perm, b->dab, b->dx_perm, b->w1t, b->w2t, b->ws, b->hp_cols};
     for (const void *p : al)
         if (p && !aligned16(p)) return MOE_ERR_ALIGN;
     if (!aligned4(b->w1t_scale) || !aligned4(b->w2t_scale)) return MOE_ERR_ALIGN;
+    if (b->hp_cols_scale && !aligned4(b->hp_cols_scale)) return MOE_ERR_ALIGN;
     const int64_t R = b->T * b->k;
     const int d = b->d, h = b->h, E = b->E;
     const MxBwdLayout L = mx_bwd_layout(R, d, h, E);
@@ -408,14 +410,18 @@ static moe_status backward_mxfp8(const moe_bwd_desc *b, hipStream_t s) {
         if ((st = gemm_launch(&g, s)) != MOE_OK) return st;
     }
     if ((st = stage_mark(b, 2, s)) != MOE_OK) return st;
-    // GEMM2 wgrad: dy and H' along rows, per expert
-    if ((st = mxfp8_quantize_launch(b->hp, MOE_BF16, R, h, 0, b->offsets, E, nullptr, b1q, b1s,
-                                    s)) != MOE_OK ||
-        (st = stage_mark(b, 3, s)) != MOE_OK)
+    // GEMM2 wgrad: dy and H' along rows, per expert (H' quantised here unless
+    // the caller brings it in that layout)
+    if (!b->hp_cols &&
+        (st = mxfp8_quantize_launch(b->hp, MOE_BF16, R, h, 0, b->offsets, E, nullptr, b1q, b1s,
+                                    s)) != MOE_OK)
         return st;
+    if ((st = stage_mark(b, 3, s)) != MOE_OK) return st;
     g.mode = MOE_GG_WGRAD; g.epilogue = MOE_EPI_NONE; g.aux = nullptr; g.M = d; g.N = h; g.K = 0;
     g.accumulate = b->accumulate_dw;
-    g.A = b0q; g.a_scale = b0s; g.B = b1q; g.b_scale = b1s; g.C = b->dw2;
+    g.A = b0q; g.a_scale = b0s; g.C = b->dw2;
+    g.B = b->hp_cols ? b->hp_cols : b1q;
+    g.b_scale = b->hp_cols ? b->hp_cols_scale : b1s;
     if ((st = gemm_launch(&g, s)) != MOE_OK || (st = stage_mark(b, 4, s)) != MOE_OK) return st;
     // dAB along 2h (GEMM1 dgrad) and along rows per expert (GEMM1 wgrad), one read
     if ((st = R > 0 ? mxfp8_quantize_both_launch(b->dab, MOE_BF16, R, 2 * h, b->offsets, E, aq, as, b0q,

@@ -448,3 +448,21 @@ def test_mxfp8_backward_forms_dy_bit_exact():
                          b_scale=hcs, dtype=moe.MOE_MXFP8, rows=R)
     torch.cuda.synchronize()
     assert torch.equal(dw2, g["dw2"])
+
+
+def test_mxfp8_backward_with_forward_quantised_hp_bit_exact():
+    """The MXFP8 layer quantises H' in both layouts in the forward and hands
+    the backward H' along rows per expert (hp_cols), so the backward reads no
+    bf16 H'. The gradients equal, bit for bit, those of the backward that
+    quantises the bf16 H' itself."""
+    T, d, E, k, h = 300, 256, 8, 2, 128
+    inp = _mx_inputs(T, d, E, k, h, seed=12)
+    inp["logits"][:, 1] -= 100.0                      # an empty expert
+    layer, _, g = _run_mx(inp, k)
+    sv = layer.saved()
+    assert sv.get("hp_cols") is not None and sv["hp"] is None
+    sv.update(hp=layer.hp, hp_cols=None, hp_cols_scale=None)   # H' is still in the forward's buffer
+    g2 = moe.moe_backward(sv, dev(inp["dout"], torch.bfloat16), E, k, d, h, mxfp8=True)
+    torch.cuda.synchronize()
+    for key in ("dx", "dlogits", "dw1", "dw2", "dab", "dx_perm", "dgate"):
+        assert torch.equal(g[key], g2[key]), key
