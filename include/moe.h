@@ -38,7 +38,8 @@
  *   - Non-finite logits are outside the contract: outputs are then
  *     unspecified, but no kernel indexes out of bounds.
  *   - Stateless and re-entrant: concurrent calls on different streams are
- *     safe given distinct output and workspace buffers.
+ *     safe given distinct output and workspace buffers (moe_route_noalloc,
+ *     which keeps its scratch in the library, is the one exception).
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -71,7 +72,9 @@ enum {
 /* Human-readable name of a status code (static string). */
 const char *moe_status_str(moe_status s);
 
-/* ABI version of this header (major * 100 + minor). */
+/* ABI version of this header (major * 100 + minor). 101: moe_bwd_desc ends
+ * with hp_cols, hp_cols_scale (zero them when unused), and the MXFP8
+ * backward uses dy_perm as scratch. */
 int32_t moe_version(void);
 
 /* ------------------------------------------------------------------ */

@@ -123,7 +123,7 @@ const char *moe_status_str(moe_status s) {
     }
 }
 
-int32_t moe_version(void) { return 100; }
+int32_t moe_version(void) { return 101; }
 
 size_t moe_route_workspace_size(int64_t T, int32_t E, int32_t k) {
     (void)k;

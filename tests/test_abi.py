@@ -50,7 +50,7 @@ def test_status_strings(lib):
     for s in range(7):
         assert lib.moe_status_str(s).startswith(b"MOE_")
     lib.moe_version.restype = ctypes.c_int32
-    assert lib.moe_version() == 100
+    assert lib.moe_version() == 101
 
 
 def test_validation_without_gpu(lib):
