@@ -11,15 +11,20 @@
 // The scale is taken from the fp32 bit pattern:
 //   scale byte = max(biased fp32 exponent of amax - 8, 0)   (zero and fp32
 //                subnormal amax give byte 0, i.e. 2^-127)
-// The elements x * 2^-shared are encoded by the CDNA4 conversion instruction
-// (v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even) on inputs clamped to
-// +-448, which is the saturation; its only departure from the format is a
-// NaN, which it writes as 0xff whatever the sign, so a positive NaN is
-// patched to 0x7f. Waves without a NaN clamp with v_med3_f32 (e4m3x4).
-// Checked on the GPU against an integer encoding of the format (mantissa
-// rounded from 23 to 3 bits ties to even, exponent rebased from 127 to 7;
-// rint(|v| * 2^9) below 2^-6) on all 2^32 fp32 patterns: identical except
-// NaN's sign, which the patch restores.
+// The elements x * 2^-shared are encoded by the CDNA4 conversion instructions
+// (OCP E4M3, round to nearest even) on inputs clamped to +-448 (after the
+// scaling), which is the saturation. Waves without a NaN clamp with
+// v_med3_f32 and convert with v_cvt_scalef32_pk_fp8_f32, which applies the
+// shared exponent itself; a wave with a NaN scales with ldexp and converts
+// with v_cvt_pk_fp8_f32, whose only departure from the format is a NaN,
+// written as 0xff whatever the sign, so a positive NaN is patched to 0x7f.
+// Checked on the GPU: the ldexp form against an integer encoding of the
+// format (mantissa rounded from 23 to 3 bits ties to even, exponent rebased
+// from 127 to 7; rint(|v| * 2^9) below 2^-6) on all 2^32 fp32 patterns,
+// identical except NaN's sign, which the patch restores; the scaled form
+// against the ldexp form on all 2^32 non-NaN fp32 patterns for scale bytes
+// 0, 1, 64, 119, 120, 127, 134, 200, 246, 254 and on every bf16 pattern for
+// every scale byte 0..254, identical.
 // Each kernel reads its input once and writes each output once; the encoding
 // arithmetic is about half of the time of the both-layouts kernels, memory
 // traffic the rest.
@@ -32,29 +37,39 @@ MOE_DEV uint32_t mx_scale_byte(float amax) {
     return (uint32_t)max(ef - 8, 0);
 }
 
-// four elements, scaled by 2^sh, to four E4M3 bytes (first element lowest)
-MOE_DEV uint32_t e4m3x4(float a, float b, float c, float d, int sh) {
-    const float v[4] = {ldexpf(a, sh), ldexpf(b, sh), ldexpf(c, sh), ldexpf(d, sh)};
-    // With no NaN in the wave (the rule) the +-448 saturation is one
-    // v_med3_f32 per value, which gives the same bytes as the select form
-    // below for every other input (checked on the GPU on all 2^32 patterns);
-    // med3 maps a NaN to a finite value, so a wave that holds one takes the
-    // select form.
-    const bool any_nan = __builtin_isnan(v[0]) || __builtin_isnan(v[1]) || __builtin_isnan(v[2]) ||
-                         __builtin_isnan(v[3]);
+// four elements, scaled by 2^(127 - sb), to four E4M3 bytes (first element
+// lowest). With no NaN in the wave (the rule): each value is clamped to
+// +-448 * 2^(sb - 127) by one v_med3_f32 and the pair converted by
+// v_cvt_scalef32_pk_fp8_f32, which takes the E8M0 byte as the exponent field
+// of its scale operand and divides by it (checked on the GPU on every bf16
+// pattern and every scale byte 0..254: the same bytes as the form below).
+// med3 maps a NaN to a finite value, so a wave that holds one takes the
+// select form, which scales with ldexp, saturates and patches NaN signs.
+MOE_DEV uint32_t e4m3x4(float a, float b, float c, float d, uint32_t sb) {
+    const float x[4] = {a, b, c, d};
+    const bool any_nan = __builtin_isnan(a) || __builtin_isnan(b) || __builtin_isnan(c) ||
+                         __builtin_isnan(d);
     if (__ballot(any_nan) == 0) {
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(v[0], -448.0f, 448.0f),
-                                                __builtin_amdgcn_fmed3f(v[1], -448.0f, 448.0f), 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(v[2], -448.0f, 448.0f),
-                                            __builtin_amdgcn_fmed3f(v[3], -448.0f, 448.0f), w, true);
-        return (uint32_t)w;
+        typedef short s16x2 __attribute__((ext_vector_type(2)));
+        const float scale = __uint_as_float(sb << 23);
+        const float bound = sb + 8 < 255 ? __uint_as_float(((sb + 8) << 23) | 0x600000u)
+                                         : __builtin_inff();   // 448 * 2^(sb - 127)
+        float cl[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) cl[i] = __builtin_amdgcn_fmed3f(x[i], -bound, bound);
+        const s16x2 z = {0, 0};
+        const s16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, cl[0], cl[1], scale, false);
+        const s16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, cl[2], cl[3], scale, true);
+        return (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
     }
+    const int sh = 127 - (int)sb;
     float cl[4];
     uint32_t pnan = 0;                                  // positive NaNs: 0xff -> 0x7f
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        cl[i] = fabsf(v[i]) > 448.0f ? copysignf(448.0f, v[i]) : v[i];
-        pnan |= ((int32_t)__float_as_uint(v[i]) > 0x7f800000) ? 0x80u << (8 * i) : 0u;
+        const float v = ldexpf(x[i], sh);
+        cl[i] = fabsf(v) > 448.0f ? copysignf(448.0f, v) : v;
+        pnan |= ((int32_t)__float_as_uint(v) > 0x7f800000) ? 0x80u << (8 * i) : 0u;
     }
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl[0], cl[1], 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(cl[2], cl[3], w, true);
@@ -109,10 +124,9 @@ __global__ __launch_bounds__(256) void mx_quant_rows(const void *__restrict__ in
     amax = fmaxf(amax, dpp_move<kDppXor1>(amax));
     const uint32_t sb = mx_scale_byte(amax);
     if (!ok) return;
-    const int sh = 127 - (int)sb;
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) w[i] = e4m3x4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], sh);
+    for (int i = 0; i < 4; i++) w[i] = e4m3x4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], sb);
     reinterpret_cast<uint4 *>(q)[gid] = make_uint4(w[0], w[1], w[2], w[3]);
     if ((threadIdx.x & 1) == 0) scale[blk] = (uint8_t)sb;
 }
@@ -196,10 +210,9 @@ MOE_DEV uint32_t encode_block32(const float *f, uint8_t *dst) {
 #pragma unroll
     for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(f[i]));
     const uint32_t sb = mx_scale_byte(amax);
-    const int sh = 127 - (int)sb;
     uint32_t w[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) w[i] = e4m3x4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], sh);
+    for (int i = 0; i < 8; i++) w[i] = e4m3x4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], sb);
     uint4 *d = reinterpret_cast<uint4 *>(dst);
     d[0] = make_uint4(w[0], w[1], w[2], w[3]);
     d[1] = make_uint4(w[4], w[5], w[6], w[7]);
@@ -270,8 +283,7 @@ __global__ __launch_bounds__(256) void mx_quant_cols_f32(const float *__restrict
                 am = fmaxf(am, dpp_move<kDppHalfMirror>(am));
                 if (r < u.n && cok) {
                     const uint32_t sb = mx_scale_byte(am);
-                    const int sh = 127 - (int)sb;
-                    const uint32_t w = e4m3x4(v[p].x, v[p].y, v[p].z, v[p].w, sh);
+                    const uint32_t w = e4m3x4(v[p].x, v[p].y, v[p].z, v[p].w, sb);
                     *reinterpret_cast<uint32_t *>(q1 + (u.r0 + r) * cols + c0 + 4 * ch) = w;
                     if ((ch & 7) == 0) s1[(u.r0 + r) * (cols / 32) + (c0 + 4 * ch) / 32] = (uint8_t)sb;
                 }
@@ -412,9 +424,8 @@ __global__ __launch_bounds__(256) void mx_quant_cols_bf16(const uint16_t *__rest
                 am = fmaxf(am, dpp_move<kDppXor1>(am));
                 am = fmaxf(am, dpp_move<kDppXor2>(am));
                 const uint32_t sb = mx_scale_byte(am);
-                const int sh = 127 - (int)sb;
-                const uint32_t lo4 = e4m3x4(f[0], f[1], f[2], f[3], sh);
-                const uint32_t hi4 = e4m3x4(f[4], f[5], f[6], f[7], sh);
+                const uint32_t lo4 = e4m3x4(f[0], f[1], f[2], f[3], sb);
+                const uint32_t hi4 = e4m3x4(f[4], f[5], f[6], f[7], sb);
                 // the odd lane's 8 bytes go out with the even lane's store
                 const uint32_t plo = (uint32_t)dpp_move<kDppXor1>((int)lo4);
                 const uint32_t phi = (uint32_t)dpp_move<kDppXor1>((int)hi4);
