@@ -6,6 +6,8 @@
     python -m routing_grouped_gemm_router_amd.rocprof_summary api DIR_A DIR_B STEPS_A STEPS_B \
         TITLE CMD_A CMD_B > out.md
     python -m routing_grouped_gemm_router_amd.rocprof_summary sq DIR TITLE CMD [NAMES] > out.md
+    python -m routing_grouped_gemm_router_amd.rocprof_summary counters FETCH_DIR WRITE_DIR \
+        LABEL=KERNEL[#n/p];... COPY_BYTES TITLE CMD_FETCH CMD_WRITE > out.md
 
 `stats` tabulates DIR/run_kernel_stats.csv (from --kernel-trace --stats
 --output-format csv). `pmc` reads two --pmc runs (FETCH_SIZE, then
@@ -17,7 +19,9 @@ run. The result carries the hash of the GEMM sources it was measured on, so
 a reader can tell whether it still describes the current kernel. `api`
 compares the HIP API call counts of two runs that differ only in their
 number of timed steps (what one step issues); `sq` tabulates SQ counters
-per kernel.
+per kernel; `counters` tabulates the scaled FETCH_SIZE / WRITE_SIZE of several
+kernels of one step (the row movers and quantisers) and carries the hash of
+their sources.
 
 Only reads the CSV files; runs nothing.
 """
@@ -32,14 +36,21 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 # the sources that make up the grouped GEMM kernel
 GEMM_SOURCES = ("csrc/gemm.hip", "csrc/copy_plan.h", "csrc/common.h", "../include/moe.h")
+# the sources of the row movers, the routing kernels and the MXFP8 quantisers
+ROW_SOURCES = ("csrc/rows.hip", "csrc/route.hip", "csrc/mxfp8.hip", "csrc/common.h",
+               "../include/moe.h")
 
 
-def gemm_source_hash() -> str:
+def source_hash(sources) -> str:
     h = hashlib.sha256()
-    for rel in GEMM_SOURCES:
+    for rel in sources:
         with open(os.path.join(PKG, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def gemm_source_hash() -> str:
+    return source_hash(GEMM_SOURCES)
 
 
 def _short(name: str, n: int = 96) -> str:
@@ -113,6 +124,44 @@ def pmc(fetch_dir: str, write_dir: str, kernel: str, copy_bytes: int, title: str
     return "\n".join(out)
 
 
+def _scaled(d: str, counter: str, copy_bytes: int):
+    """Per-dispatch bytes of one counter run, scaled by the copy calibration."""
+    vals, names = _per_dispatch(d, counter)
+    copies = [vals[i] * 1024 for i in vals if "copyBuffer" in names[i]]
+    if not copies:
+        raise SystemExit(f"{counter}: no copy dispatch in {d}")
+    scale = copy_bytes / max(copies)
+    return {i: v * 1024 * scale for i, v in vals.items()}, names, scale
+
+
+def counters(fetch_dir: str, write_dir: str, specs, copy_bytes: int, title: str, cmd_fetch: str,
+             cmd_write: str) -> str:
+    """Scaled read and written bytes per launch of several kernels; specs are
+    LABEL=KERNEL[#n/p] strings (see _select)."""
+    rd, rnames, rs = _scaled(fetch_dir, "FETCH_SIZE", copy_bytes)
+    wr, wnames, ws = _scaled(write_dir, "WRITE_SIZE", copy_bytes)
+    out = [f"# {title}", "",
+           "HBM bytes per launch from two counter runs (FETCH_SIZE, then WRITE_SIZE),",
+           f"each scaled by what the counter reads for a {copy_bytes / 2**20:.0f} MiB device copy in",
+           f"that run (reads x{rs:.3f}, writes x{ws:.3f}).", "",
+           "Commands (one MI355X):", "", "```", cmd_fetch, cmd_write, "```", "",
+           "| role | kernel | launches | read bytes / launch | written bytes / launch |",
+           "|---|---|---|---|---|"]
+    for spec in specs:
+        label, kernel = spec.split("=", 1)
+        kname, nth, period = _select(kernel)
+        per = []
+        for vals, names in ((rd, rnames), (wr, wnames)):
+            ids = sorted(i for i in vals if kname in names[i])
+            kv = [vals[i] for j, i in enumerate(ids) if j % period == nth]
+            if not kv:
+                raise SystemExit(f"no '{kernel}' dispatch")
+            per.append((sum(kv) / len(kv), len(kv)))
+        out.append(f"| {label} | `{_short(kname, 60)}` | {per[0][1]} | {per[0][0]:.4g} | {per[1][0]:.4g} |")
+    out += ["", f"row_source_hash = {source_hash(ROW_SOURCES)}", ""]
+    return "\n".join(out)
+
+
 def api_diff(d_small: str, d_large: str, n_small: int, n_large: int, title: str, cmd_small: str,
              cmd_large: str) -> str:
     """HIP API calls of two runs that differ only in their number of timed
@@ -177,6 +226,9 @@ if __name__ == "__main__":
     elif sys.argv[1] == "sq":
         sys.stdout.write(sq(sys.argv[2], sys.argv[3], sys.argv[4],
                             sys.argv[5].split(",") if len(sys.argv) > 5 else None))
+    elif sys.argv[1] == "counters":
+        sys.stdout.write(counters(sys.argv[2], sys.argv[3], sys.argv[4].split(";"), int(sys.argv[5]),
+                                  sys.argv[6], sys.argv[7], sys.argv[8]))
     elif sys.argv[1] == "pmc":
         sys.stdout.write(pmc(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6],
                              sys.argv[7], sys.argv[8]))

@@ -117,3 +117,41 @@ def test_role_table_carries_median_and_min():
     assert r["us"] == pytest.approx(350.0)
     assert r["us_median"] == pytest.approx(348.0) and r["us_min"] == pytest.approx(341.0)
     assert "us_median" not in bench.role_table(w, {"gemm2": 0.350})["gemm2"]
+
+
+def test_counter_tables_of_the_row_movers(tmp_path):
+    """The multi-kernel summary: copy-scaled bytes per launch, the n-th of
+    every p launches of a shared name, and the hash of the row sources."""
+    import csv
+
+    def write(d, counter, rows):
+        d.mkdir()
+        with open(d / "run_counter_collection.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for i, (name, kib) in enumerate(rows):
+                for half in (0.5, 0.5):              # two counter instances per dispatch
+                    w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": counter,
+                                "Counter_Value": kib * half})
+    step = [("moe::permute_rows16<4>", 100.0), ("moe::mx_quant_cols_bf16<true>", 10.0),
+            ("moe::mx_quant_cols_bf16<true>", 20.0), ("__amd_rocclr_copyBuffer", 512.0)]
+    write(tmp_path / "f", "FETCH_SIZE", step)
+    write(tmp_path / "w", "WRITE_SIZE", [(n, 2 * v) for n, v in step])
+    md = rps.counters(str(tmp_path / "f"), str(tmp_path / "w"),
+                      ["dispatch=permute_rows16", "second=mx_quant_cols_bf16<true>#1/2"],
+                      1024 * 1024, "t", "cf", "cw")
+    rows = {l.split("|")[1].strip(): l.split("|") for l in md.splitlines() if l.startswith("| d") or l.startswith("| s")}
+    # FETCH: the copy of 1 MiB reads 512 KiB -> x2; WRITE: 1 MiB -> x1
+    assert float(rows["dispatch"][4]) == pytest.approx(100 * 1024 * 2)
+    assert float(rows["dispatch"][5]) == pytest.approx(200 * 1024)
+    assert float(rows["second"][4]) == pytest.approx(20 * 1024 * 2)
+    assert f"row_source_hash = {rps.source_hash(rps.ROW_SOURCES)}" in md
+
+
+def test_committed_row_mover_tables_name_their_sources():
+    prof = os.path.join(ROOT, "profiles")
+    files = [f for f in os.listdir(prof) if f.endswith("_counters.md") and f.startswith("row_movers")]
+    assert len(files) == 2
+    for f in files:
+        lines = [l for l in open(os.path.join(prof, f)) if l.startswith("row_source_hash = ")]
+        assert len(lines) == 1 and len(lines[0].split("=")[1].strip()) == 16, f
