@@ -614,9 +614,11 @@ def padded_baseline(moe, torch, inp, w, steps, warmup, ms_dropless, capacity=Non
 
 
 def sample_sclk(torch, run_step, seconds: float = 0.6):
-    """The GPU's graphics clock (MHz) sampled every 10 ms while the step runs
-    back to back, from amd-smi; the GPU with the most graphics activity
-    meanwhile is the one reported. None if amd-smi is not usable."""
+    """The GPU's graphics clock (MHz) and socket power (W) sampled every 10 ms
+    while the step runs back to back, from amd-smi; the GPU with the most
+    graphics activity meanwhile is the one reported, with its power cap (the
+    row GEMMs run at it, which is what holds the clock below 2.4 GHz). None
+    if amd-smi is not usable."""
     try:
         import threading
         import amdsmi
@@ -630,6 +632,7 @@ def sample_sclk(torch, run_step, seconds: float = 0.6):
         handles = amdsmi.amdsmi_get_processor_handles()
         clk = {i: [] for i in range(len(handles))}
         act = {i: [] for i in range(len(handles))}
+        pwr = {i: [] for i in range(len(handles))}
         stop = threading.Event()
 
         def poll():
@@ -640,8 +643,13 @@ def sample_sclk(torch, run_step, seconds: float = 0.6):
                         a = amdsmi.amdsmi_get_gpu_activity(hdl)["gfx_activity"]
                     except Exception:
                         continue
+                    try:
+                        p = amdsmi.amdsmi_get_power_info(hdl).get("current_socket_power")
+                    except Exception:
+                        p = None
                     clk[i].append(c)
                     act[i].append(a)
+                    pwr[i].append(p)
                 time.sleep(0.01)
 
         th = threading.Thread(target=poll, daemon=True)
@@ -658,14 +666,25 @@ def sample_sclk(torch, run_step, seconds: float = 0.6):
         i = max(busy, key=lambda j: sum(act[j]) / len(act[j]))
         # the samples taken while the graphics engine was busy (at least half
         # the highest activity read), so that gaps between steps do not count
-        pairs = [(c, a) for c, a in zip(clk[i], act[i])
-                 if isinstance(c, (int, float)) and isinstance(a, (int, float))]
-        top = max((a for _, a in pairs), default=0)
-        c = sorted(c for c, a in pairs if top > 0 and a >= top / 2)
+        num = (int, float)
+        trip = [(c, a, p) for c, a, p in zip(clk[i], act[i], pwr[i])
+                if isinstance(c, num) and isinstance(a, num)]
+        top = max((a for _, a, _ in trip), default=0)
+        busy_s = [(c, p) for c, a, p in trip if top > 0 and a >= top / 2]
+        c = sorted(c for c, _ in busy_s)
         if not c:
             return None
-        return {"median_mhz": c[len(c) // 2], "min_mhz": c[0], "max_mhz": c[-1], "samples": len(c),
-                "all_samples": len(pairs), "spec_mhz": 2400}
+        res = {"median_mhz": c[len(c) // 2], "min_mhz": c[0], "max_mhz": c[-1], "samples": len(c),
+               "all_samples": len(trip), "spec_mhz": 2400}
+        p = sorted(p for _, p in busy_s if isinstance(p, num))
+        if p:
+            res.update(power_median_w=p[len(p) // 2], power_max_w=p[-1])
+            try:
+                cap = amdsmi.amdsmi_get_power_cap_info(handles[i])["power_cap"]
+                res["power_cap_w"] = cap / 1e6 if cap > 1e5 else cap   # reported in uW
+            except Exception:
+                pass
+        return res
     except Exception:
         return None
     finally:
