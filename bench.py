@@ -19,9 +19,11 @@ Besides the layer throughput the line carries:
   roofline     -- the role that takes the most time per launch (the dominant
                   kernel) against the roof that binds it;
   workloads    -- the other layer configurations (E=8 forward and the
-                  8 -> 128 expert per-token cost; Zipf-skewed routing against
-                  the padded-capacity layout; MXFP8 against bf16 on the same
-                  seed), each timed the same way after the main region;
+                  8 -> 128 expert per-token cost; one GPU's 16-expert share
+                  of the E=128 layer under an 8-way expert split; Zipf-skewed
+                  routing against the padded-capacity layout; MXFP8 against
+                  bf16 on the same seed), each timed the same way after the
+                  main region;
   cpu_baseline -- the CPU oracle (plain loops, fp64) on the host cores, on a
                   bounded sample: the same layer on the first few thousand
                   tokens of the workload (all experts), in tokens/s.
@@ -395,7 +397,7 @@ def main():
         del layer
         inp = None
         torch.cuda.empty_cache()
-        res["workloads"] = other_workloads(moe, torch, synth, a, fwd_us_e128)
+        res["workloads"] = other_workloads(moe, torch, synth, a, fwd_us_e128, ms)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(synth.device_inputs(w, seed=a.seed, with_dout=w.backward)
                                            if inp is None else inp, w, a.cpu_tokens)
@@ -406,7 +408,7 @@ def main():
 # the other configurations, timed like the main step after the main region
 
 
-def other_workloads(moe, torch, synth, a, fwd_us_e128):
+def other_workloads(moe, torch, synth, a, fwd_us_e128, ms_e128):
     out = {}
     # E=8 forward: the same d, h and k as the headline with 8 instead of 128
     # experts (the pages' expert-pool scaling: 8 -> 128 experts at top-4 cost
@@ -420,6 +422,18 @@ def other_workloads(moe, torch, synth, a, fwd_us_e128):
     e128 = fwd_us_e128 / synth.WORKLOADS["e128_bf16"].T
     out["expert_scaling"] = {"fwd_us_per_token_e8": e8, "fwd_us_per_token_e128": e128,
                              "e128_throughput_over_e8": e8 / e128}
+    del inp
+    torch.cuda.empty_cache()
+
+    # one GPU's share of the E=128 layer under an 8-way expert split: 16
+    # experts x ~512 rows, the per-GPU grouped GEMM work of that layout (the
+    # row exchange between GPUs is not part of a one-GPU run)
+    we = synth.WORKLOADS["e16_bf16_ep_share"]
+    inp = synth.device_inputs(we, seed=a.seed)
+    print(f"[bench] {we.name}", file=sys.stderr, flush=True)
+    _, ms, st = run_layer(moe, torch, we, inp, a.steps, a.warmup)
+    out[we.name] = workload_summary(we, ms, st)
+    out[we.name]["us_per_token_over_e128"] = (ms / we.T) / (ms_e128 / synth.WORKLOADS["e128_bf16"].T)
     del inp
     torch.cuda.empty_cache()
 

@@ -63,6 +63,11 @@ WORKLOADS = {
     "e128_bf16_zipf": Workload("e128_bf16_zipf", 16384, 2048, 128, 4, 1024, "bf16", 1.0, 1.0,
                                0.02, zipf_s=1.2),
     "e128_mxfp8": Workload("e128_mxfp8", 32768, 4096, 128, 4, 2048, "mxfp8", 1.0, 1.0, 0.02),
+    # one GPU's share of the E=128 fwd+bwd layer if its experts were spread
+    # over 8 GPUs: 16 experts with ~512 rows each (the same rows per expert,
+    # d, h and k; an eighth of the tokens)
+    "e16_bf16_ep_share": Workload("e16_bf16_ep_share", 2048, 2048, 16, 4, 1024, "bf16", 1.0,
+                                  1.0, 0.02),
 }
 
 

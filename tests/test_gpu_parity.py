@@ -59,7 +59,7 @@ def test_route_ties_and_signed_zero():
         _route_eq(g, oracle.route(rows, k, 7))
 
 
-@pytest.mark.parametrize("name", ["e128_bf16", "e128_bf16_zipf", "e8_bf16_fwd"])
+@pytest.mark.parametrize("name", ["e128_bf16", "e128_bf16_zipf", "e8_bf16_fwd", "e16_bf16_ep_share"])
 def test_route_full_size(name):
     w = synth.WORKLOADS[name]
     logits = synth.normal((w.T, w.E), 0, synth.STREAM_LOGITS, w.logit_scale)
@@ -446,7 +446,7 @@ def _sample_experts(counts, n_random, seed):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["e128_bf16", "e128_bf16_zipf", "e8_bf16_fwd"])
+@pytest.mark.parametrize("name", ["e128_bf16", "e128_bf16_zipf", "e8_bf16_fwd", "e16_bf16_ep_share"])
 def test_full_size_sampled(name):
     """The full-size workloads in the launch configuration the bench times:
     routing in full, 512 sampled tokens (out, dX, dlogits) and the weight
