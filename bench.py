@@ -45,8 +45,7 @@ PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 
 FWD_STAGES = {"bf16": ("route", "permute", "gemm1_swiglu", "gemm2", "combine"),
-              "mxfp8": ("quant_x", "route", "permute", "gemm1_swiglu", "quant_hp", "gemm2",
-                        "combine")}
+              "mxfp8": ("quant_x", "route", "permute", "gemm1_swiglu", "gemm2", "combine")}
 
 
 def parse():
@@ -99,15 +98,18 @@ def role_work(w) -> dict:
         "gemm1_wgrad": (4 * R * d * h, R * 2 * h * q + R * d * q + 8 * E * d * h),
     }
     if mx:
+        # GEMM1 stores A||B in bf16 and H' quantised in both layouts (GEMM2's
+        # operand and GEMM2 wgrad's), so no pass quantises H'
+        W["gemm1_swiglu"] = (4 * R * d * h,
+                             R * d * q + E * 2 * h * d * q + a * R * 2 * h + 2 * R * h * q)
         # the MXFP8 backward stores no dy_perm: the combine backward writes one
         # fp32 gate per routed row, and the dy quantiser reads the dOut rows
         # (each token's once at the least) and those gates
         W["combine_bwd"] = (0, a * T * d + a * R * d + 12 * T * k + 4 * R + 4 * T * E + 4 * T * k)
         W.update({
             "quant_x": (0, a * T * d + T * d * q),
-            # H' in both layouts from one read (GEMM2's operand and GEMM2
-            # wgrad's), so the backward's H' quantiser has no work
-            "quant_hp": (0, a * R * h + 2 * R * h * q),
+            # the backward's H' quantiser has no work: the layer holds GEMM1's
+            # column layout of H'
             "quant_dy_both": (0, a * T * d + 8 * R + 2 * R * d * q),     # + gates, row map
             "quant_hp_cols": (0, 0),
             "quant_dab_both": (0, a * R * 2 * h + 2 * R * 2 * h * q),
@@ -220,16 +222,17 @@ def run_layer(moe, torch, w, inp, steps, warmup, layer=None, flush=None):
             moe.moe_permute(layer.xq, r["token_pos"], layer.xpq, x_scale=layer.xs,
                             x_perm_scale=layer.xps)
             mark(3)
+            # H' leaves GEMM1 already quantised for GEMM2 and GEMM2's wgrad
             moe.moe_grouped_gemm(moe.MOE_GG_FWD, layer.xpq, layer.w1q, layer.ab, r["offsets"],
-                                 moe.MOE_EPI_SWIGLU_FWD, N=2 * h, K=d, aux_out=layer.hp,
-                                 a_scale=layer.xps, b_scale=layer.w1s, dtype=moe.MOE_MXFP8)
+                                 moe.MOE_EPI_SWIGLU_FWD, N=2 * h, K=d, aux_out=layer.hpq,
+                                 aux_out_scale=layer.hps, aux_out_cols=layer.hpc,
+                                 aux_out_cols_scale=layer.hpcs, a_scale=layer.xps,
+                                 b_scale=layer.w1s, dtype=moe.MOE_MXFP8)
             mark(4)
-            layer.quantize_hp(r["offsets"])
-            mark(5)
             moe.moe_grouped_gemm(moe.MOE_GG_FWD, layer.hpq, layer.w2q, layer.y_perm, r["offsets"],
                                  N=d, K=h, a_scale=layer.hps, b_scale=layer.w2s,
                                  dtype=moe.MOE_MXFP8)
-            mark(6)
+            mark(5)
         else:
             layer._alloc(T, x.device, x.dtype)
             layer.x = x

@@ -74,7 +74,9 @@ const char *moe_status_str(moe_status s);
 
 /* ABI version of this header (major * 100 + minor). 101: moe_bwd_desc ends
  * with hp_cols, hp_cols_scale (zero them when unused), and the MXFP8
- * backward uses dy_perm as scratch. */
+ * backward uses dy_perm as scratch. 102: moe_gemm_desc ends with
+ * aux_out_cols, aux_out_cols_scale, and aux_out_scale selects the MXFP8
+ * SwiGLU forward that stores H' quantised (zero all three when unused). */
 int32_t moe_version(void);
 
 /* ------------------------------------------------------------------ */
@@ -202,7 +204,24 @@ enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU_FWD = 1, MOE_EPI_SWIGLU_BWD = 2 };
  *     used scale byte, into the spare blocks). rows <= 2^24 (MOE_ERR_SHAPE
  *     otherwise): the kernel addresses the 256 rows of a B tile in one
  *     group's column block with 32-bit offsets from one base.
- * (aux_out_scale is reserved and must be null.)
+ * epilogue MOE_EPI_SWIGLU_FWD with dtype MOE_MXFP8 and aux_out_scale set: H'
+ *   is not stored in bf16 but handed to GEMM2 and to GEMM2's weight
+ *   gradient already quantised, in the two layouts mxfp8_quantize_both
+ *   writes for it (groups = offsets), from the bf16-rounded values the plain
+ *   epilogue would store (the same bytes, padding rows of the column layout
+ *   written as zeros):
+ *     aux_out            E4M3 [rows, h], blocks of 32 along h (axis 1),
+ *     aux_out_scale      E8M0 [rows, h/32],
+ *     aux_out_cols       E4M3 column-block layout along the rows of each
+ *                        group (axis 0), sized by mxfp8_col_blocks(rows, E),
+ *     aux_out_cols_scale its E8M0 scales.
+ *   All four must be set (aux_out and aux_out_cols 16-byte aligned, the
+ *   scales 4-byte aligned) or aux_out_scale null. MXFP8 quantisation of a GEMM input along its own
+ *   reduction axis is the pages' recipe (aikraft.ru, technical
+ *   optimisations: MXFP8 with 32-element scales); doing it in the producing
+ *   GEMM saves the bf16 H' round trip through HBM.
+ * aux_out_cols and aux_out_cols_scale are ignored unless aux_out_scale is
+ * set; aux_out_scale must be null for every other epilogue and dtype.
  */
 typedef struct moe_gemm_desc {
     int32_t mode;          /* MOE_GG_* */
@@ -219,10 +238,12 @@ typedef struct moe_gemm_desc {
     const uint8_t *b_scale;  /* MXFP8 */
     const void *aux;         /* SWIGLU_BWD: AB [rows, 2h] */
     void *aux_out;           /* SWIGLU_FWD: H' [rows, h] */
-    uint8_t *aux_out_scale;  /* SWIGLU_FWD with MXFP8: H' scales */
+    uint8_t *aux_out_scale;  /* SWIGLU_FWD with MXFP8: H' quantised along h, scales */
     void *ws;                /* scratch (split-K partials); may be null if ws_bytes = 0 */
     size_t ws_bytes;
     int32_t accumulate;      /* WGRAD only: 1 = C[g] += the product (fp32 add), 0 = overwrite */
+    uint8_t *aux_out_cols;        /* SWIGLU_FWD with MXFP8 and aux_out_scale: H' along rows */
+    uint8_t *aux_out_cols_scale;  /* ... and its scales */
 } moe_gemm_desc;
 
 /* Scratch bytes moe_grouped_gemm needs for this descriptor (0 when none). */

@@ -44,7 +44,8 @@ class GemmDesc(ctypes.Structure):
                 ("rows", _I64), ("M", _I32), ("N", _I32), ("K", _I32),
                 ("offsets", _P), ("A", _P), ("B", _P), ("C", _P), ("a_scale", _P),
                 ("b_scale", _P), ("aux", _P), ("aux_out", _P), ("aux_out_scale", _P),
-                ("ws", _P), ("ws_bytes", _SZ), ("accumulate", _I32)]
+                ("ws", _P), ("ws_bytes", _SZ), ("accumulate", _I32), ("aux_out_cols", _P),
+                ("aux_out_cols_scale", _P)]
 
 
 class BwdDesc(ctypes.Structure):
@@ -273,12 +274,16 @@ _TORCH_DT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_MXFP8: torch.
 
 
 def _check_gemm_operands(mode, dt, epilogue, A, B, C, offsets, rows, M, N, K, aux, aux_out,
-                         a_scale, b_scale):
+                         a_scale, b_scale, aux_out_scale=None, aux_out_cols=None,
+                         aux_out_cols_scale=None):
     """Host-side sizes of every operand against what the mode reads and
     writes (the C ABI sees only pointers, so an undersized tensor would be
     read or written past its end on the device)."""
     E = offsets.numel() - 1
     _need_elems(offsets, E + 1, torch.int32, "offsets")
+    hp_quantised = aux_out_scale is not None
+    if hp_quantised and (dt != MOE_MXFP8 or epilogue != MOE_EPI_SWIGLU_FWD):
+        raise ValueError("aux_out_scale: only the MXFP8 SwiGLU forward stores H' quantised")
     if offsets.device != A.device:
         raise ValueError("offsets must be on A's device")
     et = _TORCH_DT[dt]
@@ -306,7 +311,15 @@ def _check_gemm_operands(mode, dt, epilogue, A, B, C, offsets, rows, M, N, K, au
     else:
         _need_elems(C, rows * N, act, "C")
     if epilogue == MOE_EPI_SWIGLU_FWD:
-        _need_elems(aux_out, rows * (N // 2), act, "aux_out")
+        if hp_quantised:
+            # H' stored as MXFP8 in both layouts instead of bf16
+            h, nb = N // 2, mxfp8_col_blocks(rows, E)
+            _need_elems(aux_out, rows * h, torch.uint8, "aux_out")
+            _need_elems(aux_out_scale, rows * (h // 32), torch.uint8, "aux_out_scale")
+            _need_elems(aux_out_cols, nb * 32 * h, torch.uint8, "aux_out_cols")
+            _need_elems(aux_out_cols_scale, nb * h, torch.uint8, "aux_out_cols_scale")
+        else:
+            _need_elems(aux_out, rows * (N // 2), act, "aux_out")
 
 
 def moe_grouped_gemm(mode: int, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
@@ -314,11 +327,15 @@ def moe_grouped_gemm(mode: int, A: torch.Tensor, B: torch.Tensor, C: torch.Tenso
                      K: int = 0, aux: torch.Tensor | None = None,
                      aux_out: torch.Tensor | None = None, a_scale=None, b_scale=None,
                      aux_out_scale=None, dtype: int | None = None, accumulate: bool = False,
-                     rows: int | None = None):
+                     rows: int | None = None, aux_out_cols=None, aux_out_cols_scale=None):
     """One grouped GEMM (see moe.h for the modes and epilogues). Every
     operand's dtype and size is checked against the mode before the call.
     rows = total routed rows (offsets[-1]); it defaults to A.shape[0] and must
-    be given for MXFP8 WGRAD, whose operands are flat column-block arrays."""
+    be given for MXFP8 WGRAD, whose operands are flat column-block arrays.
+    MXFP8 SwiGLU forward with aux_out_scale: H' is stored quantised, along h
+    into aux_out (uint8 [rows, h]) and aux_out_scale, and along the rows of
+    each group into aux_out_cols / aux_out_cols_scale (the layouts
+    mxfp8_quantize_both writes)."""
     dt = _dt(A) if dtype is None else dtype
     if dt not in _TORCH_DT:
         raise ValueError(f"unsupported GEMM dtype {dt}")
@@ -327,7 +344,7 @@ def moe_grouped_gemm(mode: int, A: torch.Tensor, B: torch.Tensor, C: torch.Tenso
             raise ValueError("MXFP8 WGRAD: pass rows (the column-block operands are flat)")
         rows = A.shape[0]
     _check_gemm_operands(mode, dt, epilogue, A, B, C, offsets, rows, M, N, K, aux, aux_out,
-                         a_scale, b_scale)
+                         a_scale, b_scale, aux_out_scale, aux_out_cols, aux_out_cols_scale)
     desc = GemmDesc()
     desc.accumulate = 1 if accumulate else 0
     desc.mode = mode
@@ -343,6 +360,9 @@ def moe_grouped_gemm(mode: int, A: torch.Tensor, B: torch.Tensor, C: torch.Tenso
     desc.aux = aux.data_ptr() if aux is not None else None
     desc.aux_out = aux_out.data_ptr() if aux_out is not None else None
     desc.aux_out_scale = aux_out_scale.data_ptr() if aux_out_scale is not None else None
+    desc.aux_out_cols = aux_out_cols.data_ptr() if aux_out_cols is not None else None
+    desc.aux_out_cols_scale = (aux_out_cols_scale.data_ptr() if aux_out_cols_scale is not None
+                               else None)
     wsb = int(_lib.moe_grouped_gemm_workspace_size(ctypes.byref(desc)))
     ws = torch.empty(wsb, dtype=torch.uint8, device=A.device) if wsb else None
     desc.ws = ws.data_ptr() if ws is not None else None
@@ -780,9 +800,12 @@ class MoELayerMX:
     (`prepare_weights`), in both orientations: along d / h for the forward
     GEMMs and, per expert, along 2h / d for the backward dgrads. The forward
     quantises x along d before dispatch, so the row-wise dispatch moves E4M3
-    bytes plus their scales; GEMM1 writes AB and H' in bf16, H' is quantised
-    along h for GEMM2, and y, out stay bf16. The backward (moe_backward with
-    MXFP8) quantises its own GEMM operands."""
+    bytes plus their scales; GEMM1 writes AB in bf16 and H' already
+    quantised, along h for GEMM2 and along rows per expert for GEMM2's weight
+    gradient (fuse_hp; with fuse_hp = False or when recomputing, GEMM1 writes
+    bf16 H' and a separate pass quantises it: the same bytes); y and out stay
+    bf16. The backward (moe_backward with MXFP8) quantises its own GEMM
+    operands."""
 
     def __init__(self, w1_master: torch.Tensor, w2_master: torch.Tensor, k: int,
                  recompute: bool = False, aux_alpha: float | None = None):
@@ -790,6 +813,7 @@ class MoELayerMX:
         self.h = h2 // 2
         self.k = k
         self.recompute = recompute
+        self.fuse_hp = True
         self.balance = _Balance(aux_alpha) if aux_alpha is not None else None
         self.lb_stats = None
         self.prepare_weights(w1_master, w2_master)
@@ -846,14 +870,22 @@ class MoELayerMX:
         self.bwd_ws = None
         self._T = key
 
-    def _gemm1(self, x, offsets, token_pos):
+    def hp_quantised_in_gemm1(self) -> bool:
+        """GEMM1 stores H' in both MXFP8 layouts (the forward of a layer that
+        holds H' for its backward)."""
+        return self.fuse_hp and not self.recompute
+
+    def _gemm1(self, x, offsets, token_pos, quantised_hp: bool = False):
         """Quantised dispatch of x and GEMM1 + SwiGLU (forward, and again in
-        the backward when recomputing)."""
+        the backward when recomputing). quantised_hp: H' goes straight to its
+        two MXFP8 layouts instead of bf16."""
         mxfp8_quantize(x, 1, q=self.xq, scale=self.xs)
         moe_permute(self.xq, token_pos, self.xpq, x_scale=self.xs, x_perm_scale=self.xps)
+        hp = (dict(aux_out=self.hpq, aux_out_scale=self.hps, aux_out_cols=self.hpc,
+                   aux_out_cols_scale=self.hpcs) if quantised_hp else dict(aux_out=self.hp))
         moe_grouped_gemm(MOE_GG_FWD, self.xpq, self.w1q, self.ab, offsets, MOE_EPI_SWIGLU_FWD,
-                         N=2 * self.h, K=self.d, aux_out=self.hp, a_scale=self.xps,
-                         b_scale=self.w1s, dtype=MOE_MXFP8)
+                         N=2 * self.h, K=self.d, a_scale=self.xps, b_scale=self.w1s,
+                         dtype=MOE_MXFP8, **hp)
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor) -> torch.Tensor:
         if x.dim() != 2 or x.shape[1] != self.d or x.dtype != torch.bfloat16:
@@ -869,8 +901,10 @@ class MoELayerMX:
         r = moe_route(logits, self.k, out=self.route, ws=self.route_ws)
         if self.balance is not None:
             self.lb_stats = self.balance.forward(logits, r["counts"], self.k)
-        self._gemm1(x, r["offsets"], r["token_pos"])
-        self.quantize_hp(r["offsets"])
+        fused = self.hp_quantised_in_gemm1()
+        self._gemm1(x, r["offsets"], r["token_pos"], quantised_hp=fused)
+        if not fused:
+            self.quantize_hp(r["offsets"])
         moe_grouped_gemm(MOE_GG_FWD, self.hpq, self.w2q, self.y_perm, r["offsets"], N=d, K=h,
                          a_scale=self.hps, b_scale=self.w2s, dtype=MOE_MXFP8)
         moe_combine(self.y_perm, r["topk_gate"], r["token_pos"], self.out)

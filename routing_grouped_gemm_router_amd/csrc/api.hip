@@ -123,7 +123,7 @@ const char *moe_status_str(moe_status s) {
     }
 }
 
-int32_t moe_version(void) { return 101; }
+int32_t moe_version(void) { return 102; }
 
 size_t moe_route_workspace_size(int64_t T, int32_t E, int32_t k) {
     (void)k;
@@ -195,8 +195,10 @@ static moe_status check_gemm_shape(const moe_gemm_desc *g) {
     if (!g) return MOE_ERR_NULL;
     if (g->mode < MOE_GG_FWD || g->mode > MOE_GG_WGRAD) return MOE_ERR_DTYPE;
     if (g->dtype != MOE_F32 && g->dtype != MOE_BF16 && g->dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+    // H' stored quantised: the MXFP8 SwiGLU forward only
+    if (g->aux_out_scale && (g->dtype != MOE_MXFP8 || g->epilogue != MOE_EPI_SWIGLU_FWD))
+        return MOE_ERR_DTYPE;
     if (g->dtype == MOE_MXFP8) {
-        if (g->aux_out_scale) return MOE_ERR_DTYPE;
         if (g->mode != MOE_GG_WGRAD && g->K % 128) return MOE_ERR_SHAPE;
         // WGRAD: the 256 rows of a B tile in a group's column block (pitch:
         // the group's rows rounded up to 128 bytes) are addressed with 32-bit
@@ -233,6 +235,12 @@ static moe_status check_gemm(const moe_gemm_desc *g) {
     if (rows_needed && !g->A) return MOE_ERR_NULL;
     if ((rows_needed || g->mode == MOE_GG_WGRAD) && !g->C) return MOE_ERR_NULL;
     if (rows_needed && g->epilogue == MOE_EPI_SWIGLU_FWD && !g->aux_out) return MOE_ERR_NULL;
+    if (rows_needed && g->aux_out_scale && (!g->aux_out_cols || !g->aux_out_cols_scale))
+        return MOE_ERR_NULL;
+    if (g->aux_out_scale && (!aligned4(g->aux_out_scale) ||
+                             (g->aux_out_cols && !aligned16(g->aux_out_cols)) ||
+                             (g->aux_out_cols_scale && !aligned4(g->aux_out_cols_scale))))
+        return MOE_ERR_ALIGN;
     if (rows_needed && g->epilogue == MOE_EPI_SWIGLU_BWD && !g->aux) return MOE_ERR_NULL;
     if ((g->A && !aligned16(g->A)) || !aligned16(g->B) || (g->C && !aligned16(g->C)))
         return MOE_ERR_ALIGN;

@@ -47,6 +47,8 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7 - i within each 8 lanes
 constexpr int kDppRowShl4 = 0x104;    // lane i <- lane i + 4 within each 16 lanes (others keep 0)
 constexpr int kDppRowShl8 = 0x108;    // lane i <- lane i + 8 within each 16 lanes (others keep 0)
+constexpr int kDppRowRor4 = 0x124;    // each 16 lanes rotated by 4 (row_ror:4)
+constexpr int kDppRowRor8 = 0x128;    // each 16 lanes rotated by 8 (row_ror:8)
 template <int CTRL>
 MOE_DEV int dpp_move(int v) {
     return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
@@ -54,6 +56,21 @@ MOE_DEV int dpp_move(int v) {
 template <int CTRL>
 MOE_DEV float dpp_move(float v) {
     return __int_as_float(dpp_move<CTRL>(__float_as_int(v)));
+}
+
+// max of v over lanes i and i ^ 16 (within each 32 lanes) and over lanes i
+// and i ^ 32: v_permlane16_swap / v_permlane32_swap exchange the odd 16-lane
+// (32-lane) rows of one operand with the even rows of the other, so with v as
+// both operands the two results hold v and its partner lane's v (VALU, no LDS)
+MOE_DEV float max_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+MOE_DEV float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }

@@ -34,6 +34,10 @@ struct GemmArgs {
     int E;
     int h;          // hidden width (SwiGLU epilogues)
     int accumulate; // WGRAD: add to C instead of overwriting it
+    // MXFP8 SwiGLU forward with H' stored quantised (aux_out: its E4M3 rows)
+    uint8_t *aux_out_scale;
+    uint8_t *aux_out_cols;
+    uint8_t *aux_out_cols_scale;
 };
 
 // K-layout LDS tile: [R rows][128 bytes]. LDS has 64 4-byte banks, i.e. two

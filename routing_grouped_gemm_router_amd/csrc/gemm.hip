@@ -43,6 +43,7 @@
 
 #include "common.h"
 #include "copy_plan.h"
+#include "mx_encode.h"
 
 namespace moe {
 
@@ -1330,6 +1331,117 @@ void gg_ws(GemmArgs g) {
     // of the wave's (i, j) 32x32 block
     const int col_l = lane & 31;
     auto row_in = [&](int i, int v) { return wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3); };
+    // MXFP8 SwiGLU forward with H' stored quantised: A||B in bf16 as in the
+    // plain epilogue; H' rounded to bf16 as that epilogue would store it, then
+    // encoded in both MXFP8 layouts (the bytes the both-layout quantiser
+    // writes for those values). A wave holds 64 rows x 32 hidden units: one
+    // 32-element block of each row (h and the wave's first unit are
+    // multiples of 32) and, per 32-row half i, one 32-row block of each
+    // unit's column (the tile's rows start a 128-row unit of the group).
+    auto swiglu_fwd_mx = [&](const TileC &t, int r0, int j0) {
+      if constexpr (FP8 && EPI == MOE_EPI_SWIGLU_FWD) {
+        static_assert(TN == 2 && TM == 2, "one hidden-unit block and two 32-row blocks per wave");
+        const int h = g.h;
+        if (j0 >= h) return;                        // wave-uniform: no unit in range
+        uint16_t *AB = reinterpret_cast<uint16_t *>(g.C);
+        uint8_t *q1 = reinterpret_cast<uint8_t *>(g.aux_out);
+        const int e = t.e;
+        // the group's blocks [bb, bb + nb) of the column-block layout
+        const int64_t bb = 4 * (int64_t)s_tile[e], nb = 4 * (int64_t)(s_tile[e + 1] - s_tile[e]);
+        const int c = j0 + col_l;
+        uint8_t *q0c = g.aux_out_cols + bb * 32 * h + (int64_t)c * nb * 32;
+        uint8_t *s0c = g.aux_out_cols_scale + bb * h + (int64_t)c * nb;
+        const int half = lane >> 5, qd = (lane & 31) >> 2, rq = lane & 3;
+        const int lrow0 = r0 - s_off[e];            // within the group; a multiple of 64
+        const bool rows_full = wave_full(r0 + WTM <= t.row_end);
+        char *abw = wave_base(AB, r0, j0, 2 * h);
+        const uint32_t lab = lane_off<2>(lane, 2 * h);
+        // A||B stores and H' as the plain epilogue rounds it; rows past the
+        // group's end are the column layout's zero padding
+        float hq[TM][16];
+        bool nan = false;
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int ro = i * 32 + (v >> 2) * 8 + half * 4 + (v & 3);
+                const bool ok = rows_full || r0 + ro < t.row_end;
+                const float a = acc[i][0][v], b = acc[i][1][v];
+                if (ok) {
+                    char *abr = abw + (int64_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * 2 * h * 2;
+                    *reinterpret_cast<uint16_t *>(abr + lab) = f32_to_bf16(a);
+                    *reinterpret_cast<uint16_t *>(abr + (int64_t)h * 2 + lab) = f32_to_bf16(b);
+                }
+                hq[i][v] = ok ? bf16_to_f32(f32_to_bf16(silu_f(a) * b)) : 0.f;
+                nan |= __builtin_isnan(hq[i][v]);
+            }
+        // one encoder form for the whole tile (the same bytes either way)
+        const bool finite = __ballot(nan) == 0;
+        auto enc = [&](float x0, float x1, float x2, float x3, uint32_t sb) {
+            return finite ? e4m3x4_finite(x0, x1, x2, x3, sb) : e4m3x4_select(x0, x1, x2, x3, sb);
+        };
+        // column layout: the lane's unit, rows i*32 .. i*32+31 of the wave
+        // (16 in the lane, 16 in lane ^ 32: rows gq*8 + half*4 + 0..3). Two
+        // 32-lane swaps hand the lower half of the block's rows to half 0 and
+        // the upper half to half 1, so each lane stores 16 contiguous bytes.
+#pragma unroll
+        for (int i = 0; i < TM; i++) {
+            float am = 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; v++) am = fmaxf(am, fabsf(hq[i][v]));
+            const uint32_t sbc = mx_scale_byte(max_xor32(am));
+            uint32_t w[4];
+#pragma unroll
+            for (int gq = 0; gq < 4; gq++)
+                w[gq] = enc(hq[i][4 * gq], hq[i][4 * gq + 1], hq[i][4 * gq + 2], hq[i][4 * gq + 3], sbc);
+            // half 0 sends rows 16..19, 24..27 and receives 4..7, 12..15; half 1
+            // the other way round
+            uint32_t got[2];
+#pragma unroll
+            for (int m = 0; m < 2; m++) {
+                const uint32_t send = half ? w[m] : w[m + 2];
+                const auto r = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+                got[m] = half ? r[0] : r[1];
+            }
+            const uint4 out = half ? make_uint4(got[0], w[2], got[1], w[3])
+                                   : make_uint4(w[0], got[0], w[1], got[1]);
+            const int lr = lrow0 + i * 32;
+            *reinterpret_cast<uint4 *>(q0c + lr + half * 16) = out;
+            if (half == 0) s0c[lr >> 5] = (uint8_t)sbc;
+        }
+        // row layout: a 4 x 4 transpose inside each quad of lanes gives lane
+        // 4 qd + rq the units 4 qd .. 4 qd + 3 of row i*32 + gq*8 + half*4 + rq;
+        // that row's block is the lanes qd = 0..7 with the same rq
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int gq = 0; gq < 4; gq++) {
+                float x[4] = {hq[i][4 * gq], hq[i][4 * gq + 1], hq[i][4 * gq + 2], hq[i][4 * gq + 3]};
+                float p[4];
+#pragma unroll
+                for (int k = 0; k < 4; k++) p[k] = dpp_move<kDppXor2>(x[k ^ 2]);
+#pragma unroll
+                for (int k = 0; k < 4; k++)
+                    if (((k >> 1) & 1) != ((rq >> 1) & 1)) x[k] = p[k];
+#pragma unroll
+                for (int k = 0; k < 4; k++) p[k] = dpp_move<kDppXor1>(x[k ^ 1]);
+#pragma unroll
+                for (int k = 0; k < 4; k++)
+                    if ((k & 1) != (rq & 1)) x[k] = p[k];
+                float amr = fmaxf(fmaxf(fmaxf(0.f, fabsf(x[0])), fabsf(x[1])),
+                                  fmaxf(fabsf(x[2]), fabsf(x[3])));
+                amr = fmaxf(amr, dpp_move<kDppRowRor4>(amr));
+                amr = fmaxf(amr, dpp_move<kDppRowRor8>(amr));
+                const uint32_t sbr = mx_scale_byte(max_xor16(amr));
+                const uint32_t w = enc(x[0], x[1], x[2], x[3], sbr);
+                const int ro = i * 32 + gq * 8 + half * 4 + rq;
+                if (rows_full || r0 + ro < t.row_end) {
+                    *reinterpret_cast<uint32_t *>(q1 + (int64_t)(r0 + ro) * h + j0 + 4 * qd) = w;
+                    if (qd == 0) g.aux_out_scale[(int64_t)(r0 + ro) * (h >> 5) + (j0 >> 5)] = (uint8_t)sbr;
+                }
+            }
+      }
+    };
     auto epilogue = [&](const TileC &t) {
         if constexpr (MODE == MOE_GG_WGRAD) {
             float *C = reinterpret_cast<float *>(g.C) + (int64_t)t.e * g.M * g.N;
@@ -1377,6 +1489,12 @@ void gg_ws(GemmArgs g) {
             uint16_t *HP = reinterpret_cast<uint16_t *>(g.aux_out);
             const int h = g.h;
             const int r0 = t.row0 + wm * WTM, j0 = t.nt * (BN / 2) + wn * (WTN / 2);
+            if constexpr (FP8) {
+                if (g.aux_out_scale != nullptr) {       // uniform: a kernel argument
+                    swiglu_fwd_mx(t, r0, j0);
+                    return;
+                }
+            }
             if (wave_full(r0 + WTM <= t.row_end && j0 + WTN / 2 <= h)) {
                 // the wave's rows and hidden units are all in range
                 char *abw = wave_base(AB, r0, j0, 2 * h);
@@ -1804,6 +1922,11 @@ moe_status gemm_launch(const moe_gemm_desc *d, hipStream_t s) {
     a.E = d->n_groups;
     a.h = d->epilogue == MOE_EPI_SWIGLU_FWD ? d->N / 2 : d->N;
     a.accumulate = d->accumulate;
+    a.aux_out_scale = d->aux_out_scale;
+    a.aux_out_cols = d->aux_out_cols;
+    a.aux_out_cols_scale = d->aux_out_cols_scale;
+    // the comparison build's gg_mfma has no quantising SwiGLU epilogue
+    if (MOE_GG_MFMA_ALL && d->aux_out_scale) return MOE_ERR_DTYPE;
 #define GO(MODE, EPI)                                                          \
     (d->dtype == MOE_BF16    ? launch_mfma<MODE, EPI, false>(a, s)             \
      : d->dtype == MOE_MXFP8 ? launch_mfma<MODE, EPI, true>(a, s)              \

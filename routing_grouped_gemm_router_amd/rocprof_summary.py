@@ -35,10 +35,11 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 # the sources that make up the grouped GEMM kernel
-GEMM_SOURCES = ("csrc/gemm.hip", "csrc/copy_plan.h", "csrc/common.h", "../include/moe.h")
+GEMM_SOURCES = ("csrc/gemm.hip", "csrc/copy_plan.h", "csrc/common.h", "csrc/mx_encode.h",
+                "../include/moe.h")
 # the sources of the row movers, the routing kernels and the MXFP8 quantisers
 ROW_SOURCES = ("csrc/rows.hip", "csrc/route.hip", "csrc/mxfp8.hip", "csrc/common.h",
-               "../include/moe.h")
+               "csrc/mx_encode.h", "../include/moe.h")
 
 
 def source_hash(sources) -> str:

@@ -50,7 +50,7 @@ def test_status_strings(lib):
     for s in range(7):
         assert lib.moe_status_str(s).startswith(b"MOE_")
     lib.moe_version.restype = ctypes.c_int32
-    assert lib.moe_version() == 101
+    assert lib.moe_version() == 102
 
 
 def test_validation_without_gpu(lib):
@@ -141,8 +141,17 @@ def test_mxfp8_gemm_validation(lib):
     bad.a_scale = 0x100002                                           # scale words 4-byte aligned
     assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 4
     bad = GemmDesc.from_buffer_copy(g)
-    bad.aux_out_scale = 0x100000                                     # reserved
+    bad.aux_out_scale = 0x100000                     # H' quantised: SwiGLU forward only
     assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 3
+    sw = GemmDesc.from_buffer_copy(g)
+    sw.epilogue, sw.aux_out, sw.aux_out_scale = 1, 0x100000, 0x100000
+    assert lib.moe_grouped_gemm(ctypes.byref(sw), None) == 1         # column layout missing
+    sw.aux_out_cols = 0x100000
+    assert lib.moe_grouped_gemm(ctypes.byref(sw), None) == 1         # ... and its scales
+    sw.aux_out_cols_scale = 0x100002
+    assert lib.moe_grouped_gemm(ctypes.byref(sw), None) == 4         # 4-byte aligned
+    sw.dtype = 1
+    assert lib.moe_grouped_gemm(ctypes.byref(sw), None) == 3         # bf16 stores bf16 H'
     bad = GemmDesc.from_buffer_copy(g)
     bad.mode, bad.M, bad.N, bad.rows = 2, 64, 64, (1 << 24) + 1      # WGRAD column blocks:
     assert lib.moe_grouped_gemm(ctypes.byref(bad), None) == 2        # 32-bit row offsets

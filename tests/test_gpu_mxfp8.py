@@ -420,7 +420,8 @@ def test_mxfp8_backward_forms_dy_bit_exact():
     and each routed row's gate, without storing it. Its dAB and dW2 must equal,
     bit for bit, the same MXFP8 GEMMs run on dy_perm as the bf16 combine
     backward stores it (bf16 layer on the same routing and dOut), quantised
-    by mxfp8_quantize_both, with the MXFP8 layer's own saved a, b and H'."""
+    by mxfp8_quantize_both, with the MXFP8 layer's own saved a, b and H'
+    (the column layout of H' that its GEMM1 stored)."""
     T, d, E, k, h = 300, 256, 8, 2, 128
     inp = _mx_inputs(T, d, E, k, h, seed=11)
     inp["logits"][:, 1] -= 100.0                      # an empty expert
@@ -442,7 +443,7 @@ def test_mxfp8_backward_forms_dy_bit_exact():
                          dtype=moe.MOE_MXFP8)
     assert torch.equal(dab, g["dab"])
     # GEMM2 wgrad on the column layouts of dy and H'
-    hc, hcs = moe.mxfp8_quantize(layer.hp, 0, off)
+    hc, hcs = layer.hpc, layer.hpcs
     dw2 = torch.full((E, d, h), float("nan"), device="cuda")
     moe.moe_grouped_gemm(moe.MOE_GG_WGRAD, dyc, hc, dw2, off, M=d, N=h, a_scale=dycs,
                          b_scale=hcs, dtype=moe.MOE_MXFP8, rows=R)
@@ -459,10 +460,86 @@ def test_mxfp8_backward_with_forward_quantised_hp_bit_exact():
     inp = _mx_inputs(T, d, E, k, h, seed=12)
     inp["logits"][:, 1] -= 100.0                      # an empty expert
     layer, _, g = _run_mx(inp, k)
+    assert layer.saved().get("hp_cols") is not None and layer.saved()["hp"] is None
+    # the same forward again with H' stored in bf16 (and quantised by its own
+    # pass), for the backward that quantises bf16 H' itself
+    layer.fuse_hp = False
+    layer.forward(dev(inp["x"], torch.bfloat16), dev(inp["logits"], torch.float32))
     sv = layer.saved()
-    assert sv.get("hp_cols") is not None and sv["hp"] is None
-    sv.update(hp=layer.hp, hp_cols=None, hp_cols_scale=None)   # H' is still in the forward's buffer
+    sv.update(hp=layer.hp, hp_cols=None, hp_cols_scale=None)
     g2 = moe.moe_backward(sv, dev(inp["dout"], torch.bfloat16), E, k, d, h, mxfp8=True)
     torch.cuda.synchronize()
     for key in ("dx", "dlogits", "dw1", "dw2", "dab", "dx_perm", "dgate"):
+        assert torch.equal(g[key], g2[key]), key
+
+
+def _gemm1_mx_operands(T, d, E, k, h, seed, starve=()):
+    inp = _mx_inputs(T, d, E, k, h, seed)
+    for e in starve:
+        inp["logits"][:, e] -= 100.0                  # no rows for expert e
+    r = oracle.route(inp["logits"], k)
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    xq, xs = oracle.mxfp8_quantize(inp["x"][r["sorted_token"]], 1)
+    w1q, w1s = oracle.mxfp8_quantize(inp["w1"].reshape(E * 2 * h, d), 1)
+    return r, u8(xq), u8(xs), u8(w1q), u8(w1s), torch.from_numpy(r["offsets"]).cuda()
+
+
+# (T, d, E, k, h): an empty expert among ragged groups; h = 160, whose second
+# n-tile holds 32 hidden units (waves past h store nothing); groups of ~10
+# rows, where whole waves of a 128-row unit are column-layout padding; one
+# expert; the largest E
+@pytest.mark.parametrize("shape,starve", [((300, 256, 8, 2, 128), (1,)),
+                                          ((97, 128, 5, 3, 160), ()),
+                                          ((40, 128, 8, 2, 128), (0, 7)),
+                                          ((200, 128, 1, 1, 64), ()),
+                                          ((600, 128, 256, 4, 96), ())])
+def test_gemm1_quantised_hp_equals_quantiser(shape, starve):
+    """The MXFP8 SwiGLU forward that stores H' quantised writes A||B and both
+    MXFP8 layouts of H' byte for byte as the plain epilogue followed by the
+    both-layout quantiser on its bf16 H' (every byte of the output buffers,
+    pre-filled alike, so padding and untouched bytes are compared too)."""
+    T, d, E, k, h = shape
+    R = T * k
+    r, xq, xs, w1q, w1s, offd = _gemm1_mx_operands(T, d, E, k, h, seed=31, starve=starve)
+    assert all(r["counts"][e] == 0 for e in starve)
+    nb = moe.mxfp8_col_blocks(R, E)
+    bf = torch.bfloat16
+    kw = dict(N=2 * h, K=d, a_scale=xs, b_scale=w1s, dtype=moe.MOE_MXFP8)
+    ab_ref = torch.full((R, 2 * h), 3.0, dtype=bf, device="cuda")
+    hp = torch.empty((R, h), dtype=bf, device="cuda")
+    moe.moe_grouped_gemm(moe.MOE_GG_FWD, xq, w1q, ab_ref, offd, moe.MOE_EPI_SWIGLU_FWD,
+                         aux_out=hp, **kw)
+    fill = lambda *shape: torch.full(shape, 0x5A, dtype=torch.uint8, device="cuda")
+    ref = (fill(R, h), fill(R, h // 32), fill(nb * 32 * h), fill(nb * h))
+    moe.mxfp8_quantize_both(hp, offd, out=ref)
+    ab = torch.full((R, 2 * h), 3.0, dtype=bf, device="cuda")
+    got = (fill(R, h), fill(R, h // 32), fill(nb * 32 * h), fill(nb * h))
+    moe.moe_grouped_gemm(moe.MOE_GG_FWD, xq, w1q, ab, offd, moe.MOE_EPI_SWIGLU_FWD,
+                         aux_out=got[0], aux_out_scale=got[1], aux_out_cols=got[2],
+                         aux_out_cols_scale=got[3], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(ab, ab_ref)
+    for name, a, b in zip(("rows", "row scales", "cols", "col scales"), got, ref):
+        diff = torch.nonzero(a != b)
+        assert diff.numel() == 0, (name, diff[:8].flatten().tolist())
+
+
+# the layer needs h % 128 == 0 (GEMM2's MXFP8 reduction); groups of ~32 rows
+# leave whole waves of padding in each 128-row unit
+@pytest.mark.parametrize("shape", [(300, 256, 8, 2, 128), (130, 128, 16, 4, 256)])
+def test_mxfp8_layer_quantised_hp_matches_separate_pass(shape):
+    """The MXFP8 layer with H' quantised in GEMM1's epilogue gives the same
+    output and gradients, bit for bit, as with bf16 H' and a separate
+    quantiser pass."""
+    T, d, E, k, h = shape
+    inp = _mx_inputs(T, d, E, k, h, seed=17)
+    inp["logits"][:, 2] -= 100.0                      # an empty expert
+    layer, out, g = _run_mx(inp, k)
+    out, g = out.clone(), {key: v.clone() for key, v in g.items() if v is not None}
+    layer.fuse_hp = False
+    out2 = layer.forward(dev(inp["x"], torch.bfloat16), dev(inp["logits"], torch.float32))
+    g2 = layer.backward(dev(inp["dout"], torch.bfloat16))
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    for key in ("dx", "dlogits", "dw1", "dw2", "dgate"):
         assert torch.equal(g[key], g2[key]), key
