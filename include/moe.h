@@ -283,6 +283,21 @@ typedef struct moe_copy_walk {
 moe_status moe_gemm_copy_walk(const moe_gemm_desc *g, const int32_t *host_offsets,
                               moe_copy_walk *w);
 
+/* Host-side bound of the stores of the MXFP8 SwiGLU forward that writes H'
+ * quantised (moe_grouped_gemm with aux_out_scale set): no device work, no
+ * GPU needed. Walks every store its epilogue would issue for descriptor g
+ * (mode FWD, epilogue SWIGLU_FWD, dtype MXFP8; only n_groups, rows and N = 2h
+ * are used) with the group offsets host_offsets[0 .. n_groups], computing
+ * each store's byte offset with the code the kernel runs. The four outputs
+ * are the walk's operands: w->extent[0..3] = writable bytes of aux_out,
+ * aux_out_scale, aux_out_cols, aux_out_cols_scale. On return w->copies is the
+ * number of stores, lowest / end the lowest and one-past-highest byte
+ * written in each output, first_bad the first output written outside
+ * [0, extent) (-1 if none). MOE_ERR_DTYPE for any other mode, epilogue or
+ * dtype; MOE_ERR_SHAPE as for moe_gemm_copy_walk. */
+moe_status moe_gemm_hp_store_walk(const moe_gemm_desc *g, const int32_t *host_offsets,
+                                  moe_copy_walk *w);
+
 /* ------------------------------------------------------------------ */
 /* Backward of the whole layer                                          */
 

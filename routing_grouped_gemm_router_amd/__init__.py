@@ -109,6 +109,8 @@ def _load():
     lib.moe_backward_workspace_layout.restype = _I32
     lib.moe_gemm_copy_walk.argtypes = [ctypes.POINTER(GemmDesc), _P, ctypes.POINTER(CopyWalk)]
     lib.moe_gemm_copy_walk.restype = _I32
+    lib.moe_gemm_hp_store_walk.argtypes = [ctypes.POINTER(GemmDesc), _P, ctypes.POINTER(CopyWalk)]
+    lib.moe_gemm_hp_store_walk.restype = _I32
     lib.mxfp8_quantize.argtypes = [_P, _I32, _I64, _I64, _I32, _P, _I32, _P, _P, _P, _P]
     lib.mxfp8_quantize.restype = _I32
     lib.mxfp8_col_blocks.argtypes = [_I64, _I32]
@@ -443,6 +445,26 @@ def moe_gemm_copy_walk(mode: int, dtype: int, epilogue: int, offsets, M: int = 0
     return {"copies": w.copies, "zero_copies": w.zero_copies, "lowest": list(w.lowest),
             "end": list(w.end), "first_bad": w.first_bad, "bad_offset": w.bad_offset,
             "bad_bytes": w.bad_bytes}
+
+
+def moe_gemm_hp_store_walk(offsets, h: int, K: int, extents=(0, 0, 0, 0)) -> dict:
+    """Host-side walk of every store of the MXFP8 SwiGLU forward that writes
+    H' quantised (no GPU). offsets: host sequence of n_groups + 1 ints;
+    extents: writable bytes of aux_out, aux_out_scale, aux_out_cols,
+    aux_out_cols_scale."""
+    off = (ctypes.c_int32 * len(offsets))(*[int(v) for v in offsets])
+    g = GemmDesc()
+    g.mode, g.dtype, g.epilogue = MOE_GG_FWD, MOE_MXFP8, MOE_EPI_SWIGLU_FWD
+    g.n_groups = len(offsets) - 1
+    g.rows = int(offsets[-1])
+    g.N, g.K = 2 * h, K
+    w = CopyWalk()
+    for i, x in enumerate(extents):
+        w.extent[i] = int(x)
+    _check("moe_gemm_hp_store_walk", _lib.moe_gemm_hp_store_walk(ctypes.byref(g), off,
+                                                                 ctypes.byref(w)))
+    return {"stores": w.copies, "lowest": list(w.lowest), "end": list(w.end),
+            "first_bad": w.first_bad, "bad_offset": w.bad_offset, "bad_bytes": w.bad_bytes}
 
 
 def moe_backward_workspace_layout(T: int, E: int, k: int, d: int, h: int) -> dict:

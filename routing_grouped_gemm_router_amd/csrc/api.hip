@@ -29,6 +29,7 @@ moe_status combine_bwd_launch(const void *dout, const void *y, moe_dtype dt, con
                               hipStream_t s, bool row_gate_only = false);
 moe_status gemm_launch(const moe_gemm_desc *d, hipStream_t s);
 moe_status gemm_copy_walk(const moe_gemm_desc *d, const int32_t *host_offsets, moe_copy_walk *w);
+moe_status gemm_hp_store_walk(const moe_gemm_desc *d, const int32_t *host_offsets, moe_copy_walk *w);
 moe_status mxfp8_quantize_launch(const void *in, moe_dtype in_dt, int64_t rows, int64_t cols,
                                  int axis, const int32_t *group_offsets, int n_groups,
                                  const int32_t *row_map, uint8_t *q, uint8_t *scale,
@@ -272,6 +273,19 @@ moe_status moe_gemm_copy_walk(const moe_gemm_desc *g, const int32_t *host_offset
     for (int e = 0; e < g->n_groups; e++)
         if (host_offsets[e + 1] < host_offsets[e]) return MOE_ERR_SHAPE;
     return gemm_copy_walk(g, host_offsets, w);
+}
+
+moe_status moe_gemm_hp_store_walk(const moe_gemm_desc *g, const int32_t *host_offsets,
+                                  moe_copy_walk *w) {
+    moe_status st = check_gemm_shape(g);
+    if (st != MOE_OK) return st;
+    if (!host_offsets || !w) return MOE_ERR_NULL;
+    if (g->dtype != MOE_MXFP8 || g->mode != MOE_GG_FWD || g->epilogue != MOE_EPI_SWIGLU_FWD)
+        return MOE_ERR_DTYPE;
+    if (host_offsets[0] != 0 || host_offsets[g->n_groups] != g->rows) return MOE_ERR_SHAPE;
+    for (int e = 0; e < g->n_groups; e++)
+        if (host_offsets[e + 1] < host_offsets[e]) return MOE_ERR_SHAPE;
+    return gemm_hp_store_walk(g, host_offsets, w);
 }
 
 size_t moe_backward_workspace_size(const moe_bwd_desc *b) {

@@ -105,6 +105,30 @@ struct CopyGeom {
     }
 };
 
+// Byte offsets of the stores of the MXFP8 SwiGLU forward that writes H'
+// quantised (used by the kernel's epilogue and by the host walk of those
+// stores, moe_gemm_hp_store_walk). A consumer wave holds rows r0 .. r0+63 and
+// hidden units j0 .. j0+31; lane = 32 half + 4 qd + rq, column c = j0 + lane % 32.
+// The group's column-block layout covers blocks [bb, bb + nb) (bb = 4 x the
+// group's first 128-row unit, nb = 4 x its units), one nb*32-byte run per
+// hidden unit; lr is a row within the group.
+struct HpStores {
+    // 16 bytes of column c, rows lr + 16 half .. + 15 of a 32-row block
+    MOE_HD static int64_t col_q(int64_t bb, int64_t nb, int h, int c, int lr, int half) {
+        return bb * 32 * h + (int64_t)c * nb * 32 + lr + half * 16;
+    }
+    // the scale byte of column c's 32-row block starting at lr
+    MOE_HD static int64_t col_s(int64_t bb, int64_t nb, int h, int c, int lr) {
+        return bb * h + (int64_t)c * nb + (lr >> 5);
+    }
+    // 4 bytes of routed row `row`, units j0 + 4 qd .. + 3
+    MOE_HD static int64_t row_q(int64_t row, int h, int j0, int qd) {
+        return row * h + j0 + 4 * qd;
+    }
+    // the scale byte of the row's block j0 / 32
+    MOE_HD static int64_t row_s(int64_t row, int h, int j0) { return row * (h >> 5) + (j0 >> 5); }
+};
+
 // coordinates of one output tile
 struct TileC {
     int e;        // group (expert)

@@ -1349,8 +1349,6 @@ void gg_ws(GemmArgs g) {
         // the group's blocks [bb, bb + nb) of the column-block layout
         const int64_t bb = 4 * (int64_t)s_tile[e], nb = 4 * (int64_t)(s_tile[e + 1] - s_tile[e]);
         const int c = j0 + col_l;
-        uint8_t *q0c = g.aux_out_cols + bb * 32 * h + (int64_t)c * nb * 32;
-        uint8_t *s0c = g.aux_out_cols_scale + bb * h + (int64_t)c * nb;
         const int half = lane >> 5, qd = (lane & 31) >> 2, rq = lane & 3;
         const int lrow0 = r0 - s_off[e];            // within the group; a multiple of 64
         const bool rows_full = wave_full(r0 + WTM <= t.row_end);
@@ -1406,8 +1404,8 @@ void gg_ws(GemmArgs g) {
             const uint4 out = half ? make_uint4(got[0], w[2], got[1], w[3])
                                    : make_uint4(w[0], got[0], w[1], got[1]);
             const int lr = lrow0 + i * 32;
-            *reinterpret_cast<uint4 *>(q0c + lr + half * 16) = out;
-            if (half == 0) s0c[lr >> 5] = (uint8_t)sbc;
+            *reinterpret_cast<uint4 *>(g.aux_out_cols + HpStores::col_q(bb, nb, h, c, lr, half)) = out;
+            if (half == 0) g.aux_out_cols_scale[HpStores::col_s(bb, nb, h, c, lr)] = (uint8_t)sbc;
         }
         // row layout: a 4 x 4 transpose inside each quad of lanes gives lane
         // 4 qd + rq the units 4 qd .. 4 qd + 3 of row i*32 + gq*8 + half*4 + rq;
@@ -1436,8 +1434,8 @@ void gg_ws(GemmArgs g) {
                 const uint32_t w = enc(x[0], x[1], x[2], x[3], sbr);
                 const int ro = i * 32 + gq * 8 + half * 4 + rq;
                 if (rows_full || r0 + ro < t.row_end) {
-                    *reinterpret_cast<uint32_t *>(q1 + (int64_t)(r0 + ro) * h + j0 + 4 * qd) = w;
-                    if (qd == 0) g.aux_out_scale[(int64_t)(r0 + ro) * (h >> 5) + (j0 >> 5)] = (uint8_t)sbr;
+                    *reinterpret_cast<uint32_t *>(q1 + HpStores::row_q(r0 + ro, h, j0, qd)) = w;
+                    if (qd == 0) g.aux_out_scale[HpStores::row_s(r0 + ro, h, j0)] = (uint8_t)sbr;
                 }
             }
       }
@@ -2083,6 +2081,58 @@ void walk_mode(const GemmArgs &a, const int32_t *off, bool fp8, moe_copy_walk *w
 }  // namespace
 
 // the launch configuration of gemm_launch, walked on the host
+// Every store of the MXFP8 SwiGLU forward's quantised H' (the four outputs
+// as operands 0..3 of the walk), over the tiles gg_ws computes: group e's
+// 128-row units times the n-tiles of BN / 2 hidden units, each consumer
+// wave and lane, with the offsets the epilogue uses (HpStores).
+moe_status gemm_hp_store_walk(const moe_gemm_desc *d, const int32_t *off, moe_copy_walk *w) {
+    constexpr int BM = kWsBM, BN = kWsBN, WM = kWsWM, WN = kWsWN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    static_assert(WTM == 64 && WTN == 64, "the epilogue's wave tile");
+    const int h = d->N / 2, E = d->n_groups;
+    w->copies = w->zero_copies = 0;
+    for (int i = 0; i < 4; i++) {
+        w->lowest[i] = INT64_MAX;
+        w->end[i] = 0;
+    }
+    w->first_bad = -1;
+    w->bad_offset = w->bad_bytes = 0;
+    Walker wk{w};
+    const int n_tiles = (h + BN / 2 - 1) / (BN / 2);
+    int64_t ub = 0;                                   // 128-row units before group e
+    for (int e = 0; e < E; e++) {
+        const int rows_e = off[e + 1] - off[e];
+        const int units = (rows_e + BM - 1) / BM;
+        const int64_t bb = 4 * ub, nb = 4 * (int64_t)units;
+        for (int mt = 0; mt < units; mt++)
+            for (int nt = 0; nt < n_tiles; nt++)
+                for (int wm = 0; wm < WM; wm++)
+                    for (int wn = 0; wn < WN; wn++) {
+                        const int j0 = nt * (BN / 2) + wn * (WTN / 2);
+                        if (j0 >= h) continue;
+                        const int r0 = off[e] + mt * BM + wm * WTM;
+                        const int lrow0 = r0 - off[e];
+                        for (int lane = 0; lane < 64; lane++) {
+                            const int half = lane >> 5, qd = (lane & 31) >> 2, rq = lane & 3;
+                            const int c = j0 + (lane & 31);
+                            for (int i = 0; i < 2; i++) {
+                                const int lr = lrow0 + i * 32;
+                                wk.read(2, HpStores::col_q(bb, nb, h, c, lr, half), 16);
+                                if (half == 0) wk.read(3, HpStores::col_s(bb, nb, h, c, lr), 1);
+                                for (int gq = 0; gq < 4; gq++) {
+                                    const int64_t row = r0 + i * 32 + gq * 8 + half * 4 + rq;
+                                    if (row >= off[e + 1]) continue;
+                                    wk.read(0, HpStores::row_q(row, h, j0, qd), 4);
+                                    if (qd == 0) wk.read(1, HpStores::row_s(row, h, j0), 1);
+                                }
+                            }
+                        }
+                    }
+        ub += units;
+    }
+    return MOE_OK;
+}
+
 moe_status gemm_copy_walk(const moe_gemm_desc *d, const int32_t *off, moe_copy_walk *w) {
     GemmArgs a{};
     a.rows = d->rows; a.M = d->M; a.N = d->N; a.K = d->K;

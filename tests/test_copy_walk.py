@@ -11,7 +11,9 @@ one row, a row short of or past a tile, a long tail), and reduction widths
 with a half last K step (d % 64 == 32). Extents are the sizes the operand
 contract of moe.h gives each operand. The MXFP8 backward's workspace regions
 are checked against the sizes of what is quantised into them and against the
-reads of the backward's four GEMMs.
+reads of the backward's four GEMMs. The stores of the MXFP8 SwiGLU forward
+that writes H' quantised are walked the same way (moe_gemm_hp_store_walk,
+with the epilogue's own offset code) against its four outputs.
 """
 import numpy as np
 import pytest
@@ -214,3 +216,54 @@ def test_mxfp8_backward_gemm_reads_stay_in_their_regions(T, E, k, d, h):
     for mode, epi, M, N, K, ext in gemms:
         r = moe.moe_gemm_copy_walk(mode, MX, epi, off, M=M, N=N, K=K, extents=ext)
         _in_bounds(r, ext, 4)
+
+
+# The MXFP8 SwiGLU forward that stores H' quantised: every store of its
+# epilogue, walked on the host with the offsets the kernel computes
+# (moe_gemm_hp_store_walk), lies inside the four outputs at the sizes the
+# binding requires, and the stores reach exactly the bytes the layouts hold:
+# every row of H' along h, and every 128-row unit of every group (padding
+# rows included) of the column-block layout.
+@pytest.mark.parametrize("name", sorted(COUNTS))
+@pytest.mark.parametrize("h", [128, 160, 2048])
+def test_hp_store_walk_in_bounds(name, h):
+    counts = COUNTS[name]
+    off = _offsets(counts)
+    R, E = off[-1], len(counts)
+    nb = moe.mxfp8_col_blocks(R, E)
+    ext = (R * h, R * (h // 32), nb * 32 * h, nb * h)
+    w = moe.moe_gemm_hp_store_walk(off, h, 128, ext)
+    assert w["first_bad"] == -1, w
+    units = sum(-(-c // 128) for c in counts)
+    if R == 0:
+        assert w["stores"] == 0
+        return
+    # rows layout: all R rows x h bytes, scales R x h/32
+    assert w["lowest"][0] == 0 and w["end"][0] == R * h
+    assert w["lowest"][1] == 0 and w["end"][1] == R * (h // 32)
+    # column layout: 4 * units blocks of 32 rows per hidden unit
+    assert w["lowest"][2] == 0 and w["end"][2] == 4 * units * 32 * h
+    assert w["lowest"][3] == 0 and w["end"][3] == 4 * units * h
+    # stores per 32 x 32 block of a 128-row unit: 64 lanes x 1 column piece,
+    # 32 column scales; rows: 8 x 4 bytes and one scale per row
+    n_tiles_h = h // 32
+    col_stores = units * 4 * n_tiles_h * (64 + 32)
+    row_stores = R * n_tiles_h * (8 + 1)
+    assert w["stores"] == col_stores + row_stores
+
+
+def test_hp_store_walk_catches_short_outputs():
+    """A column layout one byte short (or rows one short) is reported."""
+    off = _offsets(COUNTS["ragged"])
+    R, E, h = off[-1], len(COUNTS["ragged"]), 128
+    units = sum(-(-c // 128) for c in COUNTS["ragged"])
+    full = (R * h, R * (h // 32), 4 * units * 32 * h, 4 * units * h)
+    for i in range(4):
+        ext = list(full)
+        ext[i] -= 1
+        w = moe.moe_gemm_hp_store_walk(off, h, 128, ext)
+        assert w["first_bad"] == i, (i, w)
+    bad = list(off)
+    bad[2], bad[3] = bad[3], bad[2]                                       # offsets decrease
+    with pytest.raises(moe.MoeError):
+        moe.moe_gemm_hp_store_walk(bad, h, 128, full)
