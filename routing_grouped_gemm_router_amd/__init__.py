@@ -824,8 +824,8 @@ class MoELayerMX:
     quantises x along d before dispatch, so the row-wise dispatch moves E4M3
     bytes plus their scales; GEMM1 writes AB in bf16 and H' already
     quantised, along h for GEMM2 and along rows per expert for GEMM2's weight
-    gradient (fuse_hp; with fuse_hp = False or when recomputing, GEMM1 writes
-    bf16 H' and a separate pass quantises it: the same bytes); y and out stay
+    gradient (fuse_hp; with fuse_hp = False GEMM1 writes bf16 H' and a
+    separate pass quantises it: the same bytes); y and out stay
     bf16. The backward (moe_backward with MXFP8) quantises its own GEMM
     operands."""
 
@@ -880,12 +880,16 @@ class MoELayerMX:
         self.hp = _scratch("mx_hp", (R, h), torch.bfloat16, dev)
         self.hpq = _scratch("mx_hpq", (R, h), torch.uint8, dev)
         self.hps = _scratch("mx_hps", (R, h // 32), torch.uint8, dev)
-        # H' along rows per expert (GEMM2 wgrad's operand), quantised in the
-        # forward from the same read as GEMM2's; held instead of bf16 H'
+        # H' along rows per expert (GEMM2 wgrad's operand), written by GEMM1
+        # with GEMM2's; held instead of bf16 H' (when recomputing, the backward
+        # quantises the H' it recomputes and these are scratch)
+        nb = mxfp8_col_blocks(R, E)
         if not self.recompute:
-            nb = mxfp8_col_blocks(R, E)
             self.hpc = torch.empty(nb * 32 * h, **u8)
             self.hpcs = torch.empty(nb * h, **u8)
+        else:
+            self.hpc = _scratch("mx_hpc", (nb * 32 * h,), torch.uint8, dev)
+            self.hpcs = _scratch("mx_hpcs", (nb * h,), torch.uint8, dev)
         self.y_perm = torch.empty((R, d), **bf)
         self.out = torch.empty((T, d), **bf)
         self.grads = None
@@ -893,9 +897,9 @@ class MoELayerMX:
         self._T = key
 
     def hp_quantised_in_gemm1(self) -> bool:
-        """GEMM1 stores H' in both MXFP8 layouts (the forward of a layer that
-        holds H' for its backward)."""
-        return self.fuse_hp and not self.recompute
+        """The forward's GEMM1 stores H' in both MXFP8 layouts (the backward's
+        recomputation of GEMM1 stores bf16 H', which moe_backward quantises)."""
+        return self.fuse_hp
 
     def _gemm1(self, x, offsets, token_pos, quantised_hp: bool = False):
         """Quantised dispatch of x and GEMM1 + SwiGLU (forward, and again in
